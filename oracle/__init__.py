@@ -1,0 +1,37 @@
+"""Reference oracle for paged KV-cache attention (test infrastructure only).
+
+This package is a plain, slow, CPU implementation of what the paged-attention
+hot path computes.  It exists to check the HIP kernels and nothing else: only
+``tests/``, ``__graft_entry__.smoke()`` and the ``cpu_baseline`` leg of
+``bench.py`` may import it.  The product path (the C-ABI library and its Python
+binding) never imports, links or calls anything in here, and this package never
+imports the product path.
+
+Sources (web pages; every function cites the part it follows):
+
+* "Tour: One forward pass" (explainvllm), stops 1-5 (request rows, batch order,
+  ``query_start_loc``, positions, ``seq_lens``, block tables, slot mappings,
+  ``PAD_SLOT_ID``) and stop 10 (cache write, then varlen causal attention that
+  reads keys through the block table).
+* "vLLM MHA Code Path: From QKV to Paged KV Cache", sections "One Path Covers
+  MHA, GQA, and MQA", "Worked Trace: One Decode Token", "Cache write and cache
+  read use different maps".
+* "vLLM 推理全流程深度解析" (vLLM inference deep dive): the BlockManager block
+  allocation example, the ``prepare_input_tensors`` slot-mapping example, the
+  ``reshape_and_cache`` kernel description, the PagedAttention decode kernel
+  signature and the KV-cache quantization remark.
+
+Arithmetic is float64 unless the format itself fixes the precision (the fp8
+encoder's single float32 multiply).  Modules:
+
+* ``codecs``     fp16 / bf16 / OCP e4m3fn bit decoders and the e4m3fn encoder.
+* ``metadata``   query_start_loc, seq_lens, positions, slot_mapping.
+* ``cache``      the slot_mapping scatter into ``[num_blocks, block_size, Hkv, D]``.
+* ``attention``  gather through the block table + dense causal softmax(QK^T*scale)V.
+
+Every function here is pinned by ``tests/test_oracle_*.py`` against values the
+pages print, closed forms, library routines or brute force; none is
+"parity unpinned".
+"""
+
+from . import codecs, metadata, cache, attention  # noqa: F401

@@ -1,0 +1,121 @@
+"""Paged causal attention of the oracle (test infrastructure only).
+
+What is computed (the plain definition; float64 throughout):
+
+For request ``r`` with ``n_r = query_start_loc[r+1] - query_start_loc[r]`` new
+tokens and ``s_r = seq_lens[r]`` keys in total, the ``c_r = s_r - n_r`` tokens
+cached before this step come first ("Tour: One forward pass", stop 3:
+``seq_lens = num_computed_tokens + query_len``, positions start at
+``num_computed_tokens``).  Its logical key ``j`` lives in physical block
+``block_table[r][j // block_size]`` at offset ``j % block_size`` of the global
+cache ``[num_blocks, block_size, num_kv_heads, head_size]`` ("vLLM MHA Code
+Path", "Cache write and cache read use different maps": the block table is the
+request-to-page gather map; "vLLM 推理全流程深度解析", the PagedAttention decode
+kernel reads each sequence's blocks through ``block_tables``).
+
+Query ``i`` of the request sits at position ``c_r + i`` and attends to keys
+``j = 0 .. c_r + i``: the current token attends to itself and future positions
+are masked ("vLLM MHA Code Path", Worked Trace step 10 remark; "Tour: One
+forward pass", stop 10: R1 reads 541 keys, R2 130, R3's rows together 298).
+Query head ``h`` reads K/V head ``h // G`` with ``G = Hq / Hkv`` ("vLLM MHA Code
+Path", "One Path Covers MHA, GQA, and MQA": Hq must be a multiple of Hkv, so
+each K/V head serves G query heads).  Scores are ``q . k * scale`` and the row
+is ``softmax(scores) @ V``.
+
+Readings where the pages are silent: the alignment of the causal mask for a
+cached prefix is bottom-right (it follows from the positions); ``scale`` is
+``1/sqrt(head_size)`` unless the caller passes another; query head ``h`` maps to
+K/V head ``h // G`` (contiguous groups).
+"""
+
+import math
+
+import numpy as np
+
+from . import codecs
+
+
+def gather_request_kv(key_cache_f64, value_cache_f64, block_table_row, seq_len, block_size):
+    """Logical K/V of one request: [seq_len, Hkv, D] each, through its block-table row."""
+    hkv, d = key_cache_f64.shape[2], key_cache_f64.shape[3]
+    k = np.empty((seq_len, hkv, d), dtype=np.float64)
+    v = np.empty((seq_len, hkv, d), dtype=np.float64)
+    for j in range(0, seq_len, block_size):
+        blk = int(block_table_row[j // block_size])
+        cnt = min(block_size, seq_len - j)
+        k[j:j + cnt] = key_cache_f64[blk, :cnt]
+        v[j:j + cnt] = value_cache_f64[blk, :cnt]
+    return k, v
+
+
+def causal_attention(q, k, v, num_computed, scale):
+    """Dense causal attention of one request in float64.
+
+    q: [n, Hq, D]; k, v: [s, Hkv, D] with s = num_computed + n.
+    Row i attends keys 0 .. num_computed + i.  Returns [n, Hq, D].
+    """
+    n, hq, d = q.shape
+    s, hkv, _ = k.shape
+    g = hq // hkv
+    out = np.empty((n, hq, d), dtype=np.float64)
+    if n == 0:
+        return out
+    key_idx = np.arange(s)[None, :]
+    last_key = (num_computed + np.arange(n))[:, None]
+    allowed = key_idx <= last_key                         # [n, s]
+    for h in range(hq):
+        kv = h // g
+        scores = (q[:, h, :] @ k[:, kv, :].T) * scale     # [n, s]
+        scores = np.where(allowed, scores, -np.inf)
+        mx = scores.max(axis=1, keepdims=True)
+        p = np.exp(scores - mx)
+        p = np.where(allowed, p, 0.0)
+        p /= p.sum(axis=1, keepdims=True)
+        out[:, h, :] = p @ v[:, kv, :]
+    return out
+
+
+def decode_cache(cache_bits, cache_dtype, scale=1.0):
+    """Stored cache bits -> float64 values (fp8 codes are multiplied by the scale)."""
+    vals = codecs.decode(cache_bits, cache_dtype)
+    if cache_dtype == "fp8_e4m3":
+        vals = vals * float(scale)
+    return vals
+
+
+def paged_attention(q, key_cache, value_cache, block_tables, query_start_loc, seq_lens,
+                    block_size, scale=None, requests=None, cache_dtype=None,
+                    k_scale=1.0, v_scale=1.0):
+    """Attention of a batch over the paged cache, one request at a time.
+
+    q: float64 [T, Hq, D] (already decoded).
+    key_cache/value_cache: float64 [num_blocks, block_size, Hkv, D] (decoded), or
+      raw bits when ``cache_dtype`` is given ('f16' | 'bf16' | 'fp8_e4m3'); raw
+      bits are decoded per request, so a large pool is never widened at once.
+    requests: iterable of request indices to compute (default: all).
+    Returns {r: float64 [n_r, Hq, D]}.
+    """
+    d = q.shape[2]
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+    num_reqs = len(seq_lens)
+    if requests is None:
+        requests = range(num_reqs)
+    result = {}
+    for r in requests:
+        start, end = int(query_start_loc[r]), int(query_start_loc[r + 1])
+        n = end - start
+        s = int(seq_lens[r])
+        c = s - n
+        row = block_tables[r]
+        if cache_dtype is None:
+            k, v = gather_request_kv(key_cache, value_cache, row, s, block_size)
+        else:
+            nb = -(-s // block_size)
+            ids = np.asarray(row[:nb], dtype=np.int64)
+            kb = decode_cache(key_cache[ids], cache_dtype, k_scale)
+            vb = decode_cache(value_cache[ids], cache_dtype, v_scale)
+            local = np.arange(nb)
+            k, v = gather_request_kv(kb, vb, local, s, block_size)
+        result[r] = causal_attention(q[start:end], k, v, c, scale)
+    return result

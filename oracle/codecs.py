@@ -1,0 +1,113 @@
+"""Bit-level decoders and the fp8 encoder of the oracle (test infrastructure only).
+
+The pages store K/V in the activation dtype (fp16 / bf16) and name KV-cache
+quantization as a throughput lever ("vLLM 推理全流程深度解析", the PagedAttention
+remark on KV cache int8).  The fp8 cache format used here is the OCP
+``e4m3fn`` format: 1 sign bit, 4 exponent bits with bias 7, 3 mantissa bits,
+subnormals at exponent field 0, no infinities, and only ``S.1111.111`` as NaN,
+so the largest finite magnitude is 1.75 * 2**8 = 448.
+
+Reading taken where the pages are silent: one float32 scale per tensor
+(K and V separately); a stored code means ``code_value * scale``; encoding is
+``round_to_nearest_even(saturate(float32(x) * float32(1/scale)))`` with the
+single multiply done in IEEE float32, saturation to +-448 for every finite or
+infinite overflow, and NaN kept as NaN.
+"""
+
+import numpy as np
+
+E4M3_MAX = 448.0
+
+
+def f16_bits_to_f64(bits):
+    """IEEE binary16 bit patterns (uint16) -> float64 values."""
+    bits = np.asarray(bits, dtype=np.uint16)
+    return bits.view(np.float16).astype(np.float64)
+
+
+def bf16_bits_to_f64(bits):
+    """bfloat16 bit patterns (uint16) -> float64.
+
+    A bfloat16 is the upper half of an IEEE binary32, so widening the bits by a
+    16-bit left shift gives the binary32 with the same value, exactly.
+    """
+    bits = np.asarray(bits, dtype=np.uint16)
+    return (bits.astype(np.uint32) << np.uint32(16)).view(np.float32).astype(np.float64)
+
+
+def e4m3fn_value(code):
+    """Value of one e4m3fn code (0..255), straight from the bit definition."""
+    code = int(code)
+    sign = -1.0 if (code >> 7) & 1 else 1.0
+    exp = (code >> 3) & 0xF
+    man = code & 0x7
+    if exp == 0xF and man == 0x7:
+        return float("nan")
+    if exp == 0:
+        return sign * (man / 8.0) * 2.0 ** (1 - 7)       # subnormal
+    return sign * (1.0 + man / 8.0) * 2.0 ** (exp - 7)   # normal
+
+
+E4M3FN_TABLE = np.array([e4m3fn_value(c) for c in range(256)], dtype=np.float64)
+
+
+def e4m3fn_to_f64(codes):
+    """uint8 e4m3fn codes -> float64 values (table lookup)."""
+    return E4M3FN_TABLE[np.asarray(codes, dtype=np.uint8)]
+
+
+# Non-negative finite codes 0x00..0x7E in increasing value order.
+_POS_CODES = np.arange(0x7F, dtype=np.int64)
+_POS_VALUES = E4M3FN_TABLE[:0x7F]
+
+
+def e4m3fn_encode(x_f32, inv_scale_f32):
+    """Encode float32 values as e4m3fn codes with the per-tensor scale.
+
+    ``y = float32(x * inv_scale)`` (one IEEE float32 multiply), then ``y`` is
+    clamped to [-448, 448] (saturation; 448 is representable, so clamping first
+    and rounding second equals rounding first and saturating second), then the
+    nearest representable e4m3fn magnitude is chosen, with a tie going to the
+    code whose mantissa is even.  The sign bit is the sign of ``y`` (so -0.0 and
+    negative values rounding to zero give 0x80).  NaN gives 0x7F / 0xFF.
+
+    The search over all 127 non-negative finite codes is the definition of
+    round-to-nearest-even written out; it is slow and meant to be obvious.
+    """
+    x = np.asarray(x_f32, dtype=np.float32)
+    with np.errstate(over="ignore", invalid="ignore"):
+        y = (x * np.float32(inv_scale_f32)).astype(np.float32)   # float32 multiply
+    neg = np.signbit(y)
+    nan = np.isnan(y)
+    mag = np.abs(y.astype(np.float64))
+    mag = np.where(nan, 0.0, np.minimum(mag, E4M3_MAX))
+    flat = mag.reshape(-1)
+    out = np.empty(flat.shape, dtype=np.int64)
+    step = 1 << 16
+    for lo in range(0, flat.size, step):
+        m = flat[lo:lo + step, None]
+        dist = np.abs(m - _POS_VALUES[None, :])
+        best = dist.min(axis=1, keepdims=True)
+        is_best = dist == best
+        # candidates at the minimal distance: at most two (a tie); prefer the even code
+        even = (_POS_CODES[None, :] & 1) == 0
+        pick_even = is_best & even
+        has_even = pick_even.any(axis=1)
+        idx_even = np.argmax(pick_even, axis=1)
+        idx_any = np.argmax(is_best, axis=1)
+        out[lo:lo + step] = np.where(has_even, idx_even, idx_any)
+    codes = out.reshape(mag.shape).astype(np.uint8)
+    codes = codes | np.where(neg, 0x80, 0).astype(np.uint8)
+    codes = np.where(nan, codes | 0x7F, codes)
+    return codes.astype(np.uint8)
+
+
+def decode(bits, dtype):
+    """Decode stored bits of ``dtype`` ('f16', 'bf16', 'fp8_e4m3') to float64."""
+    if dtype == "f16":
+        return f16_bits_to_f64(bits)
+    if dtype == "bf16":
+        return bf16_bits_to_f64(bits)
+    if dtype == "fp8_e4m3":
+        return e4m3fn_to_f64(bits)
+    raise ValueError(dtype)
