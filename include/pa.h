@@ -1,0 +1,229 @@
+/*
+ * pa.h -- paged KV-cache attention for one mixed continuous batch, on AMD
+ * Instinct MI355X (gfx950).  C ABI of libpa.so.
+ *
+ * The four calls follow the per-step data flow that "Tour: One forward pass"
+ * (explainvllm) walks through and that "vLLM MHA Code Path: From QKV to Paged
+ * KV Cache" summarises in its worked decode trace:
+ *
+ *   once per step   pa_metadata_build  -> query_start_loc, seq_lens,
+ *                                          positions, slot_mapping
+ *   per layer       pa_cache_write     -> scatter new K/V into the paged cache
+ *                   pa_decode          -> attention of 1-token requests
+ *                   pa_prefill_varlen  -> causal attention of (chunked) prefills
+ *
+ * Conventions shared by every call
+ * --------------------------------
+ * - Ownership: the caller allocates every buffer (device memory unless stated
+ *   otherwise) and keeps it alive until the work on `stream` has finished.
+ *   The library allocates nothing, frees nothing and keeps no state between
+ *   calls.  Calls are thread-safe and reentrant.
+ * - Ordering: every call only enqueues kernels on `stream` (a hipStream_t;
+ *   NULL means the default stream) and returns without waiting.  It never
+ *   copies device data to the host.  The write of a layer's new K/V must be
+ *   enqueued before that layer's attention on the same stream: attention reads
+ *   the current tokens' keys and values from the cache, not from the K/V
+ *   inputs (the write-before-read order of the tour's stop 10 and of step 8 of
+ *   the MHA trace).
+ * - Errors: all argument checks run on the host before any launch.  A failed
+ *   check returns PA_ERR_INVALID_ARG or PA_ERR_UNSUPPORTED and enqueues
+ *   nothing.  A launch failure returns PA_ERR_HIP.  Faults inside a kernel
+ *   surface at the caller's next synchronisation, as for any HIP call.
+ * - Cache layout: one key cache and one value cache per layer, each
+ *   [num_blocks, block_size, num_kv_heads, head_dim] row-major (the global
+ *   pool of "vLLM 推理全流程深度解析", reshape_and_cache description).  The pool
+ *   is shared by all requests; several requests may list the same block.
+ * - Index types: query_start_loc, seq_lens, num_computed_tokens, query_lens
+ *   and block tables are int32; positions and slot_mapping are int64 (the
+ *   dtypes printed in stops 3 and 4 of the tour).
+ * - Block tables: int32 [num_reqs, max_blocks_per_req] row-major, in batch
+ *   order (row r belongs to request r of the call's numbering).  Entry j of a
+ *   row is the physical block holding logical tokens j*block_size ..
+ *   j*block_size+block_size-1.  Entries at or past ceil(seq_len/block_size)
+ *   are never read.  An entry outside [0, num_blocks) is never dereferenced;
+ *   its tokens are treated as absent.
+ * - Rows: query/output rows are [num_tokens, num_q_heads, head_dim] with a
+ *   row stride (in elements) that may exceed num_q_heads*head_dim, so views
+ *   into a fused QKV buffer work.  Strides and base pointers must be 16-byte
+ *   aligned.
+ */
+#ifndef PA_H
+#define PA_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum pa_status {
+  PA_OK = 0,
+  PA_ERR_INVALID_ARG = 1,        /* null pointer, bad size, misaligned pointer/stride */
+  PA_ERR_UNSUPPORTED = 2,        /* valid request outside the built kernel set */
+  PA_ERR_WORKSPACE_TOO_SMALL = 3,
+  PA_ERR_HIP = 4                 /* a HIP launch reported an error */
+} pa_status;
+
+typedef enum pa_dtype {
+  PA_F16 = 0,       /* IEEE binary16 */
+  PA_BF16 = 1,      /* bfloat16 */
+  PA_FP8_E4M3 = 2   /* OCP e4m3fn (max 448, no inf); cache only */
+} pa_dtype;
+
+/*
+ * Per-layer attention geometry (immutable for the layer).
+ *
+ * num_q_heads % num_kv_heads == 0: query head h reads K/V head h / G with
+ * G = num_q_heads / num_kv_heads, which covers MHA (G = 1), GQA and MQA
+ * (num_kv_heads = 1) with one path ("vLLM MHA Code Path", "One Path Covers
+ * MHA, GQA, and MQA").  Supported: head_dim 64 or 128; block_size 16;
+ * act_dtype F16 or BF16; cache_dtype equal to act_dtype or FP8_E4M3; G <= 32
+ * for decode.
+ *
+ * softmax_scale multiplies q.k (1/sqrt(head_dim) is the usual value).
+ * k_scale / v_scale apply to an fp8 cache only: a stored code c means the
+ * value c * scale.  The write path encodes float32(x) * (1.0f / scale)
+ * (one float32 multiply, the reciprocal rounded once on the host) with
+ * round-to-nearest-even and saturation to +-448; NaN stays NaN.
+ *
+ * decode_partition_tokens: keys per split-K partition of pa_decode; 0 lets the
+ * library choose from the call's shape.  Otherwise a positive multiple of 128.
+ */
+typedef struct pa_attn_desc {
+  int32_t num_q_heads;
+  int32_t num_kv_heads;
+  int32_t head_dim;
+  int32_t block_size;
+  int32_t act_dtype;      /* pa_dtype */
+  int32_t cache_dtype;    /* pa_dtype */
+  float softmax_scale;
+  float k_scale;
+  float v_scale;
+  int32_t decode_partition_tokens;
+} pa_attn_desc;
+
+/* Human-readable name of a status code (static storage). */
+const char* pa_status_string(pa_status status);
+
+/*
+ * pa_metadata_build -- per-step batch metadata ("Tour: One forward pass",
+ * stops 3 and 4).  One kernel launch.
+ *
+ * In (device):  num_computed_tokens int32 [num_reqs], query_lens int32
+ *               [num_reqs], block_tables int32 [num_reqs, max_blocks_per_req].
+ * Out (device): query_start_loc int32 [qsl_len] with qsl_len >= num_reqs + 1:
+ *                 qsl[0] = 0, qsl[r+1] = qsl[r] + query_lens[r], and every
+ *                 entry past num_reqs equals the token total T (so the buffer
+ *                 never decreases);
+ *               seq_lens int32 [num_reqs] = num_computed_tokens + query_lens;
+ *               positions int64 [num_tokens_padded]: token t of request r at
+ *                 batch row qsl[r] + i gets num_computed_tokens[r] + i; rows
+ *                 >= T are not written;
+ *               slot_mapping int64 [num_tokens_padded]:
+ *                 block_tables[r][pos / block_size] * block_size
+ *                 + pos % block_size, or -1 (PAD_SLOT_ID) for rows >= T and
+ *                 for positions whose block index is >= max_blocks_per_req.
+ * Requires T <= num_tokens_padded; rows past num_tokens_padded are not
+ * written.  Empty requests (query_len 0) are allowed.
+ */
+pa_status pa_metadata_build(int32_t num_reqs, int32_t block_size, int32_t max_blocks_per_req,
+                            int32_t num_tokens_padded, int32_t qsl_len,
+                            const int32_t* num_computed_tokens, const int32_t* query_lens,
+                            const int32_t* block_tables,
+                            int32_t* query_start_loc, int32_t* seq_lens,
+                            int64_t* positions, int64_t* slot_mapping,
+                            void* stream);
+
+/*
+ * pa_cache_write -- scatter the step's new K/V rows into the paged cache
+ * (reshape_and_cache in "vLLM 推理全流程深度解析"; reshape_and_cache_flash in
+ * stop 10 of the tour).  One kernel launch.
+ *
+ * key, value: act_dtype [num_tokens, num_kv_heads, head_dim] with row strides
+ *   key_row_stride / value_row_stride in elements.
+ * slot_mapping: int64 [num_tokens].  Token t with slot s >= 0 and
+ *   s < num_blocks*block_size goes to cache[s / block_size][s % block_size];
+ *   other tokens (the -1 padding) are skipped.  Two tokens with one slot race.
+ * key_cache, value_cache: cache_dtype [num_blocks, block_size, num_kv_heads,
+ *   head_dim]; only the addressed slots are written, bit-exact copies (or
+ *   fp8 encodings, see pa_attn_desc) of the inputs.
+ */
+pa_status pa_cache_write(const pa_attn_desc* desc, int64_t num_tokens,
+                         const void* key, int64_t key_row_stride,
+                         const void* value, int64_t value_row_stride,
+                         const int64_t* slot_mapping,
+                         void* key_cache, void* value_cache, int64_t num_blocks,
+                         void* stream);
+
+/*
+ * pa_decode -- attention of decode requests through their block tables
+ * (PagedAttention decode in "vLLM 推理全流程深度解析"; the decode rows of the
+ * varlen call in stop 10 of the tour).
+ *
+ * Requests req_begin .. req_end-1 (indices into query_start_loc / seq_lens /
+ * block_tables).  Each must have query_len == 1; a request with another
+ * query length is skipped and its output rows are not written.  The query
+ * row of request r is q[qsl[r]]; it attends keys 0 .. seq_lens[r]-1 (the
+ * token written this step included):
+ *   out[qsl[r], h] = softmax_j(softmax_scale * q.k_j) v_j, k_j/v_j of K/V head
+ *   h / G.
+ * max_seq_len (host scalar) must be >= every seq_len of the range; keys past
+ * it are ignored.  Accumulation is float32; out is act_dtype, rounded to
+ * nearest even.  Long contexts are split into partitions whose float32
+ * partial results (running max, sum, weighted sum) go to `workspace` and are
+ * merged by a second kernel in a fixed order (deterministic output).
+ *
+ * Workspace: device memory of at least pa_decode_workspace_size() bytes for
+ * the same desc, request count, max_seq_len and max_blocks_per_req (else
+ * PA_ERR_WORKSPACE_TOO_SMALL); it may be NULL when that size is 0.  Its
+ * contents need no initialisation and are scratch after the call.
+ */
+pa_status pa_decode(const pa_attn_desc* desc, int32_t req_begin, int32_t req_end,
+                    const void* q, int64_t q_row_stride,
+                    const int32_t* query_start_loc, const int32_t* seq_lens,
+                    const int32_t* block_tables, int32_t max_blocks_per_req,
+                    const void* key_cache, const void* value_cache, int64_t num_blocks,
+                    int32_t max_seq_len,
+                    void* workspace, size_t workspace_bytes,
+                    void* out, int64_t out_row_stride, void* stream);
+
+/*
+ * pa_decode_workspace_size -- bytes of workspace pa_decode needs for
+ * num_reqs = req_end - req_begin requests of this desc with the given
+ * max_seq_len and block-table width (the split-K partials: for every request,
+ * query head and partition, a float32 running max, sum and head_dim weighted
+ * sums).  Host only; launches nothing.
+ */
+pa_status pa_decode_workspace_size(const pa_attn_desc* desc, int32_t num_reqs,
+                                   int32_t max_seq_len, int32_t max_blocks_per_req,
+                                   size_t* bytes);
+
+/*
+ * pa_prefill_varlen -- causal attention of prefill / chunked-prefill requests
+ * over the paged cache (flash_attn_varlen_func with cu_seqlens_q =
+ * query_start_loc, seqused_k = seq_lens and a block table, stop 10 of the
+ * tour).
+ *
+ * Requests req_begin .. req_end-1, any query_len >= 0.  Request r has
+ * n = qsl[r+1] - qsl[r] new tokens and c = seq_lens[r] - n cached ones; its
+ * query i (row qsl[r] + i) attends keys 0 .. c + i (bottom-right causal: the
+ * new token sees the whole cached prefix and itself, never a later token).
+ * max_query_len and max_seq_len (host scalars, as the tour's metadata keeps
+ * them on the CPU) must bound every n and seq_len of the range; rows past
+ * max_query_len are not computed.  Output rows of other requests and padding
+ * rows are never written.  Accumulation float32; out act_dtype.
+ */
+pa_status pa_prefill_varlen(const pa_attn_desc* desc, int32_t req_begin, int32_t req_end,
+                            const void* q, int64_t q_row_stride,
+                            const int32_t* query_start_loc, const int32_t* seq_lens,
+                            const int32_t* block_tables, int32_t max_blocks_per_req,
+                            const void* key_cache, const void* value_cache, int64_t num_blocks,
+                            int32_t max_query_len, int32_t max_seq_len,
+                            void* out, int64_t out_row_stride, void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* PA_H */

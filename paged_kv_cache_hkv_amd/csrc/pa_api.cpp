@@ -1,0 +1,307 @@
+// C ABI of libpa.so (declared in include/pa.h): host-side argument checks,
+// split-K planning and kernel launches.  Every check runs before any HIP call,
+// so a rejected call enqueues nothing.
+#include "pa.h"
+
+#include <hip/hip_runtime.h>
+
+#include <cmath>
+#include <cstdint>
+
+#include "pa_kernels.h"
+
+namespace {
+
+constexpr int kBlockSize = 16;
+constexpr int kChunkPerWg = 128;          // 4 waves x 32 keys: partition granularity
+constexpr int kMaxGridYZ = 65535;
+constexpr float kLog2e = 1.4426950408889634f;
+
+bool aligned16(const void* ptr) { return (reinterpret_cast<uintptr_t>(ptr) & 15u) == 0; }
+
+int elem_bytes(int dt) { return dt == PA_FP8_E4M3 ? 1 : 2; }
+
+pa_status check_desc(const pa_attn_desc* d) {
+  if (d == nullptr) return PA_ERR_INVALID_ARG;
+  if (d->num_q_heads <= 0 || d->num_kv_heads <= 0) return PA_ERR_INVALID_ARG;
+  if (d->num_q_heads % d->num_kv_heads != 0) return PA_ERR_INVALID_ARG;
+  if (d->head_dim <= 0 || d->block_size <= 0) return PA_ERR_INVALID_ARG;
+  if (d->act_dtype != PA_F16 && d->act_dtype != PA_BF16) {
+    return d->act_dtype == PA_FP8_E4M3 ? PA_ERR_UNSUPPORTED : PA_ERR_INVALID_ARG;
+  }
+  if (d->cache_dtype != d->act_dtype && d->cache_dtype != PA_FP8_E4M3) {
+    return (d->cache_dtype == PA_F16 || d->cache_dtype == PA_BF16) ? PA_ERR_UNSUPPORTED
+                                                                  : PA_ERR_INVALID_ARG;
+  }
+  if (d->head_dim != 64 && d->head_dim != 128) return PA_ERR_UNSUPPORTED;
+  if (d->block_size != kBlockSize) return PA_ERR_UNSUPPORTED;
+  if (!std::isfinite(d->softmax_scale)) return PA_ERR_INVALID_ARG;
+  if (d->cache_dtype == PA_FP8_E4M3) {
+    if (!(d->k_scale > 0.f) || !(d->v_scale > 0.f) || !std::isfinite(d->k_scale) ||
+        !std::isfinite(d->v_scale)) {
+      return PA_ERR_INVALID_ARG;
+    }
+  }
+  if (d->decode_partition_tokens < 0 || d->decode_partition_tokens % kChunkPerWg != 0) {
+    return PA_ERR_INVALID_ARG;
+  }
+  return PA_OK;
+}
+
+// Keys per decode partition.  Every partition costs one float32 partial of
+// G*(D+2) values per K/V head, every key of it K+V bytes; the partition is
+// long enough that the partials stay near 5% of the K/V bytes, and otherwise
+// the longest (power-of-two multiple of 128 keys) that still gives about
+// 8192 workgroups, i.e. ~32 per compute unit, to balance uneven lengths.
+int plan_partition(const pa_attn_desc* d, int num_reqs, int64_t span) {
+  if (d->decode_partition_tokens > 0) return d->decode_partition_tokens;
+  const int G = d->num_q_heads / d->num_kv_heads;
+  const int e = elem_bytes(d->cache_dtype);
+  int p_min = (40 * G) / e;
+  p_min = ((p_min + kChunkPerWg - 1) / kChunkPerWg) * kChunkPerWg;
+  if (p_min < kChunkPerWg) p_min = kChunkPerWg;
+  const double work = (double)num_reqs * d->num_kv_heads * (double)span;
+  int p = kChunkPerWg;
+  while (p < 8192 && work / (2.0 * p) >= 8192.0) p *= 2;
+  return p < p_min ? p_min : p;
+}
+
+struct DecodePlan {
+  int part_tokens;
+  int max_parts;
+  size_t ws_bytes;
+};
+
+DecodePlan plan_decode(const pa_attn_desc* d, int num_reqs, int max_seq_len, int max_blocks) {
+  DecodePlan pl{};
+  const int64_t span = std::min<int64_t>((int64_t)max_seq_len, (int64_t)max_blocks * kBlockSize);
+  pl.part_tokens = plan_partition(d, num_reqs, span);
+  pl.max_parts = span <= 0 ? 0 : (int)((span + pl.part_tokens - 1) / pl.part_tokens);
+  if (pl.max_parts <= 1) {
+    pl.ws_bytes = 0;
+  } else {
+    const size_t rows = (size_t)num_reqs * d->num_q_heads * pl.max_parts;
+    pl.ws_bytes = rows * (size_t)(d->head_dim + 2) * sizeof(float) + 256;
+  }
+  return pl;
+}
+
+pa_status from_hip(hipError_t e) {
+  if (e == hipSuccess) return PA_OK;
+  if (e == hipErrorInvalidValue) return PA_ERR_UNSUPPORTED;
+  return PA_ERR_HIP;
+}
+
+float scale_log2(const pa_attn_desc* d) {
+  const float ks = d->cache_dtype == PA_FP8_E4M3 ? d->k_scale : 1.0f;
+  return d->softmax_scale * ks * kLog2e;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* pa_status_string(pa_status status) {
+  switch (status) {
+    case PA_OK: return "PA_OK";
+    case PA_ERR_INVALID_ARG: return "PA_ERR_INVALID_ARG";
+    case PA_ERR_UNSUPPORTED: return "PA_ERR_UNSUPPORTED";
+    case PA_ERR_WORKSPACE_TOO_SMALL: return "PA_ERR_WORKSPACE_TOO_SMALL";
+    case PA_ERR_HIP: return "PA_ERR_HIP";
+  }
+  return "PA_ERR_UNKNOWN";
+}
+
+pa_status pa_metadata_build(int32_t num_reqs, int32_t block_size, int32_t max_blocks_per_req,
+                            int32_t num_tokens_padded, int32_t qsl_len,
+                            const int32_t* num_computed_tokens, const int32_t* query_lens,
+                            const int32_t* block_tables, int32_t* query_start_loc,
+                            int32_t* seq_lens, int64_t* positions, int64_t* slot_mapping,
+                            void* stream) {
+  if (num_reqs < 0 || block_size <= 0 || max_blocks_per_req < 0 || num_tokens_padded < 0) {
+    return PA_ERR_INVALID_ARG;
+  }
+  if (qsl_len < num_reqs + 1) return PA_ERR_INVALID_ARG;
+  if (query_start_loc == nullptr) return PA_ERR_INVALID_ARG;
+  if (num_reqs > 0 && (num_computed_tokens == nullptr || query_lens == nullptr ||
+                       seq_lens == nullptr)) {
+    return PA_ERR_INVALID_ARG;
+  }
+  if (num_reqs > 0 && max_blocks_per_req > 0 && block_tables == nullptr) return PA_ERR_INVALID_ARG;
+  if (num_tokens_padded > 0 && (positions == nullptr || slot_mapping == nullptr)) {
+    return PA_ERR_INVALID_ARG;
+  }
+  pa::MetadataParams p{};
+  p.num_reqs = num_reqs;
+  p.block_size = block_size;
+  p.max_blocks_per_req = max_blocks_per_req;
+  p.num_tokens_padded = num_tokens_padded;
+  p.qsl_len = qsl_len;
+  p.num_computed = num_computed_tokens;
+  p.query_lens = query_lens;
+  p.block_tables = block_tables;
+  p.qsl = query_start_loc;
+  p.seq_lens = seq_lens;
+  p.positions = positions;
+  p.slot_mapping = slot_mapping;
+  return from_hip(pa::launch_metadata(p, static_cast<hipStream_t>(stream)));
+}
+
+pa_status pa_cache_write(const pa_attn_desc* desc, int64_t num_tokens, const void* key,
+                         int64_t key_row_stride, const void* value, int64_t value_row_stride,
+                         const int64_t* slot_mapping, void* key_cache, void* value_cache,
+                         int64_t num_blocks, void* stream) {
+  pa_status st = check_desc(desc);
+  if (st != PA_OK) return st;
+  if (num_tokens < 0 || num_blocks < 0) return PA_ERR_INVALID_ARG;
+  if (num_tokens == 0) return PA_OK;
+  if (!key || !value || !slot_mapping || !key_cache || !value_cache) return PA_ERR_INVALID_ARG;
+  const int64_t row = (int64_t)desc->num_kv_heads * desc->head_dim;
+  if (key_row_stride < row || value_row_stride < row) return PA_ERR_INVALID_ARG;
+  if (!aligned16(key) || !aligned16(value) || !aligned16(key_cache) || !aligned16(value_cache)) {
+    return PA_ERR_INVALID_ARG;
+  }
+  if ((key_row_stride * 2) % 16 != 0 || (value_row_stride * 2) % 16 != 0) return PA_ERR_INVALID_ARG;
+  if (num_tokens * (row / 8) > (int64_t)0x7FFFFFFF * 256) return PA_ERR_UNSUPPORTED;
+  pa::CacheWriteParams p{};
+  p.num_tokens = num_tokens;
+  p.row_elems = (int32_t)row;
+  p.block_size = desc->block_size;
+  p.key = key;
+  p.value = value;
+  p.key_row_stride = key_row_stride;
+  p.value_row_stride = value_row_stride;
+  p.slot_mapping = slot_mapping;
+  p.key_cache = key_cache;
+  p.value_cache = value_cache;
+  p.num_slots = num_blocks * desc->block_size;
+  p.k_inv_scale = desc->cache_dtype == PA_FP8_E4M3 ? 1.0f / desc->k_scale : 1.0f;
+  p.v_inv_scale = desc->cache_dtype == PA_FP8_E4M3 ? 1.0f / desc->v_scale : 1.0f;
+  return from_hip(pa::launch_cache_write(p, desc->act_dtype, desc->cache_dtype,
+                                         static_cast<hipStream_t>(stream)));
+}
+
+static pa_status check_attn_common(const pa_attn_desc* desc, int32_t req_begin, int32_t req_end,
+                                   const void* q, int64_t q_row_stride,
+                                   const int32_t* query_start_loc, const int32_t* seq_lens,
+                                   const int32_t* block_tables, int32_t max_blocks_per_req,
+                                   const void* key_cache, const void* value_cache,
+                                   int64_t num_blocks, const void* out, int64_t out_row_stride) {
+  pa_status st = check_desc(desc);
+  if (st != PA_OK) return st;
+  if (req_begin < 0 || req_end < req_begin) return PA_ERR_INVALID_ARG;
+  if (req_end - req_begin > kMaxGridYZ) return PA_ERR_UNSUPPORTED;
+  if (req_end == req_begin) return PA_OK;
+  if (!q || !query_start_loc || !seq_lens || !block_tables || !key_cache || !value_cache || !out) {
+    return PA_ERR_INVALID_ARG;
+  }
+  if (max_blocks_per_req <= 0 || num_blocks <= 0) return PA_ERR_INVALID_ARG;
+  const int64_t row = (int64_t)desc->num_q_heads * desc->head_dim;
+  if (q_row_stride < row || out_row_stride < row) return PA_ERR_INVALID_ARG;
+  if (!aligned16(q) || !aligned16(out) || !aligned16(key_cache) || !aligned16(value_cache)) {
+    return PA_ERR_INVALID_ARG;
+  }
+  if ((q_row_stride * 2) % 16 != 0 || (out_row_stride * 2) % 16 != 0) return PA_ERR_INVALID_ARG;
+  return PA_OK;
+}
+
+static pa::AttnParams make_params(const pa_attn_desc* desc, int32_t req_begin, int32_t req_end,
+                                  const void* q, int64_t q_row_stride,
+                                  const int32_t* query_start_loc, const int32_t* seq_lens,
+                                  const int32_t* block_tables, int32_t max_blocks_per_req,
+                                  const void* key_cache, const void* value_cache,
+                                  int64_t num_blocks, void* out, int64_t out_row_stride) {
+  pa::AttnParams p{};
+  p.num_q_heads = desc->num_q_heads;
+  p.num_kv_heads = desc->num_kv_heads;
+  p.group = desc->num_q_heads / desc->num_kv_heads;
+  p.head_dim = desc->head_dim;
+  p.req_begin = req_begin;
+  p.num_reqs = req_end - req_begin;
+  p.qsl = query_start_loc;
+  p.seq_lens = seq_lens;
+  p.block_tables = block_tables;
+  p.max_blocks_per_req = max_blocks_per_req;
+  p.q = q;
+  p.q_row_stride = q_row_stride;
+  p.key_cache = key_cache;
+  p.value_cache = value_cache;
+  p.num_blocks = num_blocks;
+  p.out = out;
+  p.out_row_stride = out_row_stride;
+  p.scale_log2 = scale_log2(desc);
+  p.v_scale = desc->cache_dtype == PA_FP8_E4M3 ? desc->v_scale : 1.0f;
+  return p;
+}
+
+pa_status pa_decode_workspace_size(const pa_attn_desc* desc, int32_t num_reqs,
+                                   int32_t max_seq_len, int32_t max_blocks_per_req,
+                                   size_t* bytes) {
+  pa_status st = check_desc(desc);
+  if (st != PA_OK) return st;
+  if (bytes == nullptr || num_reqs < 0 || max_seq_len < 0 || max_blocks_per_req < 0) {
+    return PA_ERR_INVALID_ARG;
+  }
+  if (desc->num_q_heads / desc->num_kv_heads > 32) return PA_ERR_UNSUPPORTED;
+  *bytes = plan_decode(desc, num_reqs, max_seq_len, max_blocks_per_req).ws_bytes;
+  return PA_OK;
+}
+
+pa_status pa_decode(const pa_attn_desc* desc, int32_t req_begin, int32_t req_end, const void* q,
+                    int64_t q_row_stride, const int32_t* query_start_loc, const int32_t* seq_lens,
+                    const int32_t* block_tables, int32_t max_blocks_per_req,
+                    const void* key_cache, const void* value_cache, int64_t num_blocks,
+                    int32_t max_seq_len, void* workspace, size_t workspace_bytes, void* out,
+                    int64_t out_row_stride, void* stream) {
+  pa_status st = check_attn_common(desc, req_begin, req_end, q, q_row_stride, query_start_loc,
+                                   seq_lens, block_tables, max_blocks_per_req, key_cache,
+                                   value_cache, num_blocks, out, out_row_stride);
+  if (st != PA_OK) return st;
+  if (max_seq_len < 0) return PA_ERR_INVALID_ARG;
+  if (desc->num_q_heads / desc->num_kv_heads > 32) return PA_ERR_UNSUPPORTED;
+  const int num_reqs = req_end - req_begin;
+  if (num_reqs == 0) return PA_OK;
+  const DecodePlan pl = plan_decode(desc, num_reqs, max_seq_len, max_blocks_per_req);
+  if (pl.max_parts == 0) return PA_OK;
+  if (pl.ws_bytes > 0) {
+    if (workspace == nullptr || workspace_bytes < pl.ws_bytes) return PA_ERR_WORKSPACE_TOO_SMALL;
+    if (!aligned16(workspace)) return PA_ERR_INVALID_ARG;
+  }
+  pa::AttnParams p = make_params(desc, req_begin, req_end, q, q_row_stride, query_start_loc,
+                                 seq_lens, block_tables, max_blocks_per_req, key_cache,
+                                 value_cache, num_blocks, out, out_row_stride);
+  p.max_seq_len = max_seq_len;
+  p.part_tokens = pl.part_tokens;
+  p.max_parts = pl.max_parts;
+  if (pl.ws_bytes > 0) {
+    const size_t acc_elems = (size_t)num_reqs * desc->num_q_heads * pl.max_parts * desc->head_dim;
+    p.ws_acc = static_cast<float*>(workspace);
+    p.ws_ml = static_cast<float*>(workspace) + acc_elems;
+  }
+  return from_hip(pa::launch_decode(p, desc->act_dtype, desc->cache_dtype,
+                                    static_cast<hipStream_t>(stream)));
+}
+
+pa_status pa_prefill_varlen(const pa_attn_desc* desc, int32_t req_begin, int32_t req_end,
+                            const void* q, int64_t q_row_stride, const int32_t* query_start_loc,
+                            const int32_t* seq_lens, const int32_t* block_tables,
+                            int32_t max_blocks_per_req, const void* key_cache,
+                            const void* value_cache, int64_t num_blocks, int32_t max_query_len,
+                            int32_t max_seq_len, void* out, int64_t out_row_stride,
+                            void* stream) {
+  pa_status st = check_attn_common(desc, req_begin, req_end, q, q_row_stride, query_start_loc,
+                                   seq_lens, block_tables, max_blocks_per_req, key_cache,
+                                   value_cache, num_blocks, out, out_row_stride);
+  if (st != PA_OK) return st;
+  if (max_query_len < 0 || max_seq_len < 0) return PA_ERR_INVALID_ARG;
+  if (req_end == req_begin || max_query_len == 0) return PA_OK;
+  pa::AttnParams p = make_params(desc, req_begin, req_end, q, q_row_stride, query_start_loc,
+                                 seq_lens, block_tables, max_blocks_per_req, key_cache,
+                                 value_cache, num_blocks, out, out_row_stride);
+  p.max_seq_len = max_seq_len;
+  p.max_query_len = max_query_len;
+  return from_hip(pa::launch_prefill(p, desc->act_dtype, desc->cache_dtype,
+                                     static_cast<hipStream_t>(stream)));
+}
+
+}  // extern "C"

@@ -1,0 +1,107 @@
+// Device-side building blocks shared by the paged-attention kernels (gfx950).
+//
+// Wave64 everywhere.  MFMA operand layouts used below (CDNA3/CDNA4 matrix
+// cores, lane l of a wave):
+//   v_mfma_f32_16x16x32_{bf16,f16}: A[i][k] in lane (i + 16*(k/8)), element k%8;
+//     B[k][j] in lane (j + 16*(k/8)), element k%8; D[i][j] in lane (j + 16*(i/4)),
+//     register i%4.
+//   v_mfma_f32_32x32x16_{bf16,f16}: A[i][k] in lane (i + 32*(k/8)), element k%8;
+//     B[k][j] in lane (j + 32*(k/8)), element k%8; D[i][j] in lane (j + 32*((i/4)%2)),
+//     register 4*(i/8) + i%4.
+// Only the D layout matters for correctness of a product whose K ordering is a
+// permutation both operands share; every kernel here builds A and B with the
+// same K permutation.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace pa {
+
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef unsigned u32x2 __attribute__((ext_vector_type(2)));
+typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
+
+constexpr float kLog2e = 1.4426950408889634f;
+
+// ---- compute-type traits: bf16 or fp16 MFMA --------------------------------
+template <typename T> struct Mfma;
+
+template <> struct Mfma<__bf16> {
+  typedef bf16x8 vec8;
+  __device__ static inline f32x4 mma16(const vec8& a, const vec8& b, const f32x4& c) {
+    return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
+  }
+  __device__ static inline f32x16 mma32(const vec8& a, const vec8& b, const f32x16& c) {
+    return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
+  }
+  // two fp8 (e4m3fn) codes from 16-bit word `word` of `src` -> two exact values
+  __device__ static inline unsigned from_fp8x2(unsigned src, bool hi_word) {
+    bf16x2 v = hi_word ? __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(src, 1.0f, true)
+                       : __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(src, 1.0f, false);
+    return __builtin_bit_cast(unsigned, v);
+  }
+  __device__ static inline unsigned short from_float(float f) {
+    return __builtin_bit_cast(unsigned short, (__bf16)f);
+  }
+  __device__ static inline float to_float(unsigned short b) {
+    return __builtin_bit_cast(float, ((unsigned)b) << 16);
+  }
+};
+
+template <> struct Mfma<_Float16> {
+  typedef f16x8 vec8;
+  __device__ static inline f32x4 mma16(const vec8& a, const vec8& b, const f32x4& c) {
+    return __builtin_amdgcn_mfma_f32_16x16x32_f16(a, b, c, 0, 0, 0);
+  }
+  __device__ static inline f32x16 mma32(const vec8& a, const vec8& b, const f32x16& c) {
+    return __builtin_amdgcn_mfma_f32_32x32x16_f16(a, b, c, 0, 0, 0);
+  }
+  __device__ static inline unsigned from_fp8x2(unsigned src, bool hi_word) {
+    f16x2 v = hi_word ? __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(src, 1.0f, true)
+                      : __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(src, 1.0f, false);
+    return __builtin_bit_cast(unsigned, v);
+  }
+  __device__ static inline unsigned short from_float(float f) {
+    return __builtin_bit_cast(unsigned short, (_Float16)f);
+  }
+  __device__ static inline float to_float(unsigned short b) {
+    return (float)__builtin_bit_cast(_Float16, b);
+  }
+};
+
+// Pack two floats into one dword of two 16-bit compute-type values (lo, hi).
+template <typename T>
+__device__ inline unsigned pack2(float lo, float hi) {
+  return (unsigned)Mfma<T>::from_float(lo) | ((unsigned)Mfma<T>::from_float(hi) << 16);
+}
+
+// Byte permute: result byte k = byte sel.k of the 8-byte value {hi:lo}.
+__device__ inline unsigned perm(unsigned hi, unsigned lo, unsigned sel) {
+  return __builtin_amdgcn_perm(hi, lo, sel);
+}
+
+// Wave-wide shuffles (ds_bpermute based).
+__device__ inline float shfl(float v, int src_lane) {
+  return __builtin_bit_cast(float, __builtin_amdgcn_ds_bpermute(src_lane << 2, __builtin_bit_cast(int, v)));
+}
+__device__ inline float shfl_xor(float v, int mask) {
+  int lane = __lane_id();
+  return shfl(v, lane ^ mask);
+}
+
+__device__ inline int wave_uniform(int v) { return __builtin_amdgcn_readfirstlane(v); }
+
+// 16-byte and 8-byte global loads / stores.
+__device__ inline u32x4 ld16(const void* p) { return *reinterpret_cast<const u32x4*>(p); }
+__device__ inline u32x2 ld8(const void* p) { return *reinterpret_cast<const u32x2*>(p); }
+__device__ inline unsigned ld4(const void* p) { return *reinterpret_cast<const unsigned*>(p); }
+__device__ inline void st16(void* p, u32x4 v) { *reinterpret_cast<u32x4*>(p) = v; }
+__device__ inline void st8(void* p, u32x2 v) { *reinterpret_cast<u32x2*>(p) = v; }
+
+}  // namespace pa

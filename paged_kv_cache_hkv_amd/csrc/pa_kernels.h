@@ -1,0 +1,74 @@
+// Launch parameters and launchers of the paged-attention kernels (internal to
+// libpa.so; the C ABI in include/pa.h validates arguments and calls these).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace pa {
+
+enum DType : int { kF16 = 0, kBF16 = 1, kFP8 = 2 };
+
+struct MetadataParams {
+  int32_t num_reqs, block_size, max_blocks_per_req, num_tokens_padded, qsl_len;
+  const int32_t* num_computed;
+  const int32_t* query_lens;
+  const int32_t* block_tables;
+  int32_t* qsl;
+  int32_t* seq_lens;
+  int64_t* positions;
+  int64_t* slot_mapping;
+};
+
+struct CacheWriteParams {
+  int64_t num_tokens;
+  int32_t row_elems;       // num_kv_heads * head_dim
+  int32_t block_size;
+  const void* key;
+  const void* value;
+  int64_t key_row_stride;  // elements
+  int64_t value_row_stride;
+  const int64_t* slot_mapping;
+  void* key_cache;
+  void* value_cache;
+  int64_t num_slots;       // num_blocks * block_size
+  float k_inv_scale, v_inv_scale;  // fp8 only
+};
+
+struct AttnParams {
+  // geometry
+  int32_t num_q_heads, num_kv_heads, group, head_dim;
+  // requests
+  int32_t req_begin, num_reqs;
+  const int32_t* qsl;
+  const int32_t* seq_lens;
+  const int32_t* block_tables;
+  int32_t max_blocks_per_req;
+  // tensors
+  const void* q;
+  int64_t q_row_stride;
+  const void* key_cache;
+  const void* value_cache;
+  int64_t num_blocks;
+  void* out;
+  int64_t out_row_stride;
+  // scalars
+  float scale_log2;   // softmax_scale * k_scale * log2(e)
+  float v_scale;      // 1 unless the cache is fp8
+  int32_t max_seq_len;
+  int32_t max_query_len;
+  // decode split-K
+  int32_t part_tokens;
+  int32_t max_parts;
+  float* ws_acc;      // [num_reqs, Hq, max_parts, D]
+  float* ws_ml;       // [num_reqs, Hq, max_parts, 2]
+};
+
+hipError_t launch_metadata(const MetadataParams& p, hipStream_t stream);
+hipError_t launch_cache_write(const CacheWriteParams& p, int act_dtype, int cache_dtype,
+                              hipStream_t stream);
+// Returns hipErrorInvalidValue for a combination no kernel is built for.
+hipError_t launch_decode(const AttnParams& p, int act_dtype, int cache_dtype, hipStream_t stream);
+hipError_t launch_prefill(const AttnParams& p, int act_dtype, int cache_dtype, hipStream_t stream);
+
+}  // namespace pa
