@@ -1,0 +1,257 @@
+"""Benchmark of the paged-attention hot path on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--config decode_mha]
+                    [--no-extra] [--no-cpu]
+
+A step is one pass of the whole path over one synthetic batch: metadata
+build, cache write of the step's new K/V, decode attention, varlen prefill
+attention (whichever the batch has).  The headline workload is the 64-request
+MHA decode batch (contexts uniform in 512..4096, 32/32 heads, head_dim 128,
+fp16, 65536-block pool).  ``value`` is its KV GB/s: every K/V byte each
+decode request must read (seq_len * Hkv * D * 2 * bytes, counted once per
+request) divided by the step time, inputs resident in HBM.
+
+Also reported on the same JSON line:
+* ``roofline`` of the dominant kernel (the decode call: split kernel plus its
+  reduce), timed live with HIP events on the launch stream;
+* ``cpu_baseline``: the oracle on the host cores over a bounded sample of the
+  same batch;
+* ``extra``: the other measured workloads (GQA decode, chunked-prefill mix,
+  long-context fp8 MQA decode), each call timed with events between 1 GiB
+  cache-flush writes.
+"""
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+import numpy as np
+import torch
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+from paged_kv_cache_hkv_amd import binding as B  # noqa: E402
+from paged_kv_cache_hkv_amd import synth as S  # noqa: E402
+from paged_kv_cache_hkv_amd.step import PagedAttentionStep  # noqa: E402
+
+HBM_PEAK_GBS = 8000.0          # MI355X HBM3E
+BF16_PEAK_TFLOPS = 2500.0      # MI355X dense bf16/fp16 MFMA
+DECODE_SRC = os.path.join(ROOT, "paged_kv_cache_hkv_amd", "csrc", "pa_decode.hip")
+PREFILL_SRC = os.path.join(ROOT, "paged_kv_cache_hkv_amd", "csrc", "pa_prefill.hip")
+
+
+def kv_bytes(wl, reqs):
+    e = 1 if wl.cache_fp8 else 2
+    s = wl.seq_lens_host[list(reqs)].astype(np.int64)
+    return int(s.sum()) * wl.num_kv_heads * wl.head_dim * 2 * e
+
+
+def prefill_flops(wl, reqs):
+    tot = 0
+    for r in reqs:
+        n = int(wl.query_lens[r])
+        c = int(wl.num_computed[r])
+        tot += 4 * wl.num_q_heads * wl.head_dim * (n * c + n * (n + 1) // 2)
+    return tot
+
+
+def src_sha(path):
+    with open(path, "rb") as f:
+        return hashlib.sha256(f.read()).hexdigest()[:16]
+
+
+def read_traffic(name, kernel_src):
+    """HBM bytes per launch from committed rocprofv3 counter runs, if still current."""
+    path = os.path.join(ROOT, "profiles", f"{name}_traffic.json")
+    if not os.path.exists(path):
+        return None
+    with open(path) as f:
+        rec = json.load(f)
+    if rec.get("kernel_src_sha") != src_sha(kernel_src):
+        return None
+    return rec.get("hbm_bytes_per_launch")
+
+
+def time_calls(fn_list, iters, flush):
+    """Median / p10 / p90 milliseconds of each callable, events on the current stream."""
+    stream = torch.cuda.current_stream()
+    res = [[] for _ in fn_list]
+    for _ in range(iters):
+        flush.add_(1)                   # evict L2 and the 256 MB last-level cache
+        for i, fn in enumerate(fn_list):
+            a = torch.cuda.Event(enable_timing=True)
+            b = torch.cuda.Event(enable_timing=True)
+            a.record(stream)
+            fn()
+            b.record(stream)
+            res[i].append((a, b))
+    torch.cuda.synchronize()
+    out = []
+    for pairs in res:
+        ms = np.array([a.elapsed_time(b) for a, b in pairs])
+        out.append((float(np.median(ms)), float(np.percentile(ms, 10)),
+                    float(np.percentile(ms, 90))))
+    return out
+
+
+def bench_extra(name, iters, flush):
+    wl = S.CONFIGS[name]()
+    t = S.make_tensors(wl, "cuda", poison=False)
+    st = PagedAttentionStep(wl, t)
+    st.run()
+    torch.cuda.synchronize()
+    rec = {"workload": name, "requests": wl.num_reqs, "decodes": wl.num_decodes,
+           "tokens": wl.num_tokens}
+    fns, names = [], []
+    if wl.num_decodes:
+        fns.append(st.decode)
+        names.append("decode")
+    if wl.num_reqs > wl.num_decodes:
+        fns.append(st.prefill)
+        names.append("prefill")
+    fns.append(st.cache_write)
+    names.append("cache_write")
+    for _ in range(3):
+        for f in fns:
+            f()
+    times = time_calls(fns, iters, flush)
+    for nm, (med, p10, p90) in zip(names, times):
+        rec[f"{nm}_ms"] = round(med, 4)
+        rec[f"{nm}_ms_p10_p90"] = [round(p10, 4), round(p90, 4)]
+    if wl.num_decodes:
+        kb = kv_bytes(wl, range(wl.num_decodes))
+        gbs = kb / (rec["decode_ms"] * 1e-3) / 1e9
+        rec["decode_kv_bytes"] = kb
+        rec["decode_kv_GBps"] = round(gbs, 1)
+        rec["decode_hbm_frac"] = round(gbs / HBM_PEAK_GBS, 4)
+    if wl.num_reqs > wl.num_decodes:
+        pre = range(wl.num_decodes, wl.num_reqs)
+        fl = prefill_flops(wl, pre)
+        toks = int(wl.query_lens[wl.num_decodes:].sum())
+        sec = rec["prefill_ms"] * 1e-3
+        rec["prefill_flops"] = fl
+        rec["prefill_tok_per_s"] = round(toks / sec, 1)
+        rec["prefill_TFLOPs"] = round(fl / sec / 1e12, 1)
+        rec["prefill_mfma_frac"] = round(fl / sec / 1e12 / BF16_PEAK_TFLOPS, 4)
+    del st, t
+    torch.cuda.empty_cache()
+    return rec
+
+
+def take_snapshot(wl, t):
+    """Host copy of the decode requests' blocks as drawn, before any kernel runs."""
+    sys.path.insert(0, os.path.join(ROOT, "tests"))
+    from harness import Snapshot   # test infrastructure
+    return Snapshot(wl, t, list(range(wl.num_decodes)))
+
+
+def cpu_baseline(wl, t, snap, budget_s=12.0):
+    """The oracle (as it stands) on the host, over the batch's requests in order."""
+    from harness import oracle_outputs   # test infrastructure: the oracle
+    reqs_all = list(range(wl.num_decodes))
+    done, spent, kb = 0, 0.0, 0
+    chunk = 4
+    while done < len(reqs_all) and spent < budget_s:
+        req = reqs_all[done:done + chunk]
+        t0 = time.perf_counter()
+        oracle_outputs(wl, t, snap, req)
+        spent += time.perf_counter() - t0
+        kb += kv_bytes(wl, req)
+        done += len(req)
+    return {"value": round(kb / spent / 1e9, 4), "unit": "GB/s", "cores": torch.get_num_threads(),
+            "kind": "oracle",
+            "sample": f"first {done} of {len(reqs_all)} decode requests of {wl.name} "
+                      f"({kb} KV bytes, {spent:.1f} s, NumPy float64)"}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--config", default="decode_mha")
+    ap.add_argument("--extra-iters", type=int, default=20)
+    ap.add_argument("--no-extra", action="store_true")
+    ap.add_argument("--no-cpu", action="store_true")
+    args = ap.parse_args()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
+        print("bench.py measures one GPU only: this path has no multi-GPU mode "
+              "(each GPU would run the same kernels on its own share of requests or heads)",
+              file=sys.stderr)
+        sys.exit(2)
+    B.load()
+    torch.cuda.init()
+    wl = S.CONFIGS[args.config]()
+    t = S.make_tensors(wl, "cuda", poison=False)
+    snap = None if args.no_cpu else take_snapshot(wl, t)
+    st = PagedAttentionStep(wl, t)
+    stream = torch.cuda.current_stream()
+    for _ in range(args.warmup):
+        st.run()
+    torch.cuda.synchronize()
+
+    ev = []
+    t0 = time.perf_counter()
+    for _ in range(args.steps):
+        st.metadata()
+        st.cache_write()
+        a = torch.cuda.Event(enable_timing=True)
+        b = torch.cuda.Event(enable_timing=True)
+        a.record(stream)
+        st.decode()
+        b.record(stream)
+        st.prefill()
+        ev.append((a, b))
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    ms_step = wall / args.steps * 1e3
+    dec_ms = float(np.mean([a.elapsed_time(b) for a, b in ev]))
+
+    kb = kv_bytes(wl, range(wl.num_decodes))
+    value = kb / (ms_step * 1e-3) / 1e9
+    achieved = kb / (dec_ms * 1e-3) / 1e9
+    line = {
+        "metric": "paged decode attn achieved KV GB/s (% HBM peak) + prefill query tok/s (% MFMA)",
+        "value": round(value, 1),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f16" if wl.act_dtype == torch.float16 else "bf16",
+        "data": "synthetic",
+        "config": {"workload": wl.name, "requests": wl.num_reqs, "decodes": wl.num_decodes,
+                   "num_q_heads": wl.num_q_heads, "num_kv_heads": wl.num_kv_heads,
+                   "head_dim": wl.head_dim, "block_size": wl.block_size,
+                   "pool_blocks": wl.pool_blocks, "kv_bytes_per_step": kb,
+                   "step": "metadata + cache_write + decode (+ prefill when present)",
+                   "parallelism": "single GPU"},
+        "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS,
+                     "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
+                     "traffic": read_traffic(wl.name + "_decode", DECODE_SRC),
+                     "kernel": "pa_decode (decode_kernel + decode_reduce_kernel)",
+                     "kernel_ms": round(dec_ms, 4)},
+    }
+    if not args.no_extra:
+        del st
+        flush = torch.empty(1 << 28, dtype=torch.float32, device="cuda")
+        extra = []
+        for name in ("decode_gqa", "chunked_prefill_mix", "mqa_fp8_long"):
+            extra.append(bench_extra(name, args.extra_iters, flush))
+            print(f"# {json.dumps(extra[-1])}", file=sys.stderr, flush=True)
+        line["extra"] = extra
+        del flush
+    if not args.no_cpu:
+        line["cpu_baseline"] = cpu_baseline(wl, t, snap)
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()
