@@ -10,20 +10,27 @@
 // tile in registers and LDS ("vLLM 推理全流程深度解析", FlashAttention keeps
 // softmax and matmul in on-chip memory and never writes the score matrix out).
 //
-// Work decomposition.  A workgroup of 4 waves owns (request, K/V head, group
-// of `hpw` query heads of that K/V head, tile of 128/hpw queries); wave w
-// takes query head w % hpw and 32 queries.  All 4 waves share each 64-key
-// K/V tile, staged through LDS:
-//   * Ks[key][d] row-major (row padded by 16 bytes, conflict-free 16-byte
-//     reads of 32 different rows);
+// Work decomposition.  A workgroup of 4 waves owns (request, group of `hpw`
+// query heads sharing one K/V head, tile of 128/hpw queries); wave w takes
+// query head w % hpw and 32 queries.  Tiles are numbered from the END of each
+// request and dispatched in that order, so the tiles with the most keys start
+// first (longest-first scheduling over uneven chunks).  All 4 waves share each
+// 64-key K/V tile, double-buffered in LDS (one barrier per tile):
+//   * Ks[key][d] row-major, rows padded by 16 bytes: the 16-byte reads of 32
+//     different rows hit distinct banks;
 //   * Vt[d][key'] transposed, key' = key with bits 2 and 3 swapped, so the 8
 //     keys one lane feeds into one MFMA step are adjacent (one 16-byte read).
+//     Each thread moves 4 consecutive keys x 8 d and writes 8-byte rows, so
+//     the transposing stores are free of bank conflicts too.
 // Per tile a wave computes S^T = K . Q^T (v_mfma_f32_32x32x16, keys x queries)
 // so each lane holds 32 scores of ONE query: the row max needs one exchange
-// with the lane 32 apart and the rescale of the O^T accumulator is
-// lane-local.  The scores, as bf16/fp16, are directly the B operand of
-// O^T = V^T . P^T.  The next tile's global loads are issued before the
-// current tile's math, into registers, and written to LDS after it.
+// with the lane 32 apart and every rescale is lane-local.  The probabilities,
+// rounded to bf16/fp16, are directly the B operand of O^T = V^T . P^T.
+// Softmax in exp2 form with the scale folded into one FMA; the accumulator is
+// only rescaled when a row's running max grows by more than 2^8 (exact up to
+// rounding: the reference max of a softmax is arbitrary as long as nothing
+// overflows).  The next tile's global loads are issued before the current
+// tile's math and land in the other LDS buffer after it.
 // fp8 caches are widened to bf16/fp16 when the tile is written to LDS.
 #include "pa_device.h"
 #include "pa_kernels.h"
@@ -35,138 +42,179 @@ namespace {
 constexpr int kWaves = 4;
 constexpr int kThreads = 64 * kWaves;
 constexpr int kBlock = 16;
-constexpr int kTileK = 64;   // keys per LDS tile
+constexpr int kTileK = 64;          // keys per LDS tile
+constexpr float kRescaleLog2 = 8.f; // lazy rescale threshold (log2 units)
 
 __device__ inline int swap_bits23(int k) {
   return (k & ~0xC) | ((k & 0x4) << 1) | ((k & 0x8) >> 1);
 }
 
-template <int D, typename CT, int KVB>
-struct TileRegs {
-  // 16-byte chunks of K and V this thread moves per tile
-  static constexpr int kElemsPerChunk = 16 / KVB;                 // 8 (2-byte) or 16 (fp8)
-  static constexpr int kChunksPerRow = D / kElemsPerChunk;
-  static constexpr int kChunks = kTileK * kChunksPerRow / kThreads;
-  u32x4 k[kChunks];
-  u32x4 v[kChunks];
+template <int D, int KVB>
+struct TileShape {
+  static constexpr int kElems = 16 / KVB;                 // cache elements per 16-byte chunk
+  static constexpr int kChunksPerRow = D / kElems;
+  static constexpr int kKChunks = kTileK * kChunksPerRow;  // K chunks per tile
+  static constexpr int kKPerThread = (kKChunks + kThreads - 1) / kThreads;
+  static constexpr int kVUnits = (kTileK / 4) * kChunksPerRow;  // (4 keys x 1 chunk) units
+  static constexpr int kVPerThread = (kVUnits + kThreads - 1) / kThreads;
+  static constexpr int KROW = D + 8;        // Ks row stride (elements)
+  static constexpr int VROW = kTileK + 8;   // Vt row stride (elements)
+  static constexpr int kKsElems = kTileK * KROW;
+  static constexpr int kVtElems = D * VROW;
 };
 
-template <int D, typename CT, int KVB>
-__device__ inline void load_tile(TileRegs<D, CT, KVB>& regs, const AttnParams& p,
-                                 const int32_t* bt_row, int nblk, int s_eff, int kt, int kvh) {
-  using R = TileRegs<D, CT, KVB>;
-  const unsigned char* kc = static_cast<const unsigned char*>(p.key_cache);
-  const unsigned char* vc = static_cast<const unsigned char*>(p.value_cache);
-  const int64_t tok_stride = (int64_t)p.num_kv_heads * D * KVB;
-  const int64_t blk_stride = tok_stride * kBlock;
+template <int D, int KVB>
+struct TileRegs {
+  using TS = TileShape<D, KVB>;
+  u32x4 k[TS::kKPerThread];
+  u32x4 v[TS::kVPerThread][4];
+};
+
+struct TileCtx {
+  const unsigned char* kc;
+  const unsigned char* vc;
+  const int32_t* bt_row;
+  int64_t tok_stride, blk_stride, head_off, num_blocks;
+  int nblk, s_eff;
+};
+
+// Byte offset of (logical key, chunk) in the cache, or -1 if the key is absent.
+template <int KVB>
+__device__ inline int64_t key_offset(const TileCtx& c, int key, int chunk) {
+  if (key >= c.s_eff) return -1;
+  const int bi = key / kBlock;
+  if (bi >= c.nblk) return -1;
+  const int b = c.bt_row[bi];
+  if (b < 0 || (int64_t)b >= c.num_blocks) return -1;
+  return (int64_t)b * c.blk_stride + (int64_t)(key % kBlock) * c.tok_stride + c.head_off +
+         (int64_t)chunk * 16;
+}
+
+template <int D, int KVB>
+__device__ inline void load_tile(TileRegs<D, KVB>& regs, const TileCtx& c, int kt) {
+  using TS = TileShape<D, KVB>;
+  const int key0 = kt * kTileK;
 #pragma unroll
-  for (int c = 0; c < R::kChunks; ++c) {
-    const int idx = threadIdx.x + kThreads * c;
-    const int key = idx / R::kChunksPerRow;
-    const int dc = idx % R::kChunksPerRow;
-    const int bi = kt * (kTileK / kBlock) + key / kBlock;
-    int b = -1;
-    if (bi < nblk) b = bt_row[bi];
-    // keys past the sequence may hold anything (the tail of the last block):
-    // load zeros so that 0-probability keys cannot turn P.V into NaN
-    if (b >= 0 && (int64_t)b < p.num_blocks && kt * kTileK + key < s_eff) {
-      const int64_t off = (int64_t)b * blk_stride + (int64_t)(key % kBlock) * tok_stride +
-                          (int64_t)kvh * D * KVB + (int64_t)dc * 16;
-      regs.k[c] = ld16(kc + off);
-      regs.v[c] = ld16(vc + off);
-    } else {
-      regs.k[c] = u32x4{0u, 0u, 0u, 0u};   // absent block: zeros, and masked
-      regs.v[c] = u32x4{0u, 0u, 0u, 0u};
+  for (int j = 0; j < TS::kKPerThread; ++j) {
+    const int idx = threadIdx.x + kThreads * j;
+    u32x4 v = {0u, 0u, 0u, 0u};
+    if (idx < TS::kKChunks) {
+      const int64_t off = key_offset<KVB>(c, key0 + idx / TS::kChunksPerRow, idx % TS::kChunksPerRow);
+      if (off >= 0) v = ld16(c.kc + off);   // absent keys load zeros (and are masked)
+    }
+    regs.k[j] = v;
+  }
+#pragma unroll
+  for (int j = 0; j < TS::kVPerThread; ++j) {
+    const int u = threadIdx.x + kThreads * j;
+    const int kg = u % 16, ch = u / 16;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      u32x4 v = {0u, 0u, 0u, 0u};
+      if (u < TS::kVUnits) {
+        const int64_t off = key_offset<KVB>(c, key0 + 4 * kg + i, ch);
+        if (off >= 0) v = ld16(c.vc + off);   // zeros keep 0-probability keys from making NaN
+      }
+      regs.v[j][i] = v;
     }
   }
 }
 
 template <int D, typename CT, int KVB>
-__device__ inline void store_tile(const TileRegs<D, CT, KVB>& regs, unsigned short* Ks,
+__device__ inline void store_tile(const TileRegs<D, KVB>& regs, unsigned short* Ks,
                                   unsigned short* Vt) {
-  using R = TileRegs<D, CT, KVB>;
+  using TS = TileShape<D, KVB>;
   using M = Mfma<CT>;
-  constexpr int KROW = D + 8;        // Ks row stride (elements)
-  constexpr int VROW = kTileK + 8;   // Vt row stride (elements)
 #pragma unroll
-  for (int c = 0; c < R::kChunks; ++c) {
-    const int idx = threadIdx.x + kThreads * c;
-    const int key = idx / R::kChunksPerRow;
-    const int dc = idx % R::kChunksPerRow;
-    const int d0 = dc * R::kElemsPerChunk;
-    const int kp = swap_bits23(key);
-    if constexpr (KVB == 2) {
-      *reinterpret_cast<u32x4*>(Ks + key * KROW + d0) = regs.k[c];
-#pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        const unsigned w = regs.v[c][e >> 1];
-        Vt[(d0 + e) * VROW + kp] = (unsigned short)((e & 1) ? (w >> 16) : (w & 0xFFFFu));
+  for (int j = 0; j < TS::kKPerThread; ++j) {
+    const int idx = threadIdx.x + kThreads * j;
+    if (idx < TS::kKChunks) {
+      const int key = idx / TS::kChunksPerRow;
+      const int d0 = (idx % TS::kChunksPerRow) * TS::kElems;
+      unsigned short* dst = Ks + key * TS::KROW + d0;
+      if constexpr (KVB == 2) {
+        *reinterpret_cast<u32x4*>(dst) = regs.k[j];
+      } else {
+        const u32x4& w = regs.k[j];
+        *reinterpret_cast<u32x4*>(dst) =
+            u32x4{M::from_fp8x2(w[0], false), M::from_fp8x2(w[0], true),
+                  M::from_fp8x2(w[1], false), M::from_fp8x2(w[1], true)};
+        *reinterpret_cast<u32x4*>(dst + 8) =
+            u32x4{M::from_fp8x2(w[2], false), M::from_fp8x2(w[2], true),
+                  M::from_fp8x2(w[3], false), M::from_fp8x2(w[3], true)};
       }
-    } else {
-      u32x4 lo, hi;
+    }
+  }
 #pragma unroll
-      for (int h = 0; h < 2; ++h) {
-        const unsigned w0 = regs.k[c][2 * h], w1 = regs.k[c][2 * h + 1];
-        u32x4 o{M::from_fp8x2(w0, false), M::from_fp8x2(w0, true),
-                M::from_fp8x2(w1, false), M::from_fp8x2(w1, true)};
-        if (h == 0) lo = o; else hi = o;
-      }
-      *reinterpret_cast<u32x4*>(Ks + key * KROW + d0) = lo;
-      *reinterpret_cast<u32x4*>(Ks + key * KROW + d0 + 8) = hi;
+  for (int j = 0; j < TS::kVPerThread; ++j) {
+    const int u = threadIdx.x + kThreads * j;
+    if (u < TS::kVUnits) {
+      const int kg = u % 16, ch = u / 16;
+      const int col = swap_bits23(4 * kg);   // 4 consecutive keys stay adjacent
+      const u32x4* v = regs.v[j];
+      if constexpr (KVB == 2) {
 #pragma unroll
-      for (int e2 = 0; e2 < 8; ++e2) {
-        const unsigned pr = M::from_fp8x2(regs.v[c][e2 >> 1], (e2 & 1) != 0);
-        Vt[(d0 + 2 * e2) * VROW + kp] = (unsigned short)(pr & 0xFFFFu);
-        Vt[(d0 + 2 * e2 + 1) * VROW + kp] = (unsigned short)(pr >> 16);
+        for (int e = 0; e < 8; ++e) {
+          const unsigned sel = (e & 1) ? 0x07060302u : 0x05040100u;
+          const u32x2 w{perm(v[1][e >> 1], v[0][e >> 1], sel), perm(v[3][e >> 1], v[2][e >> 1], sel)};
+          *reinterpret_cast<u32x2*>(Vt + (ch * 8 + e) * TS::VROW + col) = w;
+        }
+      } else {
+#pragma unroll
+        for (int m = 0; m < 8; ++m) {   // d pair (2m, 2m+1) of the 16-element chunk
+          unsigned cv[4];
+#pragma unroll
+          for (int i = 0; i < 4; ++i) cv[i] = M::from_fp8x2(v[i][m >> 1], (m & 1) != 0);
+          const u32x2 lo{perm(cv[1], cv[0], 0x05040100u), perm(cv[3], cv[2], 0x05040100u)};
+          const u32x2 hi{perm(cv[1], cv[0], 0x07060302u), perm(cv[3], cv[2], 0x07060302u)};
+          *reinterpret_cast<u32x2*>(Vt + (ch * 16 + 2 * m) * TS::VROW + col) = lo;
+          *reinterpret_cast<u32x2*>(Vt + (ch * 16 + 2 * m + 1) * TS::VROW + col) = hi;
+        }
       }
     }
   }
 }
 
 template <int D, typename CT, int KVB>
-__global__ __launch_bounds__(kThreads) void prefill_kernel(AttnParams p, int hpw) {
+__global__ __launch_bounds__(kThreads, 2) void prefill_kernel(AttnParams p, int hpw) {
   using M = Mfma<CT>;
   using vec8 = typename M::vec8;
+  using TS = TileShape<D, KVB>;
   constexpr int QS = D / 16;      // QK MFMA steps (16 d each)
   constexpr int DT = D / 32;      // 32-row d tiles of O^T
-  constexpr int KROW = D + 8;
-  constexpr int VROW = kTileK + 8;
 
-  __shared__ __attribute__((aligned(16))) unsigned short Ks[kTileK * KROW];
-  __shared__ __attribute__((aligned(16))) unsigned short Vt[D * VROW];
+  __shared__ __attribute__((aligned(16))) unsigned short Ks[2][TS::kKsElems];
+  __shared__ __attribute__((aligned(16))) unsigned short Vt[2][TS::kVtElems];
 
-  const int rr = blockIdx.z;
-  const int r = p.req_begin + rr;
+  const int r = p.req_begin + blockIdx.y;
   const int q_first = p.qsl[r];
   const int n = p.qsl[r + 1] - q_first;
   const int QB = 128 / hpw;
-  const int qtile = blockIdx.x;
-  if (qtile * QB >= n) return;
+  const int q_hi = n - (int)blockIdx.z * QB;      // tile j covers queries [q_hi - QB, q_hi)
+  if (q_hi <= 0) return;
   const int G = p.group;
   const int s_all = p.seq_lens[r];
   const int c = s_all - n;
   int s_eff = min(s_all, p.max_seq_len);
   s_eff = min(s_eff, p.max_blocks_per_req * kBlock);
-  const int nblk = (s_eff + kBlock - 1) / kBlock;
-  const int q_hi = min((qtile + 1) * QB, n);           // exclusive
-  const int k_end = min(c + q_hi, s_eff);              // keys any query of the tile may see
+  const int k_end = min(c + q_hi, s_eff);          // keys any query of the tile may see
   const int ntiles = (k_end + kTileK - 1) / kTileK;
 
   const int lane = threadIdx.x & 63;
   const int wave = wave_uniform(threadIdx.x >> 6);
   const int half = lane >> 5;
   const int l32 = lane & 31;
-  const int qh = blockIdx.y * hpw + (wave % hpw);
+  const int qh = blockIdx.x * hpw + (wave % hpw);
   const int kvh = qh / G;
-  const int wq0 = qtile * QB + (wave / hpw) * 32;       // first query of the wave
-  const int qi = wq0 + l32;                             // this lane's query
-  const bool q_ok = qi < n;
-  const int qpos = c + qi;                              // its position
+  const int wq0 = q_hi - QB + (wave / hpw) * 32;   // first query of the wave (may be < 0)
+  const int qi = wq0 + l32;                        // this lane's query
+  const bool q_ok = qi >= 0;
+  const int qpos = c + qi;
 
   // Q as the B operand of S^T = K . Q^T: B[k = 8*half + e][col = l32] = Q[qi][16 s + 8 half + e]
   vec8 qop[QS];
   {
-    const CT* qrow = static_cast<const CT*>(p.q) + (int64_t)(q_first + qi) * p.q_row_stride +
+    const CT* qrow = static_cast<const CT*>(p.q) + (int64_t)(q_first + (q_ok ? qi : 0)) * p.q_row_stride +
                      (int64_t)qh * D;
 #pragma unroll
     for (int s = 0; s < QS; ++s) {
@@ -175,110 +223,127 @@ __global__ __launch_bounds__(kThreads) void prefill_kernel(AttnParams p, int hpw
     }
   }
 
-  const int32_t* bt_row = p.block_tables + (int64_t)r * p.max_blocks_per_req;
+  TileCtx tc;
+  tc.kc = static_cast<const unsigned char*>(p.key_cache);
+  tc.vc = static_cast<const unsigned char*>(p.value_cache);
+  tc.bt_row = p.block_tables + (int64_t)r * p.max_blocks_per_req;
+  tc.tok_stride = (int64_t)p.num_kv_heads * D * KVB;
+  tc.blk_stride = tc.tok_stride * kBlock;
+  tc.head_off = (int64_t)kvh * D * KVB;
+  tc.num_blocks = p.num_blocks;
+  tc.s_eff = s_eff;
+  tc.nblk = (s_eff + kBlock - 1) / kBlock;
+
+  const float c2 = p.scale_log2;
   f32x16 acc[DT];
 #pragma unroll
   for (int t = 0; t < DT; ++t) acc[t] = f32x16{};
-  float m_run = -INFINITY, l_run = 0.f;
+  float m_used = -INFINITY, l_run = 0.f;
+  const int wave_first_pos = c + wq0;
+  const int wave_last_pos = c + wq0 + 31;
 
-  TileRegs<D, CT, KVB> regs;
-  if (ntiles > 0) load_tile<D, CT, KVB>(regs, p, bt_row, nblk, s_eff, 0, kvh);
-  const int wave_last_pos = c + min(wq0 + 31, n - 1);  // largest position in the wave
+  TileRegs<D, KVB> regs;
+  if (ntiles > 0) {
+    load_tile<D, KVB>(regs, tc, 0);
+    store_tile<D, CT, KVB>(regs, Ks[0], Vt[0]);
+  }
+  __syncthreads();
   for (int kt = 0; kt < ntiles; ++kt) {
-    __syncthreads();                 // previous tile fully consumed
-    store_tile<D, CT, KVB>(regs, Ks, Vt);
-    __syncthreads();
-    if (kt + 1 < ntiles) load_tile<D, CT, KVB>(regs, p, bt_row, nblk, s_eff, kt + 1, kvh);
+    const int buf = kt & 1;
+    if (kt + 1 < ntiles) load_tile<D, KVB>(regs, tc, kt + 1);
     const int k0 = kt * kTileK;
-    if (k0 > wave_last_pos) continue;   // whole tile is in the future of every query of the wave
-
-    // ---- S^T (keys x queries), two 32-key subtiles ----
-    f32x16 sc[2];
+    if (k0 <= wave_last_pos) {
+      // ---- S^T (keys x queries), two 32-key subtiles ----
+      f32x16 sc[2];
 #pragma unroll
-    for (int u = 0; u < 2; ++u) {
-      f32x16 a = f32x16{};
-      const unsigned short* krow = Ks + (32 * u + l32) * KROW + 8 * half;
+      for (int u = 0; u < 2; ++u) {
+        f32x16 a = f32x16{};
+        const unsigned short* krow = Ks[buf] + (32 * u + l32) * TS::KROW + 8 * half;
 #pragma unroll
-      for (int s = 0; s < QS; ++s) {
-        const vec8 kop = __builtin_bit_cast(vec8, *reinterpret_cast<const u32x4*>(krow + 16 * s));
-        a = M::mma32(kop, qop[s], a);
-      }
-      sc[u] = a;
-    }
-
-    // ---- scale, causal / length / absent-block mask ----
-    bool blk_ok[4];
-#pragma unroll
-    for (int b = 0; b < 4; ++b) {
-      const int bi = kt * 4 + b;
-      bool ok = bi < nblk;
-      if (ok) {
-        const int id = bt_row[bi];
-        ok = id >= 0 && (int64_t)id < p.num_blocks;
-      }
-      blk_ok[b] = ok;
-    }
-    const bool need_mask = (k0 + kTileK - 1 > c + wq0) || (k0 + kTileK > s_eff) ||
-                           !blk_ok[0] || !blk_ok[1] || !blk_ok[2] || !blk_ok[3];
-    float x[2][16];
-#pragma unroll
-    for (int u = 0; u < 2; ++u) {
-#pragma unroll
-      for (int g = 0; g < 16; ++g) {
-        float v = sc[u][g] * p.scale_log2;
-        if (need_mask) {
-          const int key = k0 + 32 * u + 8 * (g / 4) + 4 * half + (g % 4);
-          const bool ok = key <= qpos && key < s_eff && blk_ok[(32 * u + 8 * (g / 4)) / kBlock];
-          v = ok ? v : -INFINITY;
+        for (int s = 0; s < QS; ++s) {
+          const vec8 kop = __builtin_bit_cast(vec8, *reinterpret_cast<const u32x4*>(krow + 16 * s));
+          a = M::mma32(kop, qop[s], a);
         }
-        x[u][g] = v;
+        sc[u] = a;
       }
-    }
-    float mx = -INFINITY;
+      // ---- causal / length / absent-block mask ----
+      bool blk_ok[kTileK / kBlock];
+      bool all_ok = true;
 #pragma unroll
-    for (int u = 0; u < 2; ++u)
-#pragma unroll
-      for (int g = 0; g < 16; ++g) mx = fmaxf(mx, x[u][g]);
-    mx = fmaxf(mx, shfl_xor(mx, 32));
-    const float m_new = fmaxf(m_run, mx);
-    const float m_safe = (m_new == -INFINITY) ? 0.f : m_new;
-    const float alpha = exp2f(m_run - m_safe);
-    float psum = 0.f;
-#pragma unroll
-    for (int u = 0; u < 2; ++u)
-#pragma unroll
-      for (int g = 0; g < 16; ++g) {
-        x[u][g] = exp2f(x[u][g] - m_safe);
-        psum += x[u][g];
+      for (int b = 0; b < kTileK / kBlock; ++b) {
+        const int bi = kt * (kTileK / kBlock) + b;
+        bool ok = true;
+        if (bi < tc.nblk) {
+          const int id = tc.bt_row[bi];
+          ok = id >= 0 && (int64_t)id < tc.num_blocks;
+        }
+        blk_ok[b] = ok;
+        all_ok = all_ok && ok;
       }
-    l_run = l_run * alpha + psum;
-    m_run = m_new;
+      if (k0 + kTileK - 1 > wave_first_pos || k0 + kTileK > s_eff || !all_ok) {
 #pragma unroll
-    for (int t = 0; t < DT; ++t) acc[t] *= alpha;
+        for (int u = 0; u < 2; ++u)
+#pragma unroll
+          for (int g = 0; g < 16; ++g) {
+            const int kin = 32 * u + 8 * (g / 4) + 4 * half + (g % 4);
+            const int key = k0 + kin;
+            if (key > qpos || key >= s_eff || !blk_ok[kin / kBlock]) sc[u][g] = -INFINITY;
+          }
+      }
+      float mx = -INFINITY;
+#pragma unroll
+      for (int u = 0; u < 2; ++u)
+#pragma unroll
+        for (int g = 0; g < 16; ++g) mx = fmaxf(mx, sc[u][g]);
+      mx = fmaxf(mx, shfl_xor(mx, 32));
+      // ---- lazy rescale: move the reference max only when it grew by > 2^8 ----
+      const bool grow = (m_used == -INFINITY) ? (mx > -INFINITY) : ((mx - m_used) * c2 > kRescaleLog2);
+      if (__builtin_amdgcn_read_exec() & __ballot(grow)) {
+        const float m_new = grow ? mx : m_used;
+        const float alpha = (m_used == -INFINITY) ? 0.f : exp2f((m_used - m_new) * c2);
+        l_run *= alpha;
+#pragma unroll
+        for (int t = 0; t < DT; ++t) acc[t] *= alpha;
+        m_used = m_new;
+      }
+      const float mref = (m_used == -INFINITY) ? 0.f : m_used * c2;
+      float psum = 0.f;
+#pragma unroll
+      for (int u = 0; u < 2; ++u)
+#pragma unroll
+        for (int g = 0; g < 16; ++g) {
+          const float e = exp2f(__builtin_fmaf(sc[u][g], c2, -mref));
+          sc[u][g] = e;
+          psum += e;
+        }
+      l_run += psum;
 
-    // ---- O^T += V^T . P^T, four 16-key steps ----
+      // ---- O^T += V^T . P^T, four 16-key steps ----
 #pragma unroll
-    for (int u = 0; u < 2; ++u) {
+      for (int u = 0; u < 2; ++u) {
 #pragma unroll
-      for (int v = 0; v < 2; ++v) {
-        const u32x4 pw{pack2<CT>(x[u][8 * v + 0], x[u][8 * v + 1]),
-                       pack2<CT>(x[u][8 * v + 2], x[u][8 * v + 3]),
-                       pack2<CT>(x[u][8 * v + 4], x[u][8 * v + 5]),
-                       pack2<CT>(x[u][8 * v + 6], x[u][8 * v + 7])};
-        const vec8 pop = __builtin_bit_cast(vec8, pw);
-        const int col = 32 * u + 16 * v + 8 * half;   // Vt column of this lane's 8 keys
+        for (int v = 0; v < 2; ++v) {
+          const u32x4 pw{pack2<CT>(sc[u][8 * v + 0], sc[u][8 * v + 1]),
+                         pack2<CT>(sc[u][8 * v + 2], sc[u][8 * v + 3]),
+                         pack2<CT>(sc[u][8 * v + 4], sc[u][8 * v + 5]),
+                         pack2<CT>(sc[u][8 * v + 6], sc[u][8 * v + 7])};
+          const vec8 pop = __builtin_bit_cast(vec8, pw);
+          const int col = 32 * u + 16 * v + 8 * half;   // Vt column of this lane's 8 keys
 #pragma unroll
-        for (int t = 0; t < DT; ++t) {
-          const vec8 vop = __builtin_bit_cast(
-              vec8, *reinterpret_cast<const u32x4*>(Vt + (32 * t + l32) * VROW + col));
-          acc[t] = M::mma32(vop, pop, acc[t]);
+          for (int t = 0; t < DT; ++t) {
+            const vec8 vop = __builtin_bit_cast(
+                vec8, *reinterpret_cast<const u32x4*>(Vt[buf] + (32 * t + l32) * TS::VROW + col));
+            acc[t] = M::mma32(vop, pop, acc[t]);
+          }
         }
       }
     }
+    if (kt + 1 < ntiles) store_tile<D, CT, KVB>(regs, Ks[buf ^ 1], Vt[buf ^ 1]);
+    __syncthreads();
   }
 
   // ---- normalise and store: lane holds O[qi][32 t + 8 j + 4 half + i] ----
-  float lt = l_run + shfl_xor(l_run, 32);
+  const float lt = l_run + shfl_xor(l_run, 32);
   if (!q_ok) return;
   const float inv = (lt > 0.f) ? p.v_scale / lt : 0.f;
   unsigned short* orow = static_cast<unsigned short*>(p.out) +
@@ -307,7 +372,8 @@ hipError_t launch_typed(const AttnParams& p, hipStream_t stream) {
   const int QB = 128 / hpw;
   const int qtiles = (p.max_query_len + QB - 1) / QB;
   if (qtiles == 0) return hipSuccess;
-  dim3 grid((unsigned)qtiles, (unsigned)(p.num_q_heads / hpw), (unsigned)p.num_reqs);
+  // x: query-head group, y: request, z: tile counted from the end of the request
+  dim3 grid((unsigned)(p.num_q_heads / hpw), (unsigned)p.num_reqs, (unsigned)qtiles);
   hipLaunchKernelGGL((prefill_kernel<D, CT, KVB>), grid, dim3(kThreads), 0, stream, p, hpw);
   return hipGetLastError();
 }
