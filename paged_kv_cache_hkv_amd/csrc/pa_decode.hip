@@ -247,12 +247,12 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(AttnParams p) {
       mx = fmaxf(mx, shfl_xor(mx, 32));
       const float m_new = fmaxf(m_run[ht], mx);
       const float m_safe = (m_new == -INFINITY) ? 0.f : m_new;
-      const float alpha = exp2f(m_run[ht] - m_safe);
+      const float alpha = fast_exp2(m_run[ht] - m_safe);
       float pr[8];
       float psum = 0.f;
 #pragma unroll
       for (int i = 0; i < 8; ++i) {
-        pr[i] = exp2f(x[i] - m_safe);
+        pr[i] = fast_exp2(x[i] - m_safe);
         psum += pr[i];
       }
       l_run[ht] = l_run[ht] * alpha + psum;
@@ -307,7 +307,7 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(AttnParams p) {
       float wgt[kWaves];
 #pragma unroll
       for (int w = 0; w < kWaves; ++w) {
-        wgt[w] = exp2f(mw[w] - msafe);
+        wgt[w] = fast_exp2(mw[w] - msafe);
         L += wgt[w] * red_l[w][hh];
       }
       float o[EPT];
@@ -367,14 +367,14 @@ __global__ __launch_bounds__(64) void decode_reduce_kernel(AttnParams p) {
   for (int i = 0; i < nparts; ++i) mmax = fmaxf(mmax, ml[2 * i]);
   const float msafe = (mmax == -INFINITY) ? 0.f : mmax;
   float L = 0.f;
-  for (int i = 0; i < nparts; ++i) L += exp2f(ml[2 * i] - msafe) * ml[2 * i + 1];
+  for (int i = 0; i < nparts; ++i) L += fast_exp2(ml[2 * i] - msafe) * ml[2 * i + 1];
   const float inv = (L > 0.f) ? p.v_scale / L : 0.f;
   const float* acc = p.ws_acc + base * D;
   unsigned short* orow = static_cast<unsigned short*>(p.out) + (int64_t)q_row * p.out_row_stride +
                          (int64_t)qh * D;
   for (int d = threadIdx.x; d < D; d += 64) {
     float o = 0.f;
-    for (int i = 0; i < nparts; ++i) o += exp2f(ml[2 * i] - msafe) * acc[(int64_t)i * D + d];
+    for (int i = 0; i < nparts; ++i) o += fast_exp2(ml[2 * i] - msafe) * acc[(int64_t)i * D + d];
     orow[d] = Mfma<CT>::from_float(o * inv);
   }
 }

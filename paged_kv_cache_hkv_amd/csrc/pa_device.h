@@ -75,11 +75,19 @@ template <> struct Mfma<_Float16> {
   }
 };
 
-// Pack two floats into one dword of two 16-bit compute-type values (lo, hi).
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+
+// Pack two floats into one dword of two 16-bit compute-type values (lo, hi),
+// round to nearest even: one v_cvt_pk_{bf16,f16}_f32.
 template <typename T>
 __device__ inline unsigned pack2(float lo, float hi) {
-  return (unsigned)Mfma<T>::from_float(lo) | ((unsigned)Mfma<T>::from_float(hi) << 16);
+  typedef T t2 __attribute__((ext_vector_type(2)));
+  return __builtin_bit_cast(unsigned, __builtin_convertvector(f32x2{lo, hi}, t2));
 }
+
+// 2^x with the hardware v_exp_f32 (results below 2^-126 flush to zero, which
+// only ever affects softmax weights that are negligible against the max).
+__device__ inline float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 
 // Byte permute: result byte k = byte sel.k of the 8-byte value {hi:lo}.
 __device__ inline unsigned perm(unsigned hi, unsigned lo, unsigned sel) {

@@ -78,44 +78,59 @@ struct TileCtx {
   int nblk, s_eff;
 };
 
-// Byte offset of (logical key, chunk) in the cache, or -1 if the key is absent.
-template <int KVB>
-__device__ inline int64_t key_offset(const TileCtx& c, int key, int chunk) {
-  if (key >= c.s_eff) return -1;
-  const int bi = key / kBlock;
-  if (bi >= c.nblk) return -1;
-  const int b = c.bt_row[bi];
-  if (b < 0 || (int64_t)b >= c.num_blocks) return -1;
-  return (int64_t)b * c.blk_stride + (int64_t)(key % kBlock) * c.tok_stride + c.head_off +
-         (int64_t)chunk * 16;
+// Physical block id of logical block bi, or -1 if absent (past the sequence
+// or outside the pool).
+__device__ inline int block_id(const TileCtx& c, int bi) {
+  int id = -1;
+  if (bi < c.nblk) id = c.bt_row[bi];
+  return (id >= 0 && (int64_t)id < c.num_blocks) ? id : -1;
 }
 
+// Bit b set: block b of tile kt is present (uniform across the workgroup).
+__device__ inline unsigned tile_okmask(const TileCtx& c, int kt) {
+  unsigned mask = 0;
+#pragma unroll
+  for (int b = 0; b < kTileK / kBlock; ++b)
+    mask |= (block_id(c, kt * (kTileK / kBlock) + b) >= 0) ? (1u << b) : 0u;
+  return mask;
+}
+
+// Global -> registers for tile kt.  K: thread moves chunks (key, chunk) with
+// key = idx / chunks_per_row, so one wave instruction reads whole 256-byte
+// rows.  V: thread moves 4 consecutive keys of one chunk.  Keys past the
+// sequence or in absent blocks read a valid address and are replaced by
+// zeros, so a 0-probability key can never turn P.V into NaN; the loads are
+// unconditional (no divergent branches).
 template <int D, int KVB>
 __device__ inline void load_tile(TileRegs<D, KVB>& regs, const TileCtx& c, int kt) {
   using TS = TileShape<D, KVB>;
   const int key0 = kt * kTileK;
+  const u32x4 zero = {0u, 0u, 0u, 0u};
 #pragma unroll
   for (int j = 0; j < TS::kKPerThread; ++j) {
     const int idx = threadIdx.x + kThreads * j;
-    u32x4 v = {0u, 0u, 0u, 0u};
-    if (idx < TS::kKChunks) {
-      const int64_t off = key_offset<KVB>(c, key0 + idx / TS::kChunksPerRow, idx % TS::kChunksPerRow);
-      if (off >= 0) v = ld16(c.kc + off);   // absent keys load zeros (and are masked)
-    }
-    regs.k[j] = v;
+    const int key = idx / TS::kChunksPerRow;
+    const int chunk = idx % TS::kChunksPerRow;
+    const int id = block_id(c, kt * (kTileK / kBlock) + key / kBlock);
+    const bool ok = (idx < TS::kKChunks) && id >= 0 && (key0 + key < c.s_eff);
+    const int64_t off = (int64_t)id * c.blk_stride + (int64_t)(key % kBlock) * c.tok_stride +
+                        c.head_off + chunk * 16;
+    const u32x4 v = ld16(c.kc + (ok ? off : 0));
+    regs.k[j] = ok ? v : zero;
   }
 #pragma unroll
   for (int j = 0; j < TS::kVPerThread; ++j) {
     const int u = threadIdx.x + kThreads * j;
     const int kg = u % 16, ch = u / 16;
+    const int id = block_id(c, kt * (kTileK / kBlock) + kg / 4);
+    const bool bok = (u < TS::kVUnits) && id >= 0;
+    const int64_t off0 = (int64_t)id * c.blk_stride + (int64_t)((4 * kg) % kBlock) * c.tok_stride +
+                         c.head_off + ch * 16;
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-      u32x4 v = {0u, 0u, 0u, 0u};
-      if (u < TS::kVUnits) {
-        const int64_t off = key_offset<KVB>(c, key0 + 4 * kg + i, ch);
-        if (off >= 0) v = ld16(c.vc + off);   // zeros keep 0-probability keys from making NaN
-      }
-      regs.v[j][i] = v;
+      const bool ok = bok && (key0 + 4 * kg + i < c.s_eff);
+      const u32x4 v = ld16(c.vc + (ok ? off0 + i * c.tok_stride : 0));
+      regs.v[j][i] = ok ? v : zero;
     }
   }
 }
@@ -267,27 +282,16 @@ __global__ __launch_bounds__(kThreads, 2) void prefill_kernel(AttnParams p, int 
         sc[u] = a;
       }
       // ---- causal / length / absent-block mask ----
-      bool blk_ok[kTileK / kBlock];
-      bool all_ok = true;
-#pragma unroll
-      for (int b = 0; b < kTileK / kBlock; ++b) {
-        const int bi = kt * (kTileK / kBlock) + b;
-        bool ok = true;
-        if (bi < tc.nblk) {
-          const int id = tc.bt_row[bi];
-          ok = id >= 0 && (int64_t)id < tc.num_blocks;
-        }
-        blk_ok[b] = ok;
-        all_ok = all_ok && ok;
-      }
+      const unsigned okmask = tile_okmask(tc, kt);
+      const bool all_ok = okmask == 0xFu;
       if (k0 + kTileK - 1 > wave_first_pos || k0 + kTileK > s_eff || !all_ok) {
 #pragma unroll
         for (int u = 0; u < 2; ++u)
 #pragma unroll
           for (int g = 0; g < 16; ++g) {
-            const int kin = 32 * u + 8 * (g / 4) + 4 * half + (g % 4);
-            const int key = k0 + kin;
-            if (key > qpos || key >= s_eff || !blk_ok[kin / kBlock]) sc[u][g] = -INFINITY;
+            const int key = k0 + 32 * u + 8 * (g / 4) + 4 * half + (g % 4);
+            const bool blk = (okmask >> (2 * u + (g >= 8 ? 1 : 0))) & 1u;   // the key's block
+            if (key > qpos || key >= s_eff || !blk) sc[u][g] = -INFINITY;
           }
       }
       float mx = -INFINITY;
@@ -300,7 +304,7 @@ __global__ __launch_bounds__(kThreads, 2) void prefill_kernel(AttnParams p, int 
       const bool grow = (m_used == -INFINITY) ? (mx > -INFINITY) : ((mx - m_used) * c2 > kRescaleLog2);
       if (__builtin_amdgcn_read_exec() & __ballot(grow)) {
         const float m_new = grow ? mx : m_used;
-        const float alpha = (m_used == -INFINITY) ? 0.f : exp2f((m_used - m_new) * c2);
+        const float alpha = (m_used == -INFINITY) ? 0.f : fast_exp2((m_used - m_new) * c2);
         l_run *= alpha;
 #pragma unroll
         for (int t = 0; t < DT; ++t) acc[t] *= alpha;
@@ -312,7 +316,7 @@ __global__ __launch_bounds__(kThreads, 2) void prefill_kernel(AttnParams p, int 
       for (int u = 0; u < 2; ++u)
 #pragma unroll
         for (int g = 0; g < 16; ++g) {
-          const float e = exp2f(__builtin_fmaf(sc[u][g], c2, -mref));
+          const float e = fast_exp2(__builtin_fmaf(sc[u][g], c2, -mref));
           sc[u][g] = e;
           psum += e;
         }
