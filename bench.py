@@ -177,6 +177,9 @@ def main():
     ap.add_argument("--extra-iters", type=int, default=20)
     ap.add_argument("--no-extra", action="store_true")
     ap.add_argument("--no-cpu", action="store_true")
+    ap.add_argument("--copy-bytes", type=int, default=0,
+                    help="first run a plain device-to-device copy of this many bytes three times "
+                         "(the known-size kernel that calibrates rocprofv3 FETCH_SIZE/WRITE_SIZE)")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
         print("bench.py measures one GPU only: this path has no multi-GPU mode "
@@ -185,6 +188,13 @@ def main():
         sys.exit(2)
     B.load()
     torch.cuda.init()
+    if args.copy_bytes > 0:
+        src = torch.empty(args.copy_bytes // 16, 4, dtype=torch.float32, device="cuda").fill_(1.0)
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
     wl = S.CONFIGS[args.config]()
     t = S.make_tensors(wl, "cuda", poison=False)
     snap = None if args.no_cpu else take_snapshot(wl, t)

@@ -103,6 +103,10 @@ __device__ inline float shfl_xor(float v, int mask) {
   return shfl(v, lane ^ mask);
 }
 
+// max / sum of a value over lanes l and l ^ 32.
+__device__ inline float pair32_max(float v) { return fmaxf(v, shfl_xor(v, 32)); }
+__device__ inline float pair32_sum(float v) { return v + shfl_xor(v, 32); }
+
 __device__ inline int wave_uniform(int v) { return __builtin_amdgcn_readfirstlane(v); }
 
 // 16-byte and 8-byte global loads / stores.

@@ -299,7 +299,7 @@ __global__ __launch_bounds__(kThreads, 2) void prefill_kernel(AttnParams p, int 
       for (int u = 0; u < 2; ++u)
 #pragma unroll
         for (int g = 0; g < 16; ++g) mx = fmaxf(mx, sc[u][g]);
-      mx = fmaxf(mx, shfl_xor(mx, 32));
+      mx = pair32_max(mx);
       // ---- lazy rescale: move the reference max only when it grew by > 2^8 ----
       const bool grow = (m_used == -INFINITY) ? (mx > -INFINITY) : ((mx - m_used) * c2 > kRescaleLog2);
       if (__builtin_amdgcn_read_exec() & __ballot(grow)) {
@@ -347,7 +347,270 @@ __global__ __launch_bounds__(kThreads, 2) void prefill_kernel(AttnParams p, int 
   }
 
   // ---- normalise and store: lane holds O[qi][32 t + 8 j + 4 half + i] ----
-  const float lt = l_run + shfl_xor(l_run, 32);
+  const float lt = pair32_sum(l_run);
+  if (!q_ok) return;
+  const float inv = (lt > 0.f) ? p.v_scale / lt : 0.f;
+  unsigned short* orow = static_cast<unsigned short*>(p.out) +
+                         (int64_t)(q_first + qi) * p.out_row_stride + (int64_t)qh * D;
+#pragma unroll
+  for (int t = 0; t < DT; ++t) {
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int d = 32 * t + 8 * j + 4 * half;
+      u32x2 w{pack2<CT>(acc[t][4 * j] * inv, acc[t][4 * j + 1] * inv),
+              pack2<CT>(acc[t][4 * j + 2] * inv, acc[t][4 * j + 3] * inv)};
+      st8(orow + d, w);
+    }
+  }
+}
+
+// ---------------------------------------------------------------------------
+// 16-bit caches: the same math, with the K/V tiles moved global -> LDS by the
+// DMA path (global_load_lds, 16 bytes per lane, no registers or address math
+// in the loop) and V read back transposed with ds_read_b64_tr_b16.
+//
+// LDS layout: per tile, K and V are each [64 keys][D/8 16-byte chunks] with
+// the chunks of key k stored at position (chunk ^ sw(k)); one DMA wave
+// instruction fills 64 consecutive positions, so each lane fetches the global
+// chunk that belongs at its position.  The swizzles keep every read
+// conflict-free: the S^T operand reads one chunk of 32 consecutive keys
+// (sw_k spreads 16 consecutive keys over 16 bank groups); the transposing V
+// read takes 4 consecutive keys x 32 bytes per 16 lanes (sw_v gives the 4
+// keys disjoint 64-byte bank groups).
+//
+// ds_read_b64_tr_b16 (gfx950): within each 16-lane group lane i supplies the
+// address of a row R_i of four 16-bit values and lane j receives
+// R_{4k + j/4}[j % 4], k = 0..3.  With lane i = 4a + b pointing at
+// V[key_a][d0 + 4b .. 4b+3], lane j receives V[key_0..3][d0 + j]: four keys of
+// one d column, i.e. half of a v_mfma_f32_32x32x16 A operand of V^T.
+// Keys the tile does not have (past the sequence, absent blocks) are loaded
+// from a valid address and their V rows are overwritten with zeros once the
+// DMA has landed, so 0-probability keys never meet a NaN.
+template <int D>
+struct LdsTile {
+  static constexpr int CPR = D / 8;                 // 16-byte chunks per key row
+  static constexpr int kPos = kTileK * CPR;         // 16-byte positions per tile (K or V)
+  static constexpr int kInst = kPos / 64;           // DMA wave instructions per tile (K or V)
+  static constexpr int kInstPerWave = kInst / kWaves;
+  __device__ static inline int swk(int key) { return D == 128 ? (key & 15) : ((key >> 1) & 7); }
+  __device__ static inline int swv(int key) { return D == 128 ? 4 * (key & 3) : 4 * ((key >> 1) & 1); }
+};
+
+typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) bf16x4 lds_bf16x4;
+typedef __attribute__((address_space(3))) void lds_void;
+
+__device__ inline u32x2 lds_read_tr16(const u32x4* base, int pos16, int byte_off) {
+  const char* p = reinterpret_cast<const char*>(base + pos16) + byte_off;
+  lds_bf16x4* lp = (lds_bf16x4*)(const_cast<char*>(p));
+  return __builtin_bit_cast(u32x2, __builtin_amdgcn_ds_read_tr16_b64_v4bf16(lp));
+}
+
+// Issue the DMA of tile kt into (Kl, Vl).  Each wave issues kInstPerWave
+// instructions per tensor; instruction `inst` covers positions inst*64 ..
+// inst*64+63, i.e. 64/CPR consecutive keys of one cache block.
+template <int D>
+__device__ inline void dma_tile(const TileCtx& c, int kt, u32x4* Kl, u32x4* Vl, int wave, int lane) {
+  using L = LdsTile<D>;
+#pragma unroll
+  for (int i = 0; i < L::kInstPerWave; ++i) {
+    const int inst = i * kWaves + wave;
+    const int p = inst * 64 + lane;
+    const int key = p / L::CPR;
+    const int pos = p % L::CPR;
+    const int gkey = kt * kTileK + key;
+    const int id = block_id(c, gkey / kBlock);
+    const bool ok = id >= 0 && gkey < c.s_eff;
+    const int64_t row = (int64_t)id * c.blk_stride + (int64_t)(gkey % kBlock) * c.tok_stride +
+                        c.head_off;
+    const int64_t koff = ok ? row + (int64_t)((pos ^ L::swk(key)) * 16) : 0;
+    const int64_t voff = ok ? row + (int64_t)((pos ^ L::swv(key)) * 16) : 0;
+    __builtin_amdgcn_global_load_lds(c.kc + koff, (lds_void*)(Kl + inst * 64), 16, 0, 0);
+    __builtin_amdgcn_global_load_lds(c.vc + voff, (lds_void*)(Vl + inst * 64), 16, 0, 0);
+  }
+}
+
+// After this wave's DMA of tile kt has landed (s_waitcnt by the caller): zero
+// the V positions of keys the tile lacks.  Each lane clears exactly the
+// positions its own DMA instructions wrote, so no other wave's transfer can
+// land on a cleared position afterwards.
+template <int D>
+__device__ inline void fix_tile(const TileCtx& c, int kt, u32x4* Vl, int wave, int lane) {
+  using L = LdsTile<D>;
+  const int key0 = kt * kTileK;
+  const unsigned okmask = tile_okmask(c, kt);
+  if (key0 + kTileK <= c.s_eff && okmask == 0xFu) return;   // full tile: nothing to do
+#pragma unroll
+  for (int i = 0; i < L::kInstPerWave; ++i) {
+    const int p = (i * kWaves + wave) * 64 + lane;
+    const int key = p / L::CPR;
+    if (key0 + key >= c.s_eff || !((okmask >> (key / kBlock)) & 1u)) Vl[p] = u32x4{0u, 0u, 0u, 0u};
+  }
+}
+
+template <int D, typename CT>
+__global__ __launch_bounds__(kThreads, 2) void prefill_dma_kernel(AttnParams p, int hpw) {
+  using M = Mfma<CT>;
+  using vec8 = typename M::vec8;
+  using L = LdsTile<D>;
+  constexpr int QS = D / 16;      // QK MFMA steps (16 d each)
+  constexpr int DT = D / 32;      // 32-row d tiles of O^T
+
+  __shared__ u32x4 Kl[2][L::kPos];
+  __shared__ u32x4 Vl[2][L::kPos];
+
+  const int r = p.req_begin + blockIdx.y;
+  const int q_first = p.qsl[r];
+  const int n = p.qsl[r + 1] - q_first;
+  const int QB = 128 / hpw;
+  const int q_hi = n - (int)blockIdx.z * QB;      // tile j covers queries [q_hi - QB, q_hi)
+  if (q_hi <= 0) return;
+  const int G = p.group;
+  const int s_all = p.seq_lens[r];
+  const int c = s_all - n;
+  int s_eff = min(s_all, p.max_seq_len);
+  s_eff = min(s_eff, p.max_blocks_per_req * kBlock);
+  const int k_end = min(c + q_hi, s_eff);
+  const int ntiles = (k_end + kTileK - 1) / kTileK;
+
+  const int lane = threadIdx.x & 63;
+  const int wave = wave_uniform(threadIdx.x >> 6);
+  const int half = lane >> 5;
+  const int l32 = lane & 31;
+  const int qh = blockIdx.x * hpw + (wave % hpw);
+  const int kvh = qh / G;
+  const int wq0 = q_hi - QB + (wave / hpw) * 32;
+  const int qi = wq0 + l32;
+  const bool q_ok = qi >= 0;
+  const int qpos = c + qi;
+
+  vec8 qop[QS];
+  {
+    const CT* qrow = static_cast<const CT*>(p.q) + (int64_t)(q_first + (q_ok ? qi : 0)) * p.q_row_stride +
+                     (int64_t)qh * D;
+#pragma unroll
+    for (int s = 0; s < QS; ++s) {
+      qop[s] = q_ok ? __builtin_bit_cast(vec8, ld16(qrow + 16 * s + 8 * half))
+                    : __builtin_bit_cast(vec8, u32x4{0u, 0u, 0u, 0u});
+    }
+  }
+
+  TileCtx tc;
+  tc.kc = static_cast<const unsigned char*>(p.key_cache);
+  tc.vc = static_cast<const unsigned char*>(p.value_cache);
+  tc.bt_row = p.block_tables + (int64_t)r * p.max_blocks_per_req;
+  tc.tok_stride = (int64_t)p.num_kv_heads * D * 2;
+  tc.blk_stride = tc.tok_stride * kBlock;
+  tc.head_off = (int64_t)kvh * D * 2;
+  tc.num_blocks = p.num_blocks;
+  tc.s_eff = s_eff;
+  tc.nblk = (s_eff + kBlock - 1) / kBlock;
+
+  // lane roles in the LDS reads (tile-invariant)
+  const int kswz = L::swk(l32);                  // key 32u + l32 has the swizzle of l32
+  const int g16 = lane >> 4;                      // 16-lane group
+  const int ta = (lane & 15) >> 2, tb = lane & 3; // transposed-read row supplier (key a, d 4b)
+  const int vswz = L::swv(ta);                    // keys ... + 4h + a share a's swizzle
+
+  const float c2 = p.scale_log2;
+  f32x16 acc[DT];
+#pragma unroll
+  for (int t = 0; t < DT; ++t) acc[t] = f32x16{};
+  float m_used = -INFINITY, l_run = 0.f;
+  const int wave_first_pos = c + wq0;
+  const int wave_last_pos = c + wq0 + 31;
+
+  if (ntiles > 0) {
+    dma_tile<D>(tc, 0, Kl[0], Vl[0], wave, lane);
+    __builtin_amdgcn_s_waitcnt(0);
+    fix_tile<D>(tc, 0, Vl[0], wave, lane);
+  }
+  __syncthreads();
+  for (int kt = 0; kt < ntiles; ++kt) {
+    const int buf = kt & 1;
+    if (kt + 1 < ntiles) dma_tile<D>(tc, kt + 1, Kl[buf ^ 1], Vl[buf ^ 1], wave, lane);
+    const int k0 = kt * kTileK;
+    if (k0 <= wave_last_pos) {
+      const u32x4* K = Kl[buf];
+      const u32x4* V = Vl[buf];
+      // two independent accumulation chains (the 32-key subtiles), interleaved
+      f32x16 sc[2] = {f32x16{}, f32x16{}};
+#pragma unroll
+      for (int s = 0; s < QS; ++s) {
+#pragma unroll
+        for (int u = 0; u < 2; ++u) {
+          const vec8 kop = __builtin_bit_cast(vec8, K[(32 * u + l32) * L::CPR + ((2 * s + half) ^ kswz)]);
+          sc[u] = M::mma32(kop, qop[s], sc[u]);
+        }
+      }
+      const unsigned okmask = tile_okmask(tc, kt);
+      if (k0 + kTileK - 1 > wave_first_pos || k0 + kTileK > s_eff || okmask != 0xFu) {
+#pragma unroll
+        for (int u = 0; u < 2; ++u)
+#pragma unroll
+          for (int g = 0; g < 16; ++g) {
+            const int key = k0 + 32 * u + 8 * (g / 4) + 4 * half + (g % 4);
+            const bool blk = (okmask >> (2 * u + (g >= 8 ? 1 : 0))) & 1u;
+            if (key > qpos || key >= s_eff || !blk) sc[u][g] = -INFINITY;
+          }
+      }
+      float mx = -INFINITY;
+#pragma unroll
+      for (int u = 0; u < 2; ++u)
+#pragma unroll
+        for (int g = 0; g < 16; ++g) mx = fmaxf(mx, sc[u][g]);
+      mx = pair32_max(mx);
+      const bool grow = (m_used == -INFINITY) ? (mx > -INFINITY) : ((mx - m_used) * c2 > kRescaleLog2);
+      if (__ballot(grow)) {
+        const float m_new = grow ? mx : m_used;
+        const float alpha = (m_used == -INFINITY) ? 0.f : fast_exp2((m_used - m_new) * c2);
+        l_run *= alpha;
+#pragma unroll
+        for (int t = 0; t < DT; ++t) acc[t] *= alpha;
+        m_used = m_new;
+      }
+      const float mref = (m_used == -INFINITY) ? 0.f : m_used * c2;
+      float psum = 0.f;
+#pragma unroll
+      for (int u = 0; u < 2; ++u)
+#pragma unroll
+        for (int g = 0; g < 16; ++g) {
+          const float e = fast_exp2(__builtin_fmaf(sc[u][g], c2, -mref));
+          sc[u][g] = e;
+          psum += e;
+        }
+      l_run += psum;
+#pragma unroll
+      for (int u = 0; u < 2; ++u) {
+#pragma unroll
+        for (int v = 0; v < 2; ++v) {
+          const u32x4 pw{pack2<CT>(sc[u][8 * v + 0], sc[u][8 * v + 1]),
+                         pack2<CT>(sc[u][8 * v + 2], sc[u][8 * v + 3]),
+                         pack2<CT>(sc[u][8 * v + 4], sc[u][8 * v + 5]),
+                         pack2<CT>(sc[u][8 * v + 6], sc[u][8 * v + 7])};
+          const vec8 pop = __builtin_bit_cast(vec8, pw);
+          // keys of this step: 32u + 16v + 8r + 4h + a (h = lane/32), element e = 4r + a
+          const int key_r0 = 32 * u + 16 * v + 4 * half + ta;
+#pragma unroll
+          for (int t = 0; t < DT; ++t) {
+            const int chunk = 4 * t + 2 * (g16 & 1) + (tb >> 1);
+            const int byte_off = 8 * (tb & 1);
+            const u32x2 lo = lds_read_tr16(V, key_r0 * L::CPR + (chunk ^ vswz), byte_off);
+            const u32x2 hi = lds_read_tr16(V, (key_r0 + 8) * L::CPR + (chunk ^ vswz), byte_off);
+            const vec8 vop = __builtin_bit_cast(vec8, u32x4{lo[0], lo[1], hi[0], hi[1]});
+            acc[t] = M::mma32(vop, pop, acc[t]);
+          }
+        }
+      }
+    }
+    if (kt + 1 < ntiles) {
+      __builtin_amdgcn_s_waitcnt(0);
+      fix_tile<D>(tc, kt + 1, Vl[buf ^ 1], wave, lane);
+    }
+    __syncthreads();
+  }
+
+  const float lt = pair32_sum(l_run);
   if (!q_ok) return;
   const float inv = (lt > 0.f) ? p.v_scale / lt : 0.f;
   unsigned short* orow = static_cast<unsigned short*>(p.out) +
@@ -378,7 +641,11 @@ hipError_t launch_typed(const AttnParams& p, hipStream_t stream) {
   if (qtiles == 0) return hipSuccess;
   // x: query-head group, y: request, z: tile counted from the end of the request
   dim3 grid((unsigned)(p.num_q_heads / hpw), (unsigned)p.num_reqs, (unsigned)qtiles);
-  hipLaunchKernelGGL((prefill_kernel<D, CT, KVB>), grid, dim3(kThreads), 0, stream, p, hpw);
+  if constexpr (KVB == 2) {
+    hipLaunchKernelGGL((prefill_dma_kernel<D, CT>), grid, dim3(kThreads), 0, stream, p, hpw);
+  } else {
+    hipLaunchKernelGGL((prefill_kernel<D, CT, KVB>), grid, dim3(kThreads), 0, stream, p, hpw);
+  }
   return hipGetLastError();
 }
 
