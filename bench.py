@@ -81,7 +81,8 @@ def time_calls(fn_list, iters, flush):
     stream = torch.cuda.current_stream()
     res = [[] for _ in fn_list]
     for _ in range(iters):
-        flush.add_(1)                   # evict L2 and the 256 MB last-level cache
+        flush.sum()                     # evict L2 and the 256 MB last-level cache (reads only,
+                                        # so no dirty lines are left to write back in the call)
         for i, fn in enumerate(fn_list):
             a = torch.cuda.Event(enable_timing=True)
             b = torch.cuda.Event(enable_timing=True)

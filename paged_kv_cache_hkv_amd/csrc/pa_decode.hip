@@ -203,13 +203,13 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(AttnParams p) {
       for (int i = 0; i < 8; ++i) {
         const int t = i / 4;
         const int tok = j0 + 16 * t + 4 * q4 + (i % 4);
-        const bool ok = bvalid[t] && tok < tok_end;
-        if (!ok) {
+        // selects, not a branch per token: every register is written on
+        // every path (0 * NaN would poison P.V, so absent V rows become 0)
+        const bool bad = !bvalid[t] || tok >= tok_end;
 #pragma unroll
-          for (int w = 0; w < VW; ++w) vraw[i][w] = 0u;   // 0 * NaN would poison P.V
+        for (int w = 0; w < VW; ++w) vraw[i][w] = bad ? 0u : vraw[i][w];
 #pragma unroll
-          for (int ht = 0; ht < HT; ++ht) sc[ht][t][i % 4] = -INFINITY;
-        }
+        for (int ht = 0; ht < HT; ++ht) sc[ht][t][i % 4] = bad ? -INFINITY : sc[ht][t][i % 4];
       }
     }
 
@@ -345,13 +345,18 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(AttnParams p) {
   }
 }
 
-// Merge of the partition partials of one (request, query head), partitions
-// in increasing order.
+// Merge of the partition partials of one (request, query head): one wave.
+// Lanes take partitions (64 at a time) for the global max and the weighted
+// sum of the row sums; then each lane accumulates its D/64 output columns
+// over the partitions in increasing order with the weights broadcast from
+// the lane that owns them.  Fixed order, no atomics: deterministic.
 template <int D, typename CT>
 __global__ __launch_bounds__(64) void decode_reduce_kernel(AttnParams p) {
+  constexpr int DPL = D / 64;   // output columns per lane
   const int rr = blockIdx.y;
   const int r = p.req_begin + rr;
   const int qh = blockIdx.x;
+  const int lane = threadIdx.x;
   const int q_row = p.qsl[r];
   if (p.qsl[r + 1] - q_row != 1) return;
   int s_eff = min(p.seq_lens[r], p.max_seq_len);
@@ -363,20 +368,39 @@ __global__ __launch_bounds__(64) void decode_reduce_kernel(AttnParams p) {
   nparts = min(nparts, p.max_parts);
   const int64_t base = ((int64_t)rr * p.num_q_heads + qh) * p.max_parts;
   const float* ml = p.ws_ml + base * 2;
-  float mmax = -INFINITY;
-  for (int i = 0; i < nparts; ++i) mmax = fmaxf(mmax, ml[2 * i]);
-  const float msafe = (mmax == -INFINITY) ? 0.f : mmax;
-  float L = 0.f;
-  for (int i = 0; i < nparts; ++i) L += fast_exp2(ml[2 * i] - msafe) * ml[2 * i + 1];
-  const float inv = (L > 0.f) ? p.v_scale / L : 0.f;
   const float* acc = p.ws_acc + base * D;
+
+  float mloc = -INFINITY;
+  for (int i = lane; i < nparts; i += 64) mloc = fmaxf(mloc, ml[2 * i]);
+#pragma unroll
+  for (int off = 32; off >= 1; off >>= 1) mloc = fmaxf(mloc, shfl_xor(mloc, off));
+  const float msafe = (mloc == -INFINITY) ? 0.f : mloc;
+
+  float lsum = 0.f;
+  float o[DPL];
+#pragma unroll
+  for (int e = 0; e < DPL; ++e) o[e] = 0.f;
+  for (int g = 0; g < nparts; g += 64) {
+    const int i = g + lane;
+    const float w = (i < nparts) ? fast_exp2(ml[2 * min(i, nparts - 1)] - msafe) : 0.f;
+    const float lw = (i < nparts) ? w * ml[2 * min(i, nparts - 1) + 1] : 0.f;
+    float t = lw;
+#pragma unroll
+    for (int off = 32; off >= 1; off >>= 1) t += shfl_xor(t, off);
+    lsum += t;
+    const int cnt = min(64, nparts - g);
+    for (int j = 0; j < cnt; ++j) {
+      const float wj = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, w), j));
+      const float* a = acc + (int64_t)(g + j) * D + lane;
+#pragma unroll
+      for (int e = 0; e < DPL; ++e) o[e] += wj * a[64 * e];
+    }
+  }
+  const float inv = (lsum > 0.f) ? p.v_scale / lsum : 0.f;
   unsigned short* orow = static_cast<unsigned short*>(p.out) + (int64_t)q_row * p.out_row_stride +
                          (int64_t)qh * D;
-  for (int d = threadIdx.x; d < D; d += 64) {
-    float o = 0.f;
-    for (int i = 0; i < nparts; ++i) o += fast_exp2(ml[2 * i] - msafe) * acc[(int64_t)i * D + d];
-    orow[d] = Mfma<CT>::from_float(o * inv);
-  }
+#pragma unroll
+  for (int e = 0; e < DPL; ++e) orow[lane + 64 * e] = Mfma<CT>::from_float(o[e] * inv);
 }
 
 template <int D, typename CT, int KVB, int HT>

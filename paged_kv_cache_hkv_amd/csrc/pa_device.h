@@ -32,10 +32,19 @@ constexpr float kLog2e = 1.4426950408889634f;
 // ---- compute-type traits: bf16 or fp16 MFMA --------------------------------
 template <typename T> struct Mfma;
 
+typedef short s16x4 __attribute__((ext_vector_type(4)));
+typedef _Float16 f16x4 __attribute__((ext_vector_type(4)));
+
 template <> struct Mfma<__bf16> {
   typedef bf16x8 vec8;
   __device__ static inline f32x4 mma16(const vec8& a, const vec8& b, const f32x4& c) {
     return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
+  }
+  // v_mfma_f32_16x16x16_bf16: A[i][k] in lane (i + 16*(k/4)), element k%4
+  // (two packed dwords); B likewise; D as for 16x16x32.
+  __device__ static inline f32x4 mma16k16(u32x2 a, u32x2 b, const f32x4& c) {
+    return __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(__builtin_bit_cast(s16x4, a),
+                                                     __builtin_bit_cast(s16x4, b), c, 0, 0, 0);
   }
   __device__ static inline f32x16 mma32(const vec8& a, const vec8& b, const f32x16& c) {
     return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
@@ -58,6 +67,10 @@ template <> struct Mfma<_Float16> {
   typedef f16x8 vec8;
   __device__ static inline f32x4 mma16(const vec8& a, const vec8& b, const f32x4& c) {
     return __builtin_amdgcn_mfma_f32_16x16x32_f16(a, b, c, 0, 0, 0);
+  }
+  __device__ static inline f32x4 mma16k16(u32x2 a, u32x2 b, const f32x4& c) {
+    return __builtin_amdgcn_mfma_f32_16x16x16f16(__builtin_bit_cast(f16x4, a),
+                                                 __builtin_bit_cast(f16x4, b), c, 0, 0, 0);
   }
   __device__ static inline f32x16 mma32(const vec8& a, const vec8& b, const f32x16& c) {
     return __builtin_amdgcn_mfma_f32_32x32x16_f16(a, b, c, 0, 0, 0);
@@ -108,6 +121,16 @@ __device__ inline float pair32_max(float v) { return fmaxf(v, shfl_xor(v, 32)); 
 __device__ inline float pair32_sum(float v) { return v + shfl_xor(v, 32); }
 
 __device__ inline int wave_uniform(int v) { return __builtin_amdgcn_readfirstlane(v); }
+
+// Read a wave-uniform element of a table the kernel never writes (block
+// tables, query_start_loc, seq_lens) through the constant address space: a
+// scalar load, counted by lgkmcnt, so waiting for it never waits for vector
+// loads or LDS transfers still in flight.
+__device__ inline int32_t load_uniform(const int32_t* table, int64_t idx) {
+  typedef __attribute__((address_space(4))) const int32_t const_i32;
+  const const_i32* p = (const const_i32*)(table);
+  return p[idx];
+}
 
 // 16-byte and 8-byte global loads / stores.
 __device__ inline u32x4 ld16(const void* p) { return *reinterpret_cast<const u32x4*>(p); }

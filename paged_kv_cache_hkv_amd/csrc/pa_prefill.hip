@@ -79,10 +79,13 @@ struct TileCtx {
 };
 
 // Physical block id of logical block bi, or -1 if absent (past the sequence
-// or outside the pool).
+// or outside the pool).  bi must be uniform across the wave: the table entry
+// is then a scalar load, which never waits on the vector-memory counter (and
+// so never on K/V transfers still in flight).
 __device__ inline int block_id(const TileCtx& c, int bi) {
+  bi = __builtin_amdgcn_readfirstlane(bi);
   int id = -1;
-  if (bi < c.nblk) id = c.bt_row[bi];
+  if (bi < c.nblk) id = load_uniform(c.bt_row, bi);
   return (id >= 0 && (int64_t)id < c.num_blocks) ? id : -1;
 }
 
@@ -93,6 +96,11 @@ __device__ inline unsigned tile_okmask(const TileCtx& c, int kt) {
   for (int b = 0; b < kTileK / kBlock; ++b)
     mask |= (block_id(c, kt * (kTileK / kBlock) + b) >= 0) ? (1u << b) : 0u;
   return mask;
+}
+
+// Select one of the 4 block ids of a tile by a per-lane index (no arrays).
+__device__ inline int pick_id(int i, int b0, int b1, int b2, int b3) {
+  return i == 0 ? b0 : (i == 1 ? b1 : (i == 2 ? b2 : b3));
 }
 
 // Global -> registers for tile kt.  K: thread moves chunks (key, chunk) with
@@ -106,12 +114,14 @@ __device__ inline void load_tile(TileRegs<D, KVB>& regs, const TileCtx& c, int k
   using TS = TileShape<D, KVB>;
   const int key0 = kt * kTileK;
   const u32x4 zero = {0u, 0u, 0u, 0u};
+  const int b0 = block_id(c, kt * 4 + 0), b1 = block_id(c, kt * 4 + 1);
+  const int b2 = block_id(c, kt * 4 + 2), b3 = block_id(c, kt * 4 + 3);
 #pragma unroll
   for (int j = 0; j < TS::kKPerThread; ++j) {
     const int idx = threadIdx.x + kThreads * j;
     const int key = idx / TS::kChunksPerRow;
     const int chunk = idx % TS::kChunksPerRow;
-    const int id = block_id(c, kt * (kTileK / kBlock) + key / kBlock);
+    const int id = pick_id(key / kBlock, b0, b1, b2, b3);
     const bool ok = (idx < TS::kKChunks) && id >= 0 && (key0 + key < c.s_eff);
     const int64_t off = (int64_t)id * c.blk_stride + (int64_t)(key % kBlock) * c.tok_stride +
                         c.head_off + chunk * 16;
@@ -122,7 +132,7 @@ __device__ inline void load_tile(TileRegs<D, KVB>& regs, const TileCtx& c, int k
   for (int j = 0; j < TS::kVPerThread; ++j) {
     const int u = threadIdx.x + kThreads * j;
     const int kg = u % 16, ch = u / 16;
-    const int id = block_id(c, kt * (kTileK / kBlock) + kg / 4);
+    const int id = pick_id(kg / 4, b0, b1, b2, b3);
     const bool bok = (u < TS::kVUnits) && id >= 0;
     const int64_t off0 = (int64_t)id * c.blk_stride + (int64_t)((4 * kg) % kBlock) * c.tok_stride +
                          c.head_off + ch * 16;
@@ -291,7 +301,7 @@ __global__ __launch_bounds__(kThreads, 2) void prefill_kernel(AttnParams p, int 
           for (int g = 0; g < 16; ++g) {
             const int key = k0 + 32 * u + 8 * (g / 4) + 4 * half + (g % 4);
             const bool blk = (okmask >> (2 * u + (g >= 8 ? 1 : 0))) & 1u;   // the key's block
-            if (key > qpos || key >= s_eff || !blk) sc[u][g] = -INFINITY;
+            sc[u][g] = (key > qpos || key >= s_eff || !blk) ? -INFINITY : sc[u][g];
           }
       }
       float mx = -INFINITY;
@@ -412,6 +422,7 @@ __device__ inline u32x2 lds_read_tr16(const u32x4* base, int pos16, int byte_off
 template <int D>
 __device__ inline void dma_tile(const TileCtx& c, int kt, u32x4* Kl, u32x4* Vl, int wave, int lane) {
   using L = LdsTile<D>;
+  constexpr int kKeysPerInst = 64 / L::CPR;   // consecutive keys of one cache block
 #pragma unroll
   for (int i = 0; i < L::kInstPerWave; ++i) {
     const int inst = i * kWaves + wave;
@@ -419,7 +430,8 @@ __device__ inline void dma_tile(const TileCtx& c, int kt, u32x4* Kl, u32x4* Vl, 
     const int key = p / L::CPR;
     const int pos = p % L::CPR;
     const int gkey = kt * kTileK + key;
-    const int id = block_id(c, gkey / kBlock);
+    // the instruction's block, from uniform values only (a scalar table read)
+    const int id = block_id(c, (kt * kTileK + inst * kKeysPerInst) / kBlock);
     const bool ok = id >= 0 && gkey < c.s_eff;
     const int64_t row = (int64_t)id * c.blk_stride + (int64_t)(gkey % kBlock) * c.tok_stride +
                         c.head_off;
@@ -456,8 +468,13 @@ __global__ __launch_bounds__(kThreads, 2) void prefill_dma_kernel(AttnParams p, 
   constexpr int QS = D / 16;      // QK MFMA steps (16 d each)
   constexpr int DT = D / 32;      // 32-row d tiles of O^T
 
-  __shared__ u32x4 Kl[2][L::kPos];
-  __shared__ u32x4 Vl[2][L::kPos];
+  // Double buffer as four distinct arrays, named by constants only: the
+  // compiler then knows a read of the current tile cannot alias the DMA of the
+  // next one and does not make the read wait for that transfer.
+  __shared__ u32x4 K0[L::kPos];
+  __shared__ u32x4 V0[L::kPos];
+  __shared__ u32x4 K1[L::kPos];
+  __shared__ u32x4 V1[L::kPos];
 
   const int r = p.req_begin + blockIdx.y;
   const int q_first = p.qsl[r];
@@ -521,18 +538,19 @@ __global__ __launch_bounds__(kThreads, 2) void prefill_dma_kernel(AttnParams p, 
   const int wave_last_pos = c + wq0 + 31;
 
   if (ntiles > 0) {
-    dma_tile<D>(tc, 0, Kl[0], Vl[0], wave, lane);
+    dma_tile<D>(tc, 0, K0, V0, wave, lane);
     __builtin_amdgcn_s_waitcnt(0);
-    fix_tile<D>(tc, 0, Vl[0], wave, lane);
+    fix_tile<D>(tc, 0, V0, wave, lane);
   }
+  // Q (and tile 0) resident on every path into the loop, so the loop's first
+  // MFMA never waits on the vector-memory counter while later DMAs are in flight
+  __builtin_amdgcn_s_waitcnt(0);
   __syncthreads();
-  for (int kt = 0; kt < ntiles; ++kt) {
-    const int buf = kt & 1;
-    if (kt + 1 < ntiles) dma_tile<D>(tc, kt + 1, Kl[buf ^ 1], Vl[buf ^ 1], wave, lane);
+  // one tile: start the next tile's DMA into (Kn, Vn), compute from (K, V)
+  auto tile_step = [&](int kt, const u32x4* K, const u32x4* V, u32x4* Kn, u32x4* Vn) {
+    if (kt + 1 < ntiles) dma_tile<D>(tc, kt + 1, Kn, Vn, wave, lane);
     const int k0 = kt * kTileK;
     if (k0 <= wave_last_pos) {
-      const u32x4* K = Kl[buf];
-      const u32x4* V = Vl[buf];
       // two independent accumulation chains (the 32-key subtiles), interleaved
       f32x16 sc[2] = {f32x16{}, f32x16{}};
 #pragma unroll
@@ -551,7 +569,7 @@ __global__ __launch_bounds__(kThreads, 2) void prefill_dma_kernel(AttnParams p, 
           for (int g = 0; g < 16; ++g) {
             const int key = k0 + 32 * u + 8 * (g / 4) + 4 * half + (g % 4);
             const bool blk = (okmask >> (2 * u + (g >= 8 ? 1 : 0))) & 1u;
-            if (key > qpos || key >= s_eff || !blk) sc[u][g] = -INFINITY;
+            sc[u][g] = (key > qpos || key >= s_eff || !blk) ? -INFINITY : sc[u][g];
           }
       }
       float mx = -INFINITY;
@@ -603,11 +621,15 @@ __global__ __launch_bounds__(kThreads, 2) void prefill_dma_kernel(AttnParams p, 
         }
       }
     }
-    if (kt + 1 < ntiles) {
-      __builtin_amdgcn_s_waitcnt(0);
-      fix_tile<D>(tc, kt + 1, Vl[buf ^ 1], wave, lane);
-    }
+    // unconditional, so the compiler sees no transfer pending past this point
+    // on any path and does not make the next tile's reads wait for later DMAs
+    __builtin_amdgcn_s_waitcnt(0);
+    if (kt + 1 < ntiles) fix_tile<D>(tc, kt + 1, Vn, wave, lane);
     __syncthreads();
+  };
+  for (int kt = 0; kt < ntiles; kt += 2) {
+    tile_step(kt, K0, V0, K1, V1);
+    if (kt + 1 < ntiles) tile_step(kt + 1, K1, V1, K0, V0);
   }
 
   const float lt = pair32_sum(l_run);
