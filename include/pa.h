@@ -87,8 +87,10 @@ typedef enum pa_dtype {
  * (one float32 multiply, the reciprocal rounded once on the host) with
  * round-to-nearest-even and saturation to +-448; NaN stays NaN.
  *
- * decode_partition_tokens: keys per split-K partition of pa_decode; 0 lets the
- * library choose from the call's shape.  Otherwise a positive multiple of 128.
+ * decode_workers: number of waves pa_decode divides its key stream among
+ * (see pa_decode); 0 lets the library choose (four per compute unit of the
+ * current device).  Otherwise 1 .. 2^20; the result does not depend on it
+ * beyond float32 rounding.
  */
 typedef struct pa_attn_desc {
   int32_t num_q_heads;
@@ -100,7 +102,7 @@ typedef struct pa_attn_desc {
   float softmax_scale;
   float k_scale;
   float v_scale;
-  int32_t decode_partition_tokens;
+  int32_t decode_workers;
 } pa_attn_desc;
 
 /* Human-readable name of a status code (static storage). */
@@ -170,14 +172,17 @@ pa_status pa_cache_write(const pa_attn_desc* desc, int64_t num_tokens,
  *   h / G.
  * max_seq_len (host scalar) must be >= every seq_len of the range; keys past
  * it are ignored.  Accumulation is float32; out is act_dtype, rounded to
- * nearest even.  Long contexts are split into partitions whose float32
- * partial results (running max, sum, weighted sum) go to `workspace` and are
- * merged by a second kernel in a fixed order (deterministic output).
+ * nearest even.  The (request, K/V head, 16-token block) stream of the range
+ * is cut into desc->decode_workers equal contiguous shares, one per wave;
+ * a K/V head cut between waves leaves float32 partial results (running max,
+ * sum, weighted sum) in `workspace` that a second kernel merges in a fixed
+ * order (deterministic output for a given worker count).
  *
- * Workspace: device memory of at least pa_decode_workspace_size() bytes for
- * the same desc, request count, max_seq_len and max_blocks_per_req (else
- * PA_ERR_WORKSPACE_TOO_SMALL); it may be NULL when that size is 0.  Its
- * contents need no initialisation and are scratch after the call.
+ * Workspace: 16-byte aligned device memory of at least
+ * pa_decode_workspace_size() bytes for the same desc and request count (else
+ * PA_ERR_WORKSPACE_TOO_SMALL), required whenever the range is not empty.
+ * Its contents need no initialisation and are scratch after the call; two
+ * calls in flight at once need two workspaces.
  */
 pa_status pa_decode(const pa_attn_desc* desc, int32_t req_begin, int32_t req_end,
                     const void* q, int64_t q_row_stride,
@@ -190,10 +195,11 @@ pa_status pa_decode(const pa_attn_desc* desc, int32_t req_begin, int32_t req_end
 
 /*
  * pa_decode_workspace_size -- bytes of workspace pa_decode needs for
- * num_reqs = req_end - req_begin requests of this desc with the given
- * max_seq_len and block-table width (the split-K partials: for every request,
- * query head and partition, a float32 running max, sum and head_dim weighted
- * sums).  Host only; launches nothing.
+ * num_reqs = req_end - req_begin requests of this desc (a prefix sum over the
+ * requests, and two partial slots per worker of G float32 running maxima,
+ * sums and head_dim weighted sums).  max_seq_len and max_blocks_per_req are
+ * validated but do not change the size.  0 when num_reqs is 0.  Host only;
+ * launches nothing (it may query the current device's compute-unit count).
  */
 pa_status pa_decode_workspace_size(const pa_attn_desc* desc, int32_t num_reqs,
                                    int32_t max_seq_len, int32_t max_blocks_per_req,

@@ -38,19 +38,19 @@ class AttnDesc(ctypes.Structure):
         ("softmax_scale", ctypes.c_float),
         ("k_scale", ctypes.c_float),
         ("v_scale", ctypes.c_float),
-        ("decode_partition_tokens", ctypes.c_int32),
+        ("decode_workers", ctypes.c_int32),
     ]
 
 
 def make_desc(num_q_heads, num_kv_heads, head_dim, block_size=16, act_dtype=PA_BF16,
               cache_dtype=None, softmax_scale=None, k_scale=1.0, v_scale=1.0,
-              decode_partition_tokens=0):
+              decode_workers=0):
     if cache_dtype is None:
         cache_dtype = act_dtype
     if softmax_scale is None:
         softmax_scale = head_dim ** -0.5
     return AttnDesc(num_q_heads, num_kv_heads, head_dim, block_size, act_dtype, cache_dtype,
-                    softmax_scale, k_scale, v_scale, decode_partition_tokens)
+                    softmax_scale, k_scale, v_scale, decode_workers)
 
 
 _lib = None

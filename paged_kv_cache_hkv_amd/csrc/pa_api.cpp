@@ -13,7 +13,7 @@
 namespace {
 
 constexpr int kBlockSize = 16;
-constexpr int kChunkPerWg = 128;          // 4 waves x 32 keys: partition granularity
+constexpr int kMaxDecodeWorkers = 1 << 20;
 constexpr int kMaxGridYZ = 65535;
 constexpr float kLog2e = 1.4426950408889634f;
 
@@ -42,47 +42,43 @@ pa_status check_desc(const pa_attn_desc* d) {
       return PA_ERR_INVALID_ARG;
     }
   }
-  if (d->decode_partition_tokens < 0 || d->decode_partition_tokens % kChunkPerWg != 0) {
-    return PA_ERR_INVALID_ARG;
-  }
+  if (d->decode_workers < 0 || d->decode_workers > kMaxDecodeWorkers) return PA_ERR_INVALID_ARG;
   return PA_OK;
 }
 
-// Keys per decode partition.  Every partition costs one float32 partial of
-// G*(D+2) values per K/V head, every key of it K+V bytes; the partition is
-// long enough that the partials stay near 5% of the K/V bytes, and otherwise
-// the longest (power-of-two multiple of 128 keys) that still gives about
-// 8192 workgroups, i.e. ~32 per compute unit, to balance uneven lengths.
-int plan_partition(const pa_attn_desc* d, int num_reqs, int64_t span) {
-  if (d->decode_partition_tokens > 0) return d->decode_partition_tokens;
-  const int G = d->num_q_heads / d->num_kv_heads;
-  const int e = elem_bytes(d->cache_dtype);
-  int p_min = (40 * G) / e;
-  p_min = ((p_min + kChunkPerWg - 1) / kChunkPerWg) * kChunkPerWg;
-  if (p_min < kChunkPerWg) p_min = kChunkPerWg;
-  const double work = (double)num_reqs * d->num_kv_heads * (double)span;
-  int p = kChunkPerWg;
-  while (p < 8192 && work / (2.0 * p) >= 8192.0) p *= 2;
-  return p < p_min ? p_min : p;
+// Decode workers: waves that each stream one contiguous share of the
+// (request, K/V head, block) stream.  Four per compute unit of the current
+// device (one workgroup of four independent waves per CU, all resident for
+// the whole launch) unless the descriptor fixes the count.
+int decode_workers(const pa_attn_desc* d) {
+  if (d->decode_workers > 0) return d->decode_workers;
+  int dev = 0, cus = 0;
+  if (hipGetDevice(&dev) != hipSuccess ||
+      hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
+      cus <= 0) {
+    cus = 256;
+  }
+  return 4 * cus;
 }
 
 struct DecodePlan {
-  int part_tokens;
-  int max_parts;
-  size_t ws_bytes;
+  int workers;
+  size_t cum_off, acc_off, ml_off, ws_bytes;
 };
 
-DecodePlan plan_decode(const pa_attn_desc* d, int num_reqs, int max_seq_len, int max_blocks) {
+size_t round_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
+
+// Workspace: the stream prefix (int64, num_reqs + 1) and two float32 partial
+// slots per worker of G * (head_dim + 2) values.
+DecodePlan plan_decode(const pa_attn_desc* d, int num_reqs) {
   DecodePlan pl{};
-  const int64_t span = std::min<int64_t>((int64_t)max_seq_len, (int64_t)max_blocks * kBlockSize);
-  pl.part_tokens = plan_partition(d, num_reqs, span);
-  pl.max_parts = span <= 0 ? 0 : (int)((span + pl.part_tokens - 1) / pl.part_tokens);
-  if (pl.max_parts <= 1) {
-    pl.ws_bytes = 0;
-  } else {
-    const size_t rows = (size_t)num_reqs * d->num_q_heads * pl.max_parts;
-    pl.ws_bytes = rows * (size_t)(d->head_dim + 2) * sizeof(float) + 256;
-  }
+  pl.workers = decode_workers(d);
+  const size_t G = (size_t)(d->num_q_heads / d->num_kv_heads);
+  const size_t slots = (size_t)pl.workers * 2;
+  pl.cum_off = 0;
+  pl.acc_off = round_up((size_t)(num_reqs + 1) * sizeof(int64_t), 256);
+  pl.ml_off = pl.acc_off + round_up(slots * G * d->head_dim * sizeof(float), 256);
+  pl.ws_bytes = pl.ml_off + round_up(slots * G * 2 * sizeof(float), 256);
   return pl;
 }
 
@@ -243,7 +239,7 @@ pa_status pa_decode_workspace_size(const pa_attn_desc* desc, int32_t num_reqs,
     return PA_ERR_INVALID_ARG;
   }
   if (desc->num_q_heads / desc->num_kv_heads > 32) return PA_ERR_UNSUPPORTED;
-  *bytes = plan_decode(desc, num_reqs, max_seq_len, max_blocks_per_req).ws_bytes;
+  *bytes = num_reqs == 0 ? 0 : plan_decode(desc, num_reqs).ws_bytes;
   return PA_OK;
 }
 
@@ -261,23 +257,18 @@ pa_status pa_decode(const pa_attn_desc* desc, int32_t req_begin, int32_t req_end
   if (desc->num_q_heads / desc->num_kv_heads > 32) return PA_ERR_UNSUPPORTED;
   const int num_reqs = req_end - req_begin;
   if (num_reqs == 0) return PA_OK;
-  const DecodePlan pl = plan_decode(desc, num_reqs, max_seq_len, max_blocks_per_req);
-  if (pl.max_parts == 0) return PA_OK;
-  if (pl.ws_bytes > 0) {
-    if (workspace == nullptr || workspace_bytes < pl.ws_bytes) return PA_ERR_WORKSPACE_TOO_SMALL;
-    if (!aligned16(workspace)) return PA_ERR_INVALID_ARG;
-  }
+  const DecodePlan pl = plan_decode(desc, num_reqs);
+  if (workspace == nullptr || workspace_bytes < pl.ws_bytes) return PA_ERR_WORKSPACE_TOO_SMALL;
+  if (!aligned16(workspace)) return PA_ERR_INVALID_ARG;
   pa::AttnParams p = make_params(desc, req_begin, req_end, q, q_row_stride, query_start_loc,
                                  seq_lens, block_tables, max_blocks_per_req, key_cache,
                                  value_cache, num_blocks, out, out_row_stride);
   p.max_seq_len = max_seq_len;
-  p.part_tokens = pl.part_tokens;
-  p.max_parts = pl.max_parts;
-  if (pl.ws_bytes > 0) {
-    const size_t acc_elems = (size_t)num_reqs * desc->num_q_heads * pl.max_parts * desc->head_dim;
-    p.ws_acc = static_cast<float*>(workspace);
-    p.ws_ml = static_cast<float*>(workspace) + acc_elems;
-  }
+  p.num_workers = pl.workers;
+  unsigned char* ws = static_cast<unsigned char*>(workspace);
+  p.ws_cum = reinterpret_cast<int64_t*>(ws + pl.cum_off);
+  p.ws_acc = reinterpret_cast<float*>(ws + pl.acc_off);
+  p.ws_ml = reinterpret_cast<float*>(ws + pl.ml_off);
   return from_hip(pa::launch_decode(p, desc->act_dtype, desc->cache_dtype,
                                     static_cast<hipStream_t>(stream)));
 }

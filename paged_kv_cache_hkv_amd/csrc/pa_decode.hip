@@ -1,5 +1,5 @@
 // pa_decode kernels: attention of one-token (decode) requests through their
-// block tables, with split-K over long contexts.
+// block tables.
 //
 // What is computed (PagedAttention decode in "vLLM 推理全流程深度解析"; the
 // decode rows of stop 10 in "Tour: One forward pass"): for request r with
@@ -9,27 +9,44 @@
 // Decode is bound by reading the K/V history once ("vLLM 推理全流程深度解析":
 // decode is memory-bound; PagedAttention reads the cache block by block with
 // coalesced bursts), so the design goal is to stream every K/V byte of a
-// request exactly once, for all G query heads that share it.
+// request exactly once, for all G query heads that share it, at the rate
+// HBM delivers.
 //
-// Work decomposition.  A workgroup of 4 waves owns one (request, K/V head,
-// partition of part_tokens keys).  Its waves take the partition's 32-key
-// chunks (two 16-token cache blocks) round-robin.  For one chunk a wave:
-//   * loads the chunk's K rows straight into MFMA A-operand registers: lane
-//     (token t = lane%16 of a block, quarter q4 = lane/16) reads 16 contiguous
-//     bytes per step, so one load instruction covers 16 rows x 64 bytes;
+// Work decomposition (persistent, stream-split).  Flatten the batch into one
+// stream of work units: for each decode request, for each K/V head, its
+// 16-token cache blocks in order.  The stream of T units is cut into W equal
+// contiguous ranges, one per wave ("worker"); W is a few waves per compute
+// unit and every worker is resident for the whole launch, so each wave
+// streams ~T/W blocks back to back with no start-up or tail bubbles and no
+// dependence on how the contexts' lengths are distributed.  A worker's range
+// covers a few (request, K/V head) segments.  A segment that is a whole
+// (request, K/V head) is finished in place and its output rows written
+// directly; a segment cut by a range boundary leaves a float32 partial
+// (running max, sum, weighted sum) in the worker's slot 0 (its first segment)
+// or slot 1 (its last), and the reduce kernel merges the partials of each cut
+// head in worker order (deterministic, no atomics).
+//
+// Streaming.  Each wave owns a ring of S LDS stages; a stage holds one block
+// (K and V rows of one head) plus, for the first block of a segment, the
+// segment's G query rows.  Asynchronous global -> LDS copies are issued S-1
+// blocks ahead, so the bytes in flight cost no registers.  A copy
+// instruction moves 1 KB: whole 16-byte chunks of 16/8/4 consecutive token
+// rows, each row's chunks scattered by an XOR of the token so the MFMA
+// operand reads below hit distinct LDS banks.  Per block a wave:
 //   * computes S^T[token][head] = K . Q^T on v_mfma_f32_16x16x32 with the
 //     G <= 16 query heads of the group as the 16 columns (zero-padded; G = 32
-//     uses two column tiles sharing the same K/V registers);
-//   * keeps an online softmax per head in float32 (max shared by the 4 lanes
-//     that hold a head's scores, exp2 with the scale folded into log2 units);
-//   * loads V rows as 8 tokens x (D/16) contiguous elements per lane (a load
-//     instruction covers 4 whole rows) and re-pairs them in registers with
-//     byte permutes into the B operand of O = P . V, so the PV product is also
-//     an MFMA and no LDS transpose is needed.
-// At the end the 4 waves merge their (max, sum, weighted sum) in LDS.  A
-// request that fits one partition writes its output row directly; otherwise
-// each partition writes float32 partials to the workspace and the reduce
-// kernel merges them in partition order (deterministic, no atomics).
+//     uses two column tiles sharing the same K/V operands); K rows are read
+//     from LDS as 16-byte A-operand pieces;
+//   * keeps an online softmax per head in float32: the max is shared by the 4
+//     lanes that hold a head's scores, exp2 with the scale folded in, and the
+//     accumulator is only rescaled when a head's max grows by more than 2^8
+//     (exact up to rounding: the reference max of a softmax is arbitrary as
+//     long as nothing overflows);
+//   * accumulates O^T[d][head] = V^T . P^T on v_mfma_f32_16x16x16: the scores
+//     are already the B operand (one head per lane column, 4 tokens per lane)
+//     and V^T comes from LDS with the transposing ds_read_b64_tr_b16 (16-bit
+//     caches) or row reads re-paired by byte permutes (fp8), so a lane's
+//     accumulators all belong to one head and every rescale is lane-local.
 //
 // fp8 (OCP e4m3fn) caches are widened to bf16/fp16 exactly in registers with
 // the gfx950 packed converts; the K scale is folded into the score scale and
@@ -41,337 +58,484 @@ namespace pa {
 
 namespace {
 
-constexpr int kWaves = 4;
+constexpr int kWaves = 4;                 // waves per workgroup (independent workers)
 constexpr int kThreads = 64 * kWaves;
-constexpr int kBlock = 16;   // tokens per cache block
-constexpr int kChunk = 32;   // tokens per wave iteration
+constexpr int kBlock = 16;                // tokens per cache block
+constexpr float kRescaleLog2 = 8.f;       // lazy rescale threshold (log2 units)
+constexpr int kLdsBudget = 160 * 1024;    // LDS of one compute unit
+#ifndef PA_DECODE_STAGES
+#define PA_DECODE_STAGES 3
+#endif
+constexpr int kStages = PA_DECODE_STAGES; // LDS ring depth per wave (where it fits)
 
-template <int D, typename CT, int KVB, int HT>
+// Token of MFMA row i (0..15) of a block.  Any permutation works as long as
+// scores and V use the same one; this one makes the four lane groups that
+// read one V token slot at a time (fp8 path) land on different LDS bank
+// halves.
+__device__ inline int row_token(int i) { return i ^ ((i >> 2) & 3); }
+
+// Geometry of one block of one head in a ring stage.
+template <int D, int KVB>
+struct Ring {
+  static constexpr int kRowBytes = D * KVB;             // one token row
+  static constexpr int kCPR = kRowBytes / 16;           // 16-byte chunks per row: 16, 8 or 4
+  static constexpr int kBlkBytes = kBlock * kRowBytes;  // K (or V) bytes of a block
+  static constexpr int kIPT = kBlkBytes / 1024;         // copy instructions per tensor
+  static constexpr int kIPB = 2 * kIPT;                 // per block (K and V)
+  static constexpr int kSh = kCPR == 16 ? 0 : (kCPR == 8 ? 1 : 2);   // log2(16 / kCPR)
+  // chunk c of token t sits at slot c ^ swk(t) (K) / c ^ swv(t) (V) of its row
+  __device__ static inline int swk(int t) { return (t >> kSh) & (kCPR - 1); }
+  __device__ static inline int swv(int t) {
+    return KVB == 2 ? 2 * ((t >> kSh) & (kCPR / 2 - 1)) : 0;
+  }
+};
+
+// Wait until at most n (wave-uniform, 0 .. 3) blocks' copies are in flight.
+// Copies of query rows are issued before the block they belong to, so they
+// only make the count conservative.
+template <int IPB>
+__device__ inline void wait_blocks(int n) {
+  if (n >= 3) {
+    wait_vmcnt<3 * IPB>();
+  } else if (n == 2) {
+    wait_vmcnt<2 * IPB>();
+  } else if (n == 1) {
+    wait_vmcnt<IPB>();
+  } else {
+    wait_vmcnt<0>();
+  }
+}
+
+typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) bf16x4 lds_bf16x4;
+
+// ds_read_b64_tr_b16: in each 16-lane group, lane i supplies the address of
+// an 8-byte row R_i of four 16-bit values; lane j receives R_{4k + j/4}[j%4]
+// for k = 0..3.
+__device__ inline u32x2 lds_read_tr16(const unsigned char* p) {
+  lds_bf16x4* lp = (lds_bf16x4*)(const_cast<unsigned char*>(p));
+  return __builtin_bit_cast(u32x2, __builtin_amdgcn_ds_read_tr16_b64_v4bf16(lp));
+}
+
+// Cache blocks request rr (index within the call) streams: 0 for a request
+// that is not a decode (query length != 1) or has no keys.  `uniform`: rr is
+// the same in every lane (scalar loads).
+__device__ inline int stream_blocks(const AttnParams& p, int rr, bool uniform) {
+  const int r = p.req_begin + rr;
+  int q0, q1, s;
+  if (uniform) {
+    q0 = load_uniform(p.qsl, r);
+    q1 = load_uniform(p.qsl, r + 1);
+    s = load_uniform(p.seq_lens, r);
+  } else {
+    q0 = p.qsl[r];
+    q1 = p.qsl[r + 1];
+    s = p.seq_lens[r];
+  }
+  if (q1 - q0 != 1) return 0;
+  s = min(min(s, p.max_seq_len), p.max_blocks_per_req * kBlock);
+  return s > 0 ? (s + kBlock - 1) / kBlock : 0;
+}
+
+__device__ inline int64_t readlane64(int64_t v, int l) {
+  const int lo = __builtin_amdgcn_readlane((int)(uint32_t)v, l);
+  const int hi = __builtin_amdgcn_readlane((int)(v >> 32), l);
+  return (int64_t)(((uint64_t)(uint32_t)hi << 32) | (uint32_t)lo);
+}
+
+// Inclusive prefix sum over the 64 lanes.
+__device__ inline int64_t wave_scan(int64_t v) {
+  const int lane = __lane_id();
+#pragma unroll
+  for (int off = 1; off < 64; off <<= 1) {
+    const int src = ((lane - off) & 63) << 2;
+    const int lo = __builtin_amdgcn_ds_bpermute(src, (int)(uint32_t)v);
+    const int hi = __builtin_amdgcn_ds_bpermute(src, (int)(v >> 32));
+    const int64_t t = (int64_t)(((uint64_t)(uint32_t)hi << 32) | (uint32_t)lo);
+    v += (lane >= off) ? t : 0;
+  }
+  return v;
+}
+
+// First stream unit of worker w (W workers over T units).
+__device__ inline int64_t range_begin(int64_t w, int64_t T, int64_t W) { return w * T / W; }
+
+// Position in the stream: request (index within the call), K/V head, block
+// of that head, and the request's block count.
+struct Cursor {
+  int rr, kvh, b, nb;
+};
+
+// Advance by one unit (wave-uniform); skips requests that stream nothing.
+__device__ inline void advance(const AttnParams& p, Cursor& c) {
+  if (++c.b < c.nb) return;
+  c.b = 0;
+  if (++c.kvh < p.num_kv_heads) return;
+  c.kvh = 0;
+  do {
+    ++c.rr;
+    c.nb = c.rr < p.num_reqs ? stream_blocks(p, c.rr, true) : 1;
+  } while (c.nb == 0);
+}
+
+template <int D, typename CT, int KVB, int HT, int S>
 __global__ __launch_bounds__(kThreads) void decode_kernel(AttnParams p) {
   using M = Mfma<CT>;
   using vec8 = typename M::vec8;
+  using R = Ring<D, KVB>;
   constexpr int KS = D / 32;               // QK MFMA steps (32 d each)
-  constexpr int NM = D / 16;               // PV MFMAs (16 output columns each)
-  constexpr int VE = D / 16;               // V elements per lane per token
-  constexpr int VW = (VE * KVB + 3) / 4;   // dwords per lane per V token
-  constexpr int KP = (KVB == 2) ? KS : KS / 2;  // 16-byte K loads per lane per block
-
-  __shared__ float red_acc[kWaves][16][D];
-  __shared__ float red_m[kWaves][16];
-  __shared__ float red_l[kWaves][16];
-
-  const int rr = blockIdx.z;
-  const int r = p.req_begin + rr;
-  const int kvh = blockIdx.y;
-  const int part = blockIdx.x;
-  const int q_row = p.qsl[r];
-  if (p.qsl[r + 1] - q_row != 1) return;
-  int s_eff = min(p.seq_lens[r], p.max_seq_len);
-  s_eff = min(s_eff, p.max_blocks_per_req * kBlock);
-  const int P = p.part_tokens;
-  const int tok_begin = part * P;
-  if (tok_begin >= s_eff) return;
-  const int tok_end = min(tok_begin + P, s_eff);
-  const int nparts = (s_eff + P - 1) / P;
-  const int nblk = (s_eff + kBlock - 1) / kBlock;
-  const int G = p.group;
-  const int Hkv = p.num_kv_heads;
+  constexpr int NM = D / 16;               // PV MFMAs per block (16 rows of O^T each)
+  constexpr int VE = D / 16;               // fp8 path: V bytes per lane per token
+  constexpr int kQCap = HT * 16 * D * 2;   // query rows of one segment (<= 16*HT heads)
+  constexpr int kStage = 2 * R::kBlkBytes + kQCap;   // K | V | Q
+  static_assert(S >= 2 && S <= 4, "ring depth");
+  static_assert(kWaves * S * kStage <= kLdsBudget, "ring exceeds LDS");
+  __shared__ __attribute__((aligned(1024))) unsigned char lds[kWaves * S * kStage];
 
   const int lane = threadIdx.x & 63;
   const int wave = wave_uniform(threadIdx.x >> 6);
   const int q4 = lane >> 4;
   const int c16 = lane & 15;
+  const int W = p.num_workers;
+  const int worker = blockIdx.x * kWaves + wave;
+  if (worker >= W) return;
+  const int Rn = p.num_reqs;
+  const int G = p.group;
+  const int Hkv = p.num_kv_heads;
 
-  // ---- Q as the B operand of S^T = K.Q^T: lane holds head (ht*16 + c16) ----
-  vec8 qop[HT][KS];
-  const CT* qbase = static_cast<const CT*>(p.q) + (int64_t)q_row * p.q_row_stride;
-#pragma unroll
-  for (int ht = 0; ht < HT; ++ht) {
-    const int hig = ht * 16 + c16;
-#pragma unroll
-    for (int s = 0; s < KS; ++s) {
-      const int d0 = (KVB == 2) ? (32 * s + 8 * q4) : (64 * (s / 2) + 16 * q4 + 8 * (s % 2));
-      if (hig < G) {
-        qop[ht][s] = __builtin_bit_cast(vec8, ld16(qbase + (int64_t)(kvh * G + hig) * D + d0));
-      } else {
-        qop[ht][s] = __builtin_bit_cast(vec8, u32x4{0u, 0u, 0u, 0u});
+  // ---- the stream: total units T, this worker's range, its first unit ----
+  int64_t T = 0;
+  for (int c = 0; c < Rn; c += 64) {
+    const int64_t v = (c + lane < Rn) ? (int64_t)Hkv * stream_blocks(p, c + lane, false) : 0;
+    T += readlane64(wave_scan(v), 63);
+  }
+  const int64_t g0 = range_begin(worker, T, W);
+  const int64_t n = range_begin(worker + 1, T, W) - g0;
+  Cursor cur{0, 0, 0, 0};
+  {
+    // worker 0 also publishes the exclusive prefix for the reduce kernel
+    int64_t run = 0;
+    bool found = false;
+    for (int c = 0; c < Rn; c += 64) {
+      const int64_t v = (c + lane < Rn) ? (int64_t)Hkv * stream_blocks(p, c + lane, false) : 0;
+      const int64_t incl = wave_scan(v);
+      const int64_t excl = run + incl - v;
+      if (worker == 0 && c + lane < Rn) p.ws_cum[c + lane] = excl;
+      const uint64_t hit = __builtin_amdgcn_ballot_w64(v > 0 && excl <= g0 && g0 < excl + v);
+      if (!found && hit != 0) {
+        const int l = __builtin_ctzll(hit);
+        cur.rr = c + l;
+        const int64_t within = g0 - readlane64(excl, l);
+        cur.nb = stream_blocks(p, cur.rr, true);
+        cur.kvh = (int)(within / cur.nb);
+        cur.b = (int)(within % cur.nb);
+        found = true;
+        if (worker != 0) break;
       }
+      run += readlane64(incl, 63);
     }
+    if (worker == 0 && lane == 0) p.ws_cum[Rn] = T;
+    if (!found || n <= 0) return;
   }
 
-  const int32_t* bt_row = p.block_tables + (int64_t)r * p.max_blocks_per_req;
-  const unsigned char* kc = static_cast<const unsigned char*>(p.key_cache);
-  const unsigned char* vc = static_cast<const unsigned char*>(p.value_cache);
   const int64_t tok_stride = (int64_t)Hkv * D * KVB;     // bytes between slots
   const int64_t blk_stride = tok_stride * kBlock;        // bytes between blocks
-  const int64_t head_off = (int64_t)kvh * D * KVB;
+  const int64_t num_blocks = p.num_blocks;
+  auto block_id = [&](const Cursor& c) {   // physical block, or -1 when absent
+    const int id = load_uniform(p.block_tables,
+                                (int64_t)(p.req_begin + c.rr) * p.max_blocks_per_req + c.b);
+    return (id >= 0 && (int64_t)id < num_blocks) ? id : -1;
+  };
 
-  float m_run[HT], l_run[HT];
-  f32x4 acc[HT][NM];
+  // per-lane source offsets of the copy instructions of one block
+  int koff[R::kIPT], voff[R::kIPT];
 #pragma unroll
-  for (int ht = 0; ht < HT; ++ht) {
-    m_run[ht] = -INFINITY;
-    l_run[ht] = 0.f;
+  for (int j = 0; j < R::kIPT; ++j) {
+    const int pidx = 64 * j + lane;
+    const int t = pidx / R::kCPR;
+    const int pos = pidx % R::kCPR;
+    koff[j] = (int)(t * tok_stride) + 16 * (pos ^ R::swk(t));
+    voff[j] = (int)(t * tok_stride) + 16 * (pos ^ R::swv(t));
+  }
+  unsigned char* ring = lds + wave * S * kStage;
+  const unsigned ring_m0 = lds_offset(ring);
+  const int qbytes = G * D * 2;
+
+  // ---- issue side: copies of unit j into stage st (a segment's first unit
+  // carries the segment's query rows, copied first) ----
+  Cursor ic = cur;
+  auto issue = [&](int64_t j, int st) {
+    const unsigned dst = ring_m0 + st * kStage;
+    if (ic.b == 0 || j == 0) {
+      const unsigned char* qb = static_cast<const unsigned char*>(p.q) +
+                                ((int64_t)load_uniform(p.qsl, p.req_begin + ic.rr) * p.q_row_stride +
+                                 (int64_t)ic.kvh * G * D) * 2;
+      for (int k = 0; k < qbytes; k += 1024)
+        if (k + 16 * lane < qbytes) lds_dma16(qb, (unsigned)(k + 16 * lane), dst + 2 * R::kBlkBytes + k);
+    }
+    const int id = block_id(ic);
+    const int64_t boff = (int64_t)(id < 0 ? 0 : id) * blk_stride + (int64_t)ic.kvh * D * KVB;
+    const unsigned char* kb = static_cast<const unsigned char*>(p.key_cache) + boff;
+    const unsigned char* vb = static_cast<const unsigned char*>(p.value_cache) + boff;
 #pragma unroll
-    for (int m = 0; m < NM; ++m) acc[ht][m] = f32x4{0.f, 0.f, 0.f, 0.f};
+    for (int i = 0; i < R::kIPT; ++i) {
+      lds_dma16(kb, (unsigned)koff[i], dst + 1024 * i);
+      lds_dma16(vb, (unsigned)voff[i], dst + R::kBlkBytes + 1024 * i);
+    }
+    advance(p, ic);
+  };
+
+  // ---- per-lane LDS read offsets within a stage ----
+  const int tk = row_token(c16);                  // token of this lane's K row
+  int kread[KVB == 2 ? KS : KS / 2];
+#pragma unroll
+  for (int s = 0; s < (KVB == 2 ? KS : KS / 2); ++s) {
+    const int chunk = 4 * s + q4;
+    kread[s] = 16 * (tk * R::kCPR + (chunk ^ R::swk(tk)));
+  }
+  int vread[KVB == 2 ? NM : 4];
+  if constexpr (KVB == 2) {
+    // V^T rows: lane supplies token row_token(4*q4 + c16/4), d = 16m + 4*(c16%4)
+    const int tv = row_token(4 * q4 + c16 / 4);
+#pragma unroll
+    for (int m = 0; m < NM; ++m) {
+      const int chunk = 2 * m + (c16 % 4) / 2;
+      vread[m] = R::kBlkBytes + 16 * (tv * R::kCPR + (chunk ^ R::swv(tv))) + 8 * (c16 & 1);
+    }
+  } else {
+    // fp8 rows: tokens row_token(4*q4 + k), bytes VE*c16 .. VE*c16 + VE-1
+#pragma unroll
+    for (int k = 0; k < 4; ++k) vread[k] = R::kBlkBytes + row_token(4 * q4 + k) * R::kRowBytes + VE * c16;
   }
 
-  const int first_chunk = tok_begin / kChunk;
-  const int end_chunk = (tok_end + kChunk - 1) / kChunk;
-  for (int ch = first_chunk + wave; ch < end_chunk; ch += kWaves) {
-    const int j0 = ch * kChunk;
-    // physical blocks of the chunk's two 16-token halves
-    int64_t boff[2];
-    bool bvalid[2];
-#pragma unroll
-    for (int t = 0; t < 2; ++t) {
-      const int bi = j0 / kBlock + t;
-      int b = 0;
-      bool ok = bi < nblk;
-      if (ok) {
-        b = bt_row[bi];
-        ok = (b >= 0) && ((int64_t)b < p.num_blocks);
-      }
-      bvalid[t] = ok;
-      boff[t] = ok ? (int64_t)b * blk_stride : 0;   // absent blocks read block 0, then masked
-    }
-    const bool need_mask = (j0 + kChunk > tok_end) || !bvalid[0] || !bvalid[1];
+  for (int j = 0; j < S - 1; ++j)
+    if (j < n) issue(j, j);
 
-    // ---- issue K and V loads ----
-    u32x4 kraw[2][KP];
-#pragma unroll
-    for (int t = 0; t < 2; ++t) {
-      const unsigned char* row = kc + boff[t] + (int64_t)c16 * tok_stride + head_off;
-#pragma unroll
-      for (int s = 0; s < KP; ++s) {
-        const int d0 = (KVB == 2) ? (32 * s + 8 * q4) : (64 * s + 16 * q4);
-        kraw[t][s] = ld16(row + d0 * KVB);
-      }
-    }
-    unsigned vraw[8][VW];
-#pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      const int t = i / 4;
-      const int off = 4 * q4 + (i % 4);
-      const unsigned char* row = vc + boff[t] + (int64_t)off * tok_stride + head_off +
-                                 (int64_t)(VE * c16) * KVB;
-      if constexpr (VW == 4) {
-        u32x4 v = ld16(row);
-        vraw[i][0] = v[0]; vraw[i][1] = v[1]; vraw[i][2] = v[2]; vraw[i][3] = v[3];
-      } else if constexpr (VW == 2) {
-        u32x2 v = ld8(row);
-        vraw[i][0] = v[0]; vraw[i][1] = v[1];
-      } else {
-        vraw[i][0] = ld4(row);
-      }
-    }
+  const float c2 = p.scale_log2;
+  vec8 qop[HT][KS];
+  float m_used[HT], l_run[HT];
+  f32x4 acc[HT][NM];
+  int seg = 0;          // segments this worker has finished
+  int seg_b0 = 0;       // first block of the current segment
 
-    // ---- K operands ----
-    vec8 kop[2][KS];
+  for (int64_t i = 0; i < n; ++i) {
+    if (i + S - 1 < n) issue(i + S - 1, (int)((i + S - 1) % S));
+    wait_blocks<R::kIPB>((int)min((int64_t)(S - 1), n - 1 - i));
+    const unsigned char* st = ring + (int)(i % S) * kStage;
+
+    // ---- segment start: query operands, fresh softmax state ----
+    if (cur.b == 0 || i == 0) {
+      seg_b0 = cur.b;
 #pragma unroll
-    for (int t = 0; t < 2; ++t) {
+      for (int ht = 0; ht < HT; ++ht) {
+        const int hig = ht * 16 + c16;
 #pragma unroll
-      for (int s = 0; s < KS; ++s) {
-        if constexpr (KVB == 2) {
-          kop[t][s] = __builtin_bit_cast(vec8, kraw[t][s]);
-        } else {
-          const u32x4& w = kraw[t][s / 2];
-          const unsigned d0 = w[2 * (s % 2)], d1 = w[2 * (s % 2) + 1];
-          u32x4 o{M::from_fp8x2(d0, false), M::from_fp8x2(d0, true),
-                  M::from_fp8x2(d1, false), M::from_fp8x2(d1, true)};
-          kop[t][s] = __builtin_bit_cast(vec8, o);
+        for (int s = 0; s < KS; ++s) {
+          const int d0 = (KVB == 2) ? (32 * s + 8 * q4) : (64 * (s / 2) + 16 * q4 + 8 * (s % 2));
+          const u32x4 v = *reinterpret_cast<const u32x4*>(st + 2 * R::kBlkBytes + (hig * D + d0) * 2);
+          qop[ht][s] = __builtin_bit_cast(vec8, hig < G ? v : u32x4{0u, 0u, 0u, 0u});
         }
+        m_used[ht] = -INFINITY;
+        l_run[ht] = 0.f;
+#pragma unroll
+        for (int m = 0; m < NM; ++m) acc[ht][m] = f32x4{0.f, 0.f, 0.f, 0.f};
       }
     }
 
     // ---- S^T = K . Q^T ----
-    f32x4 sc[HT][2];
+    f32x4 sc[HT];
+#pragma unroll
+    for (int ht = 0; ht < HT; ++ht) sc[ht] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int s = 0; s < KS; ++s) {
+      vec8 kop;
+      if constexpr (KVB == 2) {
+        kop = __builtin_bit_cast(vec8, *reinterpret_cast<const u32x4*>(st + kread[s]));
+      } else {
+        const u32x4 w = *reinterpret_cast<const u32x4*>(st + kread[s / 2]);
+        const unsigned d0 = w[2 * (s % 2)], d1 = w[2 * (s % 2) + 1];
+        kop = __builtin_bit_cast(vec8, u32x4{M::from_fp8x2(d0, false), M::from_fp8x2(d0, true),
+                                             M::from_fp8x2(d1, false), M::from_fp8x2(d1, true)});
+      }
+#pragma unroll
+      for (int ht = 0; ht < HT; ++ht) sc[ht] = M::mma16(kop, qop[ht][s], sc[ht]);
+    }
+
+    // ---- masks: tokens past the sequence, absent blocks (selects only) ----
+    const int s_eff = min(min(load_uniform(p.seq_lens, p.req_begin + cur.rr), p.max_seq_len),
+                          p.max_blocks_per_req * kBlock);
+    const int tok0 = cur.b * kBlock;
+    const bool blk_ok = block_id(cur) >= 0;
+    unsigned vm0 = 0xFFFFFFFFu, vm1 = 0xFFFFFFFFu;
+    if (!blk_ok || tok0 + kBlock > s_eff) {
+      bool bad[4];
+#pragma unroll
+      for (int k = 0; k < 4; ++k) bad[k] = !blk_ok || tok0 + row_token(4 * q4 + k) >= s_eff;
+      vm0 = (bad[0] ? 0u : 0x0000FFFFu) | (bad[1] ? 0u : 0xFFFF0000u);
+      vm1 = (bad[2] ? 0u : 0x0000FFFFu) | (bad[3] ? 0u : 0xFFFF0000u);
+#pragma unroll
+      for (int ht = 0; ht < HT; ++ht)
+#pragma unroll
+        for (int k = 0; k < 4; ++k) sc[ht][k] = bad[k] ? -INFINITY : sc[ht][k];
+    }
+
+    // ---- online softmax (lazy rescale), P^T as the B operand ----
+    u32x2 pop[HT];
 #pragma unroll
     for (int ht = 0; ht < HT; ++ht) {
+      float x[4];
 #pragma unroll
-      for (int t = 0; t < 2; ++t) {
-        f32x4 a = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-        for (int s = 0; s < KS; ++s) a = M::mma16(kop[t][s], qop[ht][s], a);
-        sc[ht][t] = a;
-      }
-    }
-
-    // ---- masking of absent tokens (last chunk, absent blocks) ----
-    if (need_mask) {
-#pragma unroll
-      for (int i = 0; i < 8; ++i) {
-        const int t = i / 4;
-        const int tok = j0 + 16 * t + 4 * q4 + (i % 4);
-        // selects, not a branch per token: every register is written on
-        // every path (0 * NaN would poison P.V, so absent V rows become 0)
-        const bool bad = !bvalid[t] || tok >= tok_end;
-#pragma unroll
-        for (int w = 0; w < VW; ++w) vraw[i][w] = bad ? 0u : vraw[i][w];
-#pragma unroll
-        for (int ht = 0; ht < HT; ++ht) sc[ht][t][i % 4] = bad ? -INFINITY : sc[ht][t][i % 4];
-      }
-    }
-
-    // ---- V operands: B[k = 8*q4 + i][n = c16] = V[token(i)][VE*c16 + m] ----
-    vec8 vop[NM];
-#pragma unroll
-    for (int m = 0; m < NM; ++m) {
-      unsigned w4[4];
-#pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        const unsigned* a = vraw[2 * j];
-        const unsigned* b = vraw[2 * j + 1];
-        if constexpr (KVB == 2) {
-          w4[j] = (m & 1) ? perm(b[m / 2], a[m / 2], 0x07060302u)
-                          : perm(b[m / 2], a[m / 2], 0x05040100u);
-        } else {
-          const unsigned aw = a[m / 4], bw = b[m / 4];
-          const unsigned x = (m & 2) ? perm(bw, aw, 0x07030602u) : perm(bw, aw, 0x05010400u);
-          w4[j] = M::from_fp8x2(x, (m & 1) != 0);
-        }
-      }
-      vop[m] = __builtin_bit_cast(vec8, u32x4{w4[0], w4[1], w4[2], w4[3]});
-    }
-
-    // ---- online softmax and P.V per head tile ----
-#pragma unroll
-    for (int ht = 0; ht < HT; ++ht) {
-      float x[8];
-#pragma unroll
-      for (int i = 0; i < 8; ++i) x[i] = sc[ht][i / 4][i % 4] * p.scale_log2;
-      float mx = x[0];
-#pragma unroll
-      for (int i = 1; i < 8; ++i) mx = fmaxf(mx, x[i]);
+      for (int k = 0; k < 4; ++k) x[k] = sc[ht][k] * c2;
+      float mx = fmaxf(fmaxf(x[0], x[1]), fmaxf(x[2], x[3]));
       mx = fmaxf(mx, shfl_xor(mx, 16));
       mx = fmaxf(mx, shfl_xor(mx, 32));
-      const float m_new = fmaxf(m_run[ht], mx);
-      const float m_safe = (m_new == -INFINITY) ? 0.f : m_new;
-      const float alpha = fast_exp2(m_run[ht] - m_safe);
-      float pr[8];
-      float psum = 0.f;
+      const bool grow = mx > m_used[ht] + kRescaleLog2;
+      if (__builtin_amdgcn_ballot_w64(grow)) {
+        const float m_new = grow ? mx : m_used[ht];
+        const float alpha = grow ? fast_exp2(m_used[ht] - m_new) : 1.f;
+        l_run[ht] *= alpha;
 #pragma unroll
-      for (int i = 0; i < 8; ++i) {
-        pr[i] = fast_exp2(x[i] - m_safe);
-        psum += pr[i];
+        for (int m = 0; m < NM; ++m) acc[ht][m] *= alpha;
+        m_used[ht] = m_new;
       }
-      l_run[ht] = l_run[ht] * alpha + psum;
-      m_run[ht] = m_new;
-      // accumulator rows are heads 4*q4 + i: fetch their rescale factors
+      const float msub = (m_used[ht] == -INFINITY) ? 0.f : m_used[ht];
+      float pr[4];
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const float a_i = shfl(alpha, 4 * q4 + i);
-#pragma unroll
-        for (int m = 0; m < NM; ++m) acc[ht][m][i] *= a_i;
-      }
-      const u32x4 pw{pack2<CT>(pr[0], pr[1]), pack2<CT>(pr[2], pr[3]),
-                     pack2<CT>(pr[4], pr[5]), pack2<CT>(pr[6], pr[7])};
-      const vec8 pop = __builtin_bit_cast(vec8, pw);
-#pragma unroll
-      for (int m = 0; m < NM; ++m) acc[ht][m] = M::mma16(pop, vop[m], acc[ht][m]);
+      for (int k = 0; k < 4; ++k) pr[k] = fast_exp2(x[k] - msub);
+      l_run[ht] += (pr[0] + pr[1]) + (pr[2] + pr[3]);
+      pop[ht] = u32x2{pack2<CT>(pr[0], pr[1]), pack2<CT>(pr[2], pr[3])};
     }
-  }
 
-  // ---- merge the 4 waves, then write the output or the partition partials ----
-  const int Hq = p.num_q_heads;
+    // ---- O^T += V^T . P^T ----
+    if constexpr (KVB == 2) {
 #pragma unroll
-  for (int ht = 0; ht < HT; ++ht) {
-    float lt = l_run[ht];
-    lt += shfl_xor(lt, 16);
-    lt += shfl_xor(lt, 32);
-    if (ht > 0) __syncthreads();
+      for (int m = 0; m < NM; ++m) {
+        u32x2 a = lds_read_tr16(st + vread[m]);
+        a = u32x2{a[0] & vm0, a[1] & vm1};
 #pragma unroll
-    for (int m = 0; m < NM; ++m) {
-#pragma unroll
-      for (int i = 0; i < 4; ++i) red_acc[wave][4 * q4 + i][VE * c16 + m] = acc[ht][m][i];
-    }
-    if (q4 == 0) {
-      red_m[wave][c16] = m_run[ht];
-      red_l[wave][c16] = lt;
-    }
-    __syncthreads();
-    constexpr int EPT = D / 16;   // outputs per thread: 16 heads x D over 256 threads
-    const int hh = threadIdx.x / 16;
-    const int d0 = (threadIdx.x % 16) * EPT;
-    const int hig = ht * 16 + hh;
-    if (hig < G) {
-      float mw[kWaves];
-      float mmax = -INFINITY;
-#pragma unroll
-      for (int w = 0; w < kWaves; ++w) {
-        mw[w] = red_m[w][hh];
-        mmax = fmaxf(mmax, mw[w]);
+        for (int ht = 0; ht < HT; ++ht) acc[ht][m] = M::mma16k16(a, pop[ht], acc[ht][m]);
       }
-      const float msafe = (mmax == -INFINITY) ? 0.f : mmax;
-      float L = 0.f;
-      float wgt[kWaves];
+    } else {
+      unsigned w[4][(VE + 3) / 4];
 #pragma unroll
-      for (int w = 0; w < kWaves; ++w) {
-        wgt[w] = fast_exp2(mw[w] - msafe);
-        L += wgt[w] * red_l[w][hh];
-      }
-      float o[EPT];
-#pragma unroll
-      for (int e = 0; e < EPT; ++e) {
-        float v = 0.f;
-#pragma unroll
-        for (int w = 0; w < kWaves; ++w) v += wgt[w] * red_acc[w][hh][d0 + e];
-        o[e] = v;
-      }
-      const int qh = kvh * G + hig;
-      if (nparts == 1) {
-        const float inv = (L > 0.f) ? p.v_scale / L : 0.f;
-        unsigned short* orow = static_cast<unsigned short*>(p.out) +
-                               (int64_t)q_row * p.out_row_stride + (int64_t)qh * D + d0;
-        unsigned pk[EPT / 2];
-#pragma unroll
-        for (int e = 0; e < EPT / 2; ++e) pk[e] = pack2<CT>(o[2 * e] * inv, o[2 * e + 1] * inv);
-        if constexpr (EPT == 8) {
-          st16(orow, u32x4{pk[0], pk[1], pk[2], pk[3]});
+      for (int k = 0; k < 4; ++k) {
+        if constexpr (VE == 8) {
+          const u32x2 v = *reinterpret_cast<const u32x2*>(st + vread[k]);
+          w[k][0] = v[0];
+          w[k][1] = v[1];
         } else {
-          st8(orow, u32x2{pk[0], pk[1]});
-        }
-      } else {
-        const int64_t slot = ((int64_t)rr * Hq + qh) * p.max_parts + part;
-        float* wa = p.ws_acc + slot * D + d0;
-#pragma unroll
-        for (int e = 0; e < EPT; ++e) wa[e] = o[e];
-        if ((threadIdx.x % 16) == 0) {
-          p.ws_ml[slot * 2] = mmax;
-          p.ws_ml[slot * 2 + 1] = L;
+          w[k][0] = *reinterpret_cast<const unsigned*>(st + vread[k]);
         }
       }
+#pragma unroll
+      for (int m = 0; m < NM; ++m) {
+        const unsigned sel = (m & 2) ? 0x07030602u : 0x05010400u;
+        const unsigned x01 = perm(w[1][m / 4], w[0][m / 4], sel);
+        const unsigned x23 = perm(w[3][m / 4], w[2][m / 4], sel);
+        u32x2 a{M::from_fp8x2(x01, (m & 1) != 0), M::from_fp8x2(x23, (m & 1) != 0)};
+        a = u32x2{a[0] & vm0, a[1] & vm1};
+#pragma unroll
+        for (int ht = 0; ht < HT; ++ht) acc[ht][m] = M::mma16k16(a, pop[ht], acc[ht][m]);
+      }
     }
+
+    // ---- segment end: output rows, or a partial for the reduce kernel ----
+    if (cur.b == cur.nb - 1 || i == n - 1) {
+      const bool whole = seg_b0 == 0 && cur.b == cur.nb - 1;
+      const int64_t slot = (int64_t)worker * 2 + (seg == 0 ? 0 : 1);
+      const int q_row = load_uniform(p.qsl, p.req_begin + cur.rr);
+#pragma unroll
+      for (int ht = 0; ht < HT; ++ht) {
+        float lt = l_run[ht];
+        lt += shfl_xor(lt, 16);
+        lt += shfl_xor(lt, 32);
+        const int hig = ht * 16 + c16;
+        if (hig < G) {
+          if (whole) {
+            const float inv = (lt > 0.f) ? p.v_scale / lt : 0.f;
+            unsigned short* orow = static_cast<unsigned short*>(p.out) +
+                                   (int64_t)q_row * p.out_row_stride +
+                                   (int64_t)(cur.kvh * G + hig) * D;
+#pragma unroll
+            for (int m = 0; m < NM; ++m) {
+              if constexpr (KVB == 2) {
+                // rows 4*q4 .. 4*q4+3 of tile m: d = 16m + 4*q4 + k, contiguous
+                st8(orow + 16 * m + 4 * q4,
+                    u32x2{pack2<CT>(acc[ht][m][0] * inv, acc[ht][m][1] * inv),
+                          pack2<CT>(acc[ht][m][2] * inv, acc[ht][m][3] * inv)});
+              } else {
+#pragma unroll
+                for (int k = 0; k < 4; ++k) orow[VE * (4 * q4 + k) + m] = M::from_float(acc[ht][m][k] * inv);
+              }
+            }
+          } else {
+            float* wa = p.ws_acc + (slot * G + hig) * D;
+#pragma unroll
+            for (int m = 0; m < NM; ++m) {
+              if constexpr (KVB == 2) {
+                *reinterpret_cast<f32x4*>(wa + 16 * m + 4 * q4) = acc[ht][m];
+              } else {
+#pragma unroll
+                for (int k = 0; k < 4; ++k) wa[VE * (4 * q4 + k) + m] = acc[ht][m][k];
+              }
+            }
+            if (q4 == 0) {
+              float* ml = p.ws_ml + (slot * G + hig) * 2;
+              ml[0] = m_used[ht];
+              ml[1] = lt;
+            }
+          }
+        }
+      }
+      ++seg;
+    }
+    advance(p, cur);
   }
 }
 
-// Merge of the partition partials of one (request, query head): one wave.
-// Lanes take partitions (64 at a time) for the global max and the weighted
-// sum of the row sums; then each lane accumulates its D/64 output columns
-// over the partitions in increasing order with the weights broadcast from
-// the lane that owns them.  Fixed order, no atomics: deterministic.
+// Merge of the partials of one (request, query head) whose K/V head was cut
+// between workers w_a .. w_b: one wave.  Lanes take partials (64 at a time)
+// for the global max and the weighted sum of the row sums; then each lane
+// accumulates its D/64 output columns over the partials in worker order with
+// the weights broadcast from the lane that owns them.  Fixed order, no
+// atomics: deterministic.  A head finished by one worker was written by the
+// main kernel and is skipped here.
 template <int D, typename CT>
 __global__ __launch_bounds__(64) void decode_reduce_kernel(AttnParams p) {
   constexpr int DPL = D / 64;   // output columns per lane
   const int rr = blockIdx.y;
-  const int r = p.req_begin + rr;
   const int qh = blockIdx.x;
   const int lane = threadIdx.x;
-  const int q_row = p.qsl[r];
-  if (p.qsl[r + 1] - q_row != 1) return;
-  int s_eff = min(p.seq_lens[r], p.max_seq_len);
-  s_eff = min(s_eff, p.max_blocks_per_req * kBlock);
-  if (s_eff <= 0) return;
-  const int P = p.part_tokens;
-  int nparts = (s_eff + P - 1) / P;
-  if (nparts <= 1) return;
-  nparts = min(nparts, p.max_parts);
-  const int64_t base = ((int64_t)rr * p.num_q_heads + qh) * p.max_parts;
-  const float* ml = p.ws_ml + base * 2;
-  const float* acc = p.ws_acc + base * D;
+  const int nb = stream_blocks(p, rr, true);
+  if (nb == 0) return;
+  const int G = p.group;
+  const int kvh = qh / G;
+  const int hig = qh % G;
+  const int64_t W = p.num_workers;
+  const int64_t T = p.ws_cum[p.num_reqs];
+  const int64_t a = p.ws_cum[rr] + (int64_t)kvh * nb;
+  const int64_t b = a + nb;
+  const int64_t wa = ((a + 1) * W - 1) / T;   // worker holding unit a
+  const int64_t wb = (b * W - 1) / T;         // worker holding unit b-1
+  if (wa == wb) return;
+  const int cnt = (int)(wb - wa + 1);
+  // partial of the i-th worker of the cut: slot 1 if that worker's range
+  // began before this head (the head is its last segment), else slot 0;
+  // a worker whose range is empty holds none
+  auto part_index = [&](int i, bool& valid) -> int64_t {
+    const int64_t w = wa + i;
+    const int64_t beg = range_begin(w, T, W);
+    valid = beg < range_begin(w + 1, T, W);
+    const int slot = (i == 0 && beg < a) ? 1 : 0;
+    return (w * 2 + slot) * G + hig;
+  };
 
   float mloc = -INFINITY;
-  for (int i = lane; i < nparts; i += 64) mloc = fmaxf(mloc, ml[2 * i]);
+  for (int i = lane; i < cnt; i += 64) {
+    bool ok;
+    const int64_t ix = part_index(i, ok);
+    if (ok) mloc = fmaxf(mloc, p.ws_ml[ix * 2]);
+  }
 #pragma unroll
   for (int off = 32; off >= 1; off >>= 1) mloc = fmaxf(mloc, shfl_xor(mloc, off));
   const float msafe = (mloc == -INFINITY) ? 0.f : mloc;
@@ -380,35 +544,49 @@ __global__ __launch_bounds__(64) void decode_reduce_kernel(AttnParams p) {
   float o[DPL];
 #pragma unroll
   for (int e = 0; e < DPL; ++e) o[e] = 0.f;
-  for (int g = 0; g < nparts; g += 64) {
+  for (int g = 0; g < cnt; g += 64) {
     const int i = g + lane;
-    const float w = (i < nparts) ? fast_exp2(ml[2 * min(i, nparts - 1)] - msafe) : 0.f;
-    const float lw = (i < nparts) ? w * ml[2 * min(i, nparts - 1) + 1] : 0.f;
-    float t = lw;
+    bool ok = false;
+    const int64_t ix = (i < cnt) ? part_index(i, ok) : 0;
+    const float w = ok ? fast_exp2(p.ws_ml[ix * 2] - msafe) : 0.f;
+    float t = ok ? w * p.ws_ml[ix * 2 + 1] : 0.f;
 #pragma unroll
     for (int off = 32; off >= 1; off >>= 1) t += shfl_xor(t, off);
     lsum += t;
-    const int cnt = min(64, nparts - g);
-    for (int j = 0; j < cnt; ++j) {
+    const int m = min(64, cnt - g);
+    for (int j = 0; j < m; ++j) {
       const float wj = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, w), j));
-      const float* a = acc + (int64_t)(g + j) * D + lane;
+      if (wj == 0.f) continue;   // no partial (empty range), or one that underflows
+      bool okj;
+      const float* acc = p.ws_acc + part_index(g + j, okj) * D + lane;
 #pragma unroll
-      for (int e = 0; e < DPL; ++e) o[e] += wj * a[64 * e];
+      for (int e = 0; e < DPL; ++e) o[e] += wj * acc[64 * e];
     }
   }
   const float inv = (lsum > 0.f) ? p.v_scale / lsum : 0.f;
+  const int q_row = load_uniform(p.qsl, p.req_begin + rr);
   unsigned short* orow = static_cast<unsigned short*>(p.out) + (int64_t)q_row * p.out_row_stride +
                          (int64_t)qh * D;
 #pragma unroll
   for (int e = 0; e < DPL; ++e) orow[lane + 64 * e] = Mfma<CT>::from_float(o[e] * inv);
 }
 
+// Ring depth for one instantiation: the configured depth where four waves'
+// rings fit the LDS, else less.
+template <int D, int KVB, int HT>
+constexpr int ring_depth() {
+  constexpr int stage = 2 * Ring<D, KVB>::kBlkBytes + HT * 16 * D * 2;
+  constexpr int fit = kLdsBudget / (kWaves * stage);
+  return kStages < fit ? kStages : fit;
+}
+
 template <int D, typename CT, int KVB, int HT>
 hipError_t launch_typed(const AttnParams& p, hipStream_t stream) {
-  dim3 grid((unsigned)p.max_parts, (unsigned)p.num_kv_heads, (unsigned)p.num_reqs);
-  hipLaunchKernelGGL((decode_kernel<D, CT, KVB, HT>), grid, dim3(kThreads), 0, stream, p);
+  dim3 grid((unsigned)((p.num_workers + kWaves - 1) / kWaves));
+  hipLaunchKernelGGL((decode_kernel<D, CT, KVB, HT, ring_depth<D, KVB, HT>()>), grid,
+                     dim3(kThreads), 0, stream, p);
   hipError_t e = hipGetLastError();
-  if (e != hipSuccess || p.max_parts <= 1) return e;
+  if (e != hipSuccess) return e;
   dim3 rgrid((unsigned)p.num_q_heads, (unsigned)p.num_reqs);
   hipLaunchKernelGGL((decode_reduce_kernel<D, CT>), rgrid, dim3(64), 0, stream, p);
   return hipGetLastError();
@@ -433,7 +611,7 @@ hipError_t launch_dim(const AttnParams& p, int act, int cache, hipStream_t strea
 }  // namespace
 
 hipError_t launch_decode(const AttnParams& p, int act_dtype, int cache_dtype, hipStream_t stream) {
-  if (p.num_reqs == 0 || p.max_parts == 0) return hipSuccess;
+  if (p.num_reqs == 0 || p.num_workers == 0) return hipSuccess;
   if (p.head_dim == 128) return launch_dim<128>(p, act_dtype, cache_dtype, stream);
   if (p.head_dim == 64) return launch_dim<64>(p, act_dtype, cache_dtype, stream);
   return hipErrorInvalidValue;

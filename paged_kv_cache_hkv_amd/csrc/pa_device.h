@@ -132,6 +132,41 @@ __device__ inline int32_t load_uniform(const int32_t* table, int64_t idx) {
   return p[idx];
 }
 
+// Byte offset of an LDS location (the M0 / ds address of a __shared__ pointer).
+__device__ inline unsigned lds_offset(const void* p) {
+  typedef __attribute__((address_space(3))) const void lds_cvoid;
+  return (unsigned)(uintptr_t)(lds_cvoid*)p;
+}
+
+// Asynchronous global -> LDS copy of 16 bytes per lane: lane l's bytes at
+// base + voff (voff per lane, base wave-uniform) land at LDS byte
+// m0 + 16 * l (m0 wave-uniform).  Issued from inline assembly so that the
+// compiler does not track it: it would otherwise make every LDS read wait for
+// every transfer in flight, as it cannot tell ring stages apart.  The caller
+// orders the transfers itself: a transfer into a buffer is issued only after
+// the reads of the buffer's previous contents have returned (the leading
+// lgkmcnt wait covers those still in flight), and the buffer is read only
+// after wait_vmcnt has retired the transfer.  The compiler's own vector loads
+// stay safe: transfers it does not count only make its counted waits stricter.
+__device__ inline void lds_dma16(const void* base, unsigned voff, unsigned m0) {
+  asm volatile(
+      "s_waitcnt lgkmcnt(0)\n\t"
+      "s_mov_b32 m0, %2\n\t"
+      "s_nop 0\n\t"
+      "global_load_lds_dwordx4 %0, %1"
+      :
+      : "v"(voff), "s"(base), "s"(m0)
+      : "memory");
+}
+
+// Wait until at most N vector-memory operations of this wave are in flight
+// (asynchronous LDS copies included); a compiler barrier for memory as well.
+template <int N>
+__device__ inline void wait_vmcnt() {
+  static_assert(N >= 0 && N < 64, "vmcnt is a 6-bit field");
+  asm volatile("s_waitcnt vmcnt(%0)" : : "n"(N) : "memory");
+}
+
 // 16-byte and 8-byte global loads / stores.
 __device__ inline u32x4 ld16(const void* p) { return *reinterpret_cast<const u32x4*>(p); }
 __device__ inline u32x2 ld8(const void* p) { return *reinterpret_cast<const u32x2*>(p); }

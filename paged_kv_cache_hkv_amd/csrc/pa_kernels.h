@@ -57,11 +57,12 @@ struct AttnParams {
   float v_scale;      // 1 unless the cache is fp8
   int32_t max_seq_len;
   int32_t max_query_len;
-  // decode split-K
-  int32_t part_tokens;
-  int32_t max_parts;
-  float* ws_acc;      // [num_reqs, Hq, max_parts, D]
-  float* ws_ml;       // [num_reqs, Hq, max_parts, 2]
+  // decode: the flattened (request, K/V head, block) key stream is cut into
+  // num_workers equal contiguous ranges, one per wave
+  int32_t num_workers;
+  int64_t* ws_cum;    // [num_reqs + 1] first stream block of each request; [num_reqs] = total
+  float* ws_acc;      // [num_workers, 2, G, D] partial weighted sums of split K/V heads
+  float* ws_ml;       // [num_workers, 2, G, 2] their running max (log2 units) and sum
 };
 
 hipError_t launch_metadata(const MetadataParams& p, hipStream_t stream);

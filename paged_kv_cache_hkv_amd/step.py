@@ -19,7 +19,7 @@ _ACT = {torch.float16: B.PA_F16, torch.bfloat16: B.PA_BF16}
 
 
 class PagedAttentionStep:
-    def __init__(self, wl, tensors, decode_partition_tokens=0, qsl_len=None):
+    def __init__(self, wl, tensors, decode_workers=0, qsl_len=None):
         self.wl = wl
         self.t = tensors
         dev = tensors.q.device
@@ -27,7 +27,7 @@ class PagedAttentionStep:
         cache = B.PA_FP8_E4M3 if wl.cache_fp8 else act
         self.desc = B.make_desc(wl.num_q_heads, wl.num_kv_heads, wl.head_dim, wl.block_size,
                                 act, cache, k_scale=tensors.k_scale, v_scale=tensors.v_scale,
-                                decode_partition_tokens=decode_partition_tokens)
+                                decode_workers=decode_workers)
         R = wl.num_reqs
         self.T_pad = tensors.q.shape[0]
         self.qsl = torch.empty(qsl_len or (R + 1), dtype=torch.int32, device=dev)

@@ -69,7 +69,7 @@ def _write(desc, num_tokens=4, key=FAKE, stride=1024, kc=FAKE):
     (dict(act_dtype=B.PA_F16, cache_dtype=B.PA_BF16), B.PA_ERR_UNSUPPORTED),
     (dict(cache_dtype=B.PA_FP8_E4M3, k_scale=0.0), B.PA_ERR_INVALID_ARG),
     (dict(cache_dtype=B.PA_FP8_E4M3, v_scale=float("nan")), B.PA_ERR_INVALID_ARG),
-    (dict(decode_partition_tokens=100), B.PA_ERR_INVALID_ARG),
+    (dict(decode_workers=-1), B.PA_ERR_INVALID_ARG),
     (dict(softmax_scale=float("inf")), B.PA_ERR_INVALID_ARG),
 ])
 def test_desc_rejections(kw, status):
@@ -101,7 +101,12 @@ def test_decode_checks_and_workspace_query():
     d = _desc()
     # size query is host-only
     assert B.pa_decode_workspace_size(d, 256, 8193, 513) > 0
-    assert B.pa_decode_workspace_size(d, 4, 100, 8) == 0      # one partition: no partials
+    # fixed worker count: prefix (int64, R+1) + 2 slots/worker of G*(D+2) floats, 256-aligned parts
+    d8 = _desc(decode_workers=8)
+    rup = lambda x: (x + 255) // 256 * 256
+    G, D = 4, 128
+    assert B.pa_decode_workspace_size(d8, 4, 100, 8) == rup(5 * 8) + rup(16 * G * D * 4) + rup(16 * G * 2 * 4)
+    assert B.pa_decode_workspace_size(d8, 0, 100, 8) == 0
     big = _desc(num_q_heads=64, num_kv_heads=1)
     with pytest.raises(B.PaError) as e:
         B.pa_decode_workspace_size(big, 4, 100, 8)

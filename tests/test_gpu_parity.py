@@ -31,13 +31,13 @@ def _need_gpu():
     B.load()
 
 
-def _run_and_check(wl, requests=None, part=0, poison=True, qsl_len=None, tensors=None):
+def _run_and_check(wl, requests=None, workers=0, poison=True, qsl_len=None, tensors=None):
     _need_gpu()
     t = tensors if tensors is not None else S.make_tensors(wl, DEV, poison=poison)
     if requests is None:
         requests = list(range(wl.num_reqs))
     snap = Snapshot(wl, t, requests)
-    step = PagedAttentionStep(wl, t, decode_partition_tokens=part, qsl_len=qsl_len)
+    step = PagedAttentionStep(wl, t, decode_workers=workers, qsl_len=qsl_len)
     step.run()
     torch.cuda.synchronize()
     qsl, _, _, _ = oracle_metadata(wl, qsl_len)
@@ -152,12 +152,14 @@ def test_small_mixed_parity(hq, hkv, d, act, fp8):
     _run_and_check(wl)
 
 
-@pytest.mark.parametrize("part", [128, 256, 384, 1024])
-def test_long_decode_split_parity(part):
-    """Contexts long enough for many partitions, each split size."""
+@pytest.mark.parametrize("workers", [1, 7, 64, 1000, 5000])
+def test_long_decode_split_parity(workers):
+    """Long contexts cut between decode workers in every way: one worker (no
+    cuts), a few long shares, many short ones, and more workers than units
+    (empty shares)."""
     wl = S.random_batch(77, [2047, 2048, 2049, 4000, 5000], [(3000, 5)], hq=32, hkv=4, d=128,
                         act=torch.bfloat16)
-    _run_and_check(wl, part=part)
+    _run_and_check(wl, workers=workers)
 
 
 @pytest.mark.parametrize("name,nsample", [("decode_mha", 8), ("decode_gqa", 8),

@@ -5,12 +5,12 @@ At long contexts a max-abs tolerance cannot see one missing 16-token block
 invariants directly:
 
 * spike: one key per request aligned with its query and a marker value: the
-  output must equal the marker, wherever the key sits (block and partition
-  boundaries, the token written this step);
+  output must equal the marker, wherever the key sits (block boundaries,
+  the cuts between decode workers, the token written this step);
 * block permutation: the same logical K/V under other physical block ids give
   bit-identical outputs;
 * determinism: two runs give bit-identical outputs;
-* split invariance: different partition sizes agree to float32 rounding;
+* split invariance: different decode worker counts agree to float32 rounding;
 * aliasing: requests that share prefix blocks read them correctly.
 """
 
@@ -141,7 +141,7 @@ def test_determinism_two_runs():
     wl = S.random_batch(9, [4000, 8000, 12], [(1000, 300)], hq=32, hkv=8, d=128,
                         act=torch.bfloat16)
     t = S.make_tensors(wl, DEV)
-    st = PagedAttentionStep(wl, t, decode_partition_tokens=256)
+    st = PagedAttentionStep(wl, t, decode_workers=256)
     st.run()
     torch.cuda.synchronize()
     first = st.out.clone()
@@ -156,8 +156,8 @@ def test_split_invariance():
     wl = S.random_batch(10, [6000, 9000, 300], [], hq=32, hkv=4, d=128, act=torch.bfloat16)
     t = S.make_tensors(wl, DEV)
     outs = []
-    for part in (128, 256, 896, 8192):
-        st = PagedAttentionStep(wl, t, decode_partition_tokens=part)
+    for workers in (3, 77, 0, 1):
+        st = PagedAttentionStep(wl, t, decode_workers=workers)
         if not outs:
             st.run()                 # write this step's tokens once
         else:
