@@ -37,6 +37,14 @@ COMMON_FLAGS = [
 ]
 
 
+# Per-source additions.  pa_decode.hip: MFMA accumulators in ordinary VGPRs;
+# with them in AGPRs the compiler copies every accumulator through VGPRs on
+# each block (a segment's reset and the rescale touch them with VALU ops).
+EXTRA_FLAGS = {
+    "pa_decode.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form=1"],
+}
+
+
 def hipcc():
     exe = shutil.which("hipcc") or "/opt/rocm/bin/hipcc"
     return exe
@@ -51,7 +59,8 @@ def build(verbose=False):
         obj = os.path.join(OBJDIR, os.path.splitext(src)[0] + ".o")
         objs.append(obj)
         lang = ["-x", "hip"] if src.endswith(".hip") else []
-        cmd = [hipcc()] + COMMON_FLAGS + lang + ["-c", os.path.join(CSRC, src), "-o", obj]
+        cmd = ([hipcc()] + COMMON_FLAGS + EXTRA_FLAGS.get(src, []) + lang +
+               ["-c", os.path.join(CSRC, src), "-o", obj])
         if verbose:
             print(" ".join(cmd), flush=True)
         procs.append((src, subprocess.Popen(cmd, stdout=subprocess.PIPE, stderr=subprocess.STDOUT)))

@@ -279,8 +279,8 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(AttnParams p) {
     const unsigned char* vb = static_cast<const unsigned char*>(p.value_cache) + boff;
 #pragma unroll
     for (int i = 0; i < R::kIPT; ++i) {
-      lds_dma16(kb, (unsigned)koff[i], dst + 1024 * i);
-      lds_dma16(vb, (unsigned)voff[i], dst + R::kBlkBytes + 1024 * i);
+      lds_dma16<true>(kb, (unsigned)koff[i], dst + 1024 * i);
+      lds_dma16<true>(vb, (unsigned)voff[i], dst + R::kBlkBytes + 1024 * i);
     }
     advance(p, ic);
   };
@@ -544,23 +544,36 @@ __global__ __launch_bounds__(64) void decode_reduce_kernel(AttnParams p) {
   float o[DPL];
 #pragma unroll
   for (int e = 0; e < DPL; ++e) o[e] = 0.f;
+  bool ok0;
+  const int64_t ix0 = part_index(0, ok0);   // worker w_a always holds a partial
   for (int g = 0; g < cnt; g += 64) {
     const int i = g + lane;
     bool ok = false;
-    const int64_t ix = (i < cnt) ? part_index(i, ok) : 0;
+    int64_t ix = (i < cnt) ? part_index(i, ok) : 0;
     const float w = ok ? fast_exp2(p.ws_ml[ix * 2] - msafe) : 0.f;
     float t = ok ? w * p.ws_ml[ix * 2 + 1] : 0.f;
 #pragma unroll
     for (int off = 32; off >= 1; off >>= 1) t += shfl_xor(t, off);
     lsum += t;
+    // a missing partial reads an existing one with weight 0 (its memory may
+    // hold anything, and 0 * NaN is NaN); batches of 8 keep loads in flight
+    ix = ok ? ix : ix0;
     const int m = min(64, cnt - g);
-    for (int j = 0; j < m; ++j) {
-      const float wj = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, w), j));
-      if (wj == 0.f) continue;   // no partial (empty range), or one that underflows
-      bool okj;
-      const float* acc = p.ws_acc + part_index(g + j, okj) * D + lane;
+    for (int j0 = 0; j0 < m; j0 += 8) {
+      float wj[8], v[8][DPL];
 #pragma unroll
-      for (int e = 0; e < DPL; ++e) o[e] += wj * acc[64 * e];
+      for (int u = 0; u < 8; ++u) {
+        const int j = min(j0 + u, m - 1);
+        wj[u] = (j0 + u < m) ? __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, w), j))
+                             : 0.f;
+        const float* a = p.ws_acc + readlane64(ix, j) * D + lane;
+#pragma unroll
+        for (int e = 0; e < DPL; ++e) v[u][e] = a[64 * e];
+      }
+#pragma unroll
+      for (int u = 0; u < 8; ++u)
+#pragma unroll
+        for (int e = 0; e < DPL; ++e) o[e] += wj[u] * v[u][e];
     }
   }
   const float inv = (lsum > 0.f) ? p.v_scale / lsum : 0.f;

@@ -148,15 +148,29 @@ __device__ inline unsigned lds_offset(const void* p) {
 // lgkmcnt wait covers those still in flight), and the buffer is read only
 // after wait_vmcnt has retired the transfer.  The compiler's own vector loads
 // stay safe: transfers it does not count only make its counted waits stricter.
+// NT: non-temporal (data read once, e.g. a K/V stream): measurably higher
+// HBM throughput for streams that are not re-read.
+template <bool NT = false>
 __device__ inline void lds_dma16(const void* base, unsigned voff, unsigned m0) {
-  asm volatile(
-      "s_waitcnt lgkmcnt(0)\n\t"
-      "s_mov_b32 m0, %2\n\t"
-      "s_nop 0\n\t"
-      "global_load_lds_dwordx4 %0, %1"
-      :
-      : "v"(voff), "s"(base), "s"(m0)
-      : "memory");
+  if constexpr (NT) {
+    asm volatile(
+        "s_waitcnt lgkmcnt(0)\n\t"
+        "s_mov_b32 m0, %2\n\t"
+        "s_nop 0\n\t"
+        "global_load_lds_dwordx4 %0, %1 nt"
+        :
+        : "v"(voff), "s"(base), "s"(m0)
+        : "memory");
+  } else {
+    asm volatile(
+        "s_waitcnt lgkmcnt(0)\n\t"
+        "s_mov_b32 m0, %2\n\t"
+        "s_nop 0\n\t"
+        "global_load_lds_dwordx4 %0, %1"
+        :
+        : "v"(voff), "s"(base), "s"(m0)
+        : "memory");
+  }
 }
 
 // Wait until at most N vector-memory operations of this wave are in flight
