@@ -386,11 +386,15 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(AttnParams p) {
       float x[4];
 #pragma unroll
       for (int k = 0; k < 4; ++k) x[k] = sc[ht][k] * c2;
-      float mx = fmaxf(fmaxf(x[0], x[1]), fmaxf(x[2], x[3]));
-      mx = fmaxf(mx, shfl_xor(mx, 16));
-      mx = fmaxf(mx, shfl_xor(mx, 32));
-      const bool grow = mx > m_used[ht] + kRescaleLog2;
-      if (__builtin_amdgcn_ballot_w64(grow)) {
+      // A head's reference max only moves when one of its scores exceeds it
+      // by 2^8; each lane tests its own 4 scores, and only when some lane
+      // does (rare after a segment's first block) is the head max formed
+      // across the head's 4 lanes and the accumulator rescaled.
+      const float lm = fmaxf(fmaxf(x[0], x[1]), fmaxf(x[2], x[3]));
+      if (__builtin_amdgcn_ballot_w64(lm > m_used[ht] + kRescaleLog2)) {
+        float mx = fmaxf(lm, shfl_xor(lm, 16));
+        mx = fmaxf(mx, shfl_xor(mx, 32));
+        const bool grow = mx > m_used[ht] + kRescaleLog2;
         const float m_new = grow ? mx : m_used[ht];
         const float alpha = grow ? fast_exp2(m_used[ht] - m_new) : 1.f;
         l_run[ht] *= alpha;
