@@ -47,18 +47,20 @@ pa_status check_desc(const pa_attn_desc* d) {
 }
 
 // Decode workers: waves that each stream one contiguous share of the
-// (request, K/V head, block) stream.  Four per compute unit of the current
-// device (one workgroup of four independent waves per CU, all resident for
-// the whole launch) unless the descriptor fixes the count.
+// (request, K/V head, block) stream.  decode_waves_per_cu() per compute unit
+// of the current device (one workgroup of independent waves per CU, all
+// resident for the whole launch) unless the descriptor fixes the count.
 int decode_workers(const pa_attn_desc* d) {
   if (d->decode_workers > 0) return d->decode_workers;
+  const int per_cu = pa::decode_waves_per_cu(d->num_q_heads / d->num_kv_heads,
+                                             d->cache_dtype == PA_FP8_E4M3 ? pa::kFP8 : pa::kF16);
   int dev = 0, cus = 0;
   if (hipGetDevice(&dev) != hipSuccess ||
       hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
       cus <= 0) {
     cus = 256;
   }
-  return 4 * cus;
+  return per_cu * cus;
 }
 
 struct DecodePlan {

@@ -26,10 +26,11 @@
 // or slot 1 (its last), and the reduce kernel merges the partials of each cut
 // head in worker order (deterministic, no atomics).
 //
-// Streaming.  Each wave owns a ring of S LDS stages; a stage holds one block
-// (K and V rows of one head) plus, for the first block of a segment, the
-// segment's G query rows.  Asynchronous global -> LDS copies are issued S-1
-// blocks ahead, so the bytes in flight cost no registers.  A copy
+// Streaming.  Each wave owns a ring of S LDS stages, one block (K and V rows
+// of one head) each, and a query area for one segment's G query rows, copied
+// when the segment's first block is issued (the issue side holds back while a
+// copied query is still unread).  Asynchronous global -> LDS copies are
+// issued S-1 blocks ahead, so the bytes in flight cost no registers.  A copy
 // instruction moves 1 KB: whole 16-byte chunks of 16/8/4 consecutive token
 // rows, each row's chunks scattered by an XOR of the token so the MFMA
 // operand reads below hit distinct LDS banks.  Per block a wave:
@@ -58,8 +59,6 @@ namespace pa {
 
 namespace {
 
-constexpr int kWaves = 4;                 // waves per workgroup (independent workers)
-constexpr int kThreads = 64 * kWaves;
 constexpr int kBlock = 16;                // tokens per cache block
 constexpr float kRescaleLog2 = 8.f;       // lazy rescale threshold (log2 units)
 constexpr int kLdsBudget = 160 * 1024;    // LDS of one compute unit
@@ -161,10 +160,22 @@ __device__ inline int64_t wave_scan(int64_t v) {
 __device__ inline int64_t range_begin(int64_t w, int64_t T, int64_t W) { return w * T / W; }
 
 // Position in the stream: request (index within the call), K/V head, block
-// of that head, and the request's block count.
+// of that head; and the request's block count, key count and query row.
 struct Cursor {
   int rr, kvh, b, nb;
+  int s_eff, q_row;
 };
+
+// Fill the request fields of c for request c.rr (wave-uniform loads).
+__device__ inline void load_request(const AttnParams& p, Cursor& c) {
+  const int r = p.req_begin + c.rr;
+  const int q0 = load_uniform(p.qsl, r);
+  const int q1 = load_uniform(p.qsl, r + 1);
+  const int s = min(min(load_uniform(p.seq_lens, r), p.max_seq_len), p.max_blocks_per_req * kBlock);
+  c.q_row = q0;
+  c.s_eff = s;
+  c.nb = (q1 - q0 == 1 && s > 0) ? (s + kBlock - 1) / kBlock : 0;
+}
 
 // Advance by one unit (wave-uniform); skips requests that stream nothing.
 __device__ inline void advance(const AttnParams& p, Cursor& c) {
@@ -173,31 +184,35 @@ __device__ inline void advance(const AttnParams& p, Cursor& c) {
   if (++c.kvh < p.num_kv_heads) return;
   c.kvh = 0;
   do {
-    ++c.rr;
-    c.nb = c.rr < p.num_reqs ? stream_blocks(p, c.rr, true) : 1;
+    if (++c.rr >= p.num_reqs) {   // past the stream: never used
+      c.nb = 1;
+      return;
+    }
+    load_request(p, c);
   } while (c.nb == 0);
 }
 
-template <int D, typename CT, int KVB, int HT, int S>
-__global__ __launch_bounds__(kThreads) void decode_kernel(AttnParams p) {
+template <int D, typename CT, int KVB, int HT, int S, int WV>
+__global__ __launch_bounds__(64 * WV) void decode_kernel(AttnParams p) {
   using M = Mfma<CT>;
   using vec8 = typename M::vec8;
   using R = Ring<D, KVB>;
   constexpr int KS = D / 32;               // QK MFMA steps (32 d each)
   constexpr int NM = D / 16;               // PV MFMAs per block (16 rows of O^T each)
   constexpr int VE = D / 16;               // fp8 path: V bytes per lane per token
+  constexpr int kStage = 2 * R::kBlkBytes; // K | V of one block
   constexpr int kQCap = HT * 16 * D * 2;   // query rows of one segment (<= 16*HT heads)
-  constexpr int kStage = 2 * R::kBlkBytes + kQCap;   // K | V | Q
+  constexpr int kWaveBytes = S * kStage + kQCap;
   static_assert(S >= 2 && S <= 4, "ring depth");
-  static_assert(kWaves * S * kStage <= kLdsBudget, "ring exceeds LDS");
-  __shared__ __attribute__((aligned(1024))) unsigned char lds[kWaves * S * kStage];
+  static_assert(WV * kWaveBytes <= kLdsBudget, "rings exceed LDS");
+  __shared__ __attribute__((aligned(1024))) unsigned char lds[WV * kWaveBytes];
 
   const int lane = threadIdx.x & 63;
   const int wave = wave_uniform(threadIdx.x >> 6);
   const int q4 = lane >> 4;
   const int c16 = lane & 15;
   const int W = p.num_workers;
-  const int worker = blockIdx.x * kWaves + wave;
+  const int worker = blockIdx.x * WV + wave;
   if (worker >= W) return;
   const int Rn = p.num_reqs;
   const int G = p.group;
@@ -211,7 +226,7 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(AttnParams p) {
   }
   const int64_t g0 = range_begin(worker, T, W);
   const int64_t n = range_begin(worker + 1, T, W) - g0;
-  Cursor cur{0, 0, 0, 0};
+  Cursor cur{0, 0, 0, 0, 0, 0};
   {
     // worker 0 also publishes the exclusive prefix for the reduce kernel
     int64_t run = 0;
@@ -226,7 +241,7 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(AttnParams p) {
         const int l = __builtin_ctzll(hit);
         cur.rr = c + l;
         const int64_t within = g0 - readlane64(excl, l);
-        cur.nb = stream_blocks(p, cur.rr, true);
+        load_request(p, cur);
         cur.kvh = (int)(within / cur.nb);
         cur.b = (int)(within % cur.nb);
         found = true;
@@ -241,11 +256,6 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(AttnParams p) {
   const int64_t tok_stride = (int64_t)Hkv * D * KVB;     // bytes between slots
   const int64_t blk_stride = tok_stride * kBlock;        // bytes between blocks
   const int64_t num_blocks = p.num_blocks;
-  auto block_id = [&](const Cursor& c) {   // physical block, or -1 when absent
-    const int id = load_uniform(p.block_tables,
-                                (int64_t)(p.req_begin + c.rr) * p.max_blocks_per_req + c.b);
-    return (id >= 0 && (int64_t)id < num_blocks) ? id : -1;
-  };
 
   // per-lane source offsets of the copy instructions of one block
   int koff[R::kIPT], voff[R::kIPT];
@@ -257,23 +267,34 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(AttnParams p) {
     koff[j] = (int)(t * tok_stride) + 16 * (pos ^ R::swk(t));
     voff[j] = (int)(t * tok_stride) + 16 * (pos ^ R::swv(t));
   }
-  unsigned char* ring = lds + wave * S * kStage;
+  unsigned char* ring = lds + wave * kWaveBytes;
+  const unsigned char* qarea = ring + S * kStage;
   const unsigned ring_m0 = lds_offset(ring);
+  const unsigned q_m0 = ring_m0 + S * kStage;
   const int qbytes = G * D * 2;
 
-  // ---- issue side: copies of unit j into stage st (a segment's first unit
-  // carries the segment's query rows, copied first) ----
+  // ---- issue side.  Unit j goes to stage j % S; the first unit of a
+  // segment first copies the segment's query rows into the wave's query
+  // area.  That area holds one segment's rows, so the issue side waits
+  // (issues nothing) while rows it copied are not yet read. ----
   Cursor ic = cur;
-  auto issue = [&](int64_t j, int st) {
+  int64_t jn = 0;            // units issued
+  bool q_pending = false;    // query rows copied but not yet read
+  unsigned okbits = 0;       // bit st: the unit in stage st has its block
+  auto can_issue = [&](int64_t lim) { return jn < n && jn < lim && !(q_pending && ic.b == 0); };
+  auto issue_one = [&]() {
+    const int st = (int)(jn % S);
     const unsigned dst = ring_m0 + st * kStage;
-    if (ic.b == 0 || j == 0) {
+    if (ic.b == 0 || jn == 0) {
       const unsigned char* qb = static_cast<const unsigned char*>(p.q) +
-                                ((int64_t)load_uniform(p.qsl, p.req_begin + ic.rr) * p.q_row_stride +
-                                 (int64_t)ic.kvh * G * D) * 2;
+                                ((int64_t)ic.q_row * p.q_row_stride + (int64_t)ic.kvh * G * D) * 2;
       for (int k = 0; k < qbytes; k += 1024)
-        if (k + 16 * lane < qbytes) lds_dma16(qb, (unsigned)(k + 16 * lane), dst + 2 * R::kBlkBytes + k);
+        if (k + 16 * lane < qbytes) lds_dma16(qb, (unsigned)(k + 16 * lane), q_m0 + k);
+      q_pending = true;
     }
-    const int id = block_id(ic);
+    int id = load_uniform(p.block_tables, (int64_t)(p.req_begin + ic.rr) * p.max_blocks_per_req + ic.b);
+    id = (id >= 0 && (int64_t)id < num_blocks) ? id : -1;
+    okbits = (okbits & ~(1u << st)) | ((id >= 0 ? 1u : 0u) << st);
     const int64_t boff = (int64_t)(id < 0 ? 0 : id) * blk_stride + (int64_t)ic.kvh * D * KVB;
     const unsigned char* kb = static_cast<const unsigned char*>(p.key_cache) + boff;
     const unsigned char* vb = static_cast<const unsigned char*>(p.value_cache) + boff;
@@ -283,6 +304,7 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(AttnParams p) {
       lds_dma16<true>(vb, (unsigned)voff[i], dst + R::kBlkBytes + 1024 * i);
     }
     advance(p, ic);
+    ++jn;
   };
 
   // ---- per-lane LDS read offsets within a stage ----
@@ -308,8 +330,7 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(AttnParams p) {
     for (int k = 0; k < 4; ++k) vread[k] = R::kBlkBytes + row_token(4 * q4 + k) * R::kRowBytes + VE * c16;
   }
 
-  for (int j = 0; j < S - 1; ++j)
-    if (j < n) issue(j, j);
+  while (can_issue(S - 1)) issue_one();
 
   const float c2 = p.scale_log2;
   vec8 qop[HT][KS];
@@ -319,9 +340,10 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(AttnParams p) {
   int seg_b0 = 0;       // first block of the current segment
 
   for (int64_t i = 0; i < n; ++i) {
-    if (i + S - 1 < n) issue(i + S - 1, (int)((i + S - 1) % S));
-    wait_blocks<R::kIPB>((int)min((int64_t)(S - 1), n - 1 - i));
-    const unsigned char* st = ring + (int)(i % S) * kStage;
+    while (can_issue(i + S)) issue_one();
+    wait_blocks<R::kIPB>((int)(jn - 1 - i));    // unit i landed (jn > i always holds here)
+    const int st_i = (int)(i % S);
+    const unsigned char* st = ring + st_i * kStage;
 
     // ---- segment start: query operands, fresh softmax state ----
     if (cur.b == 0 || i == 0) {
@@ -332,7 +354,7 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(AttnParams p) {
 #pragma unroll
         for (int s = 0; s < KS; ++s) {
           const int d0 = (KVB == 2) ? (32 * s + 8 * q4) : (64 * (s / 2) + 16 * q4 + 8 * (s % 2));
-          const u32x4 v = *reinterpret_cast<const u32x4*>(st + 2 * R::kBlkBytes + (hig * D + d0) * 2);
+          const u32x4 v = *reinterpret_cast<const u32x4*>(qarea + (hig * D + d0) * 2);
           qop[ht][s] = __builtin_bit_cast(vec8, hig < G ? v : u32x4{0u, 0u, 0u, 0u});
         }
         m_used[ht] = -INFINITY;
@@ -340,6 +362,7 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(AttnParams p) {
 #pragma unroll
         for (int m = 0; m < NM; ++m) acc[ht][m] = f32x4{0.f, 0.f, 0.f, 0.f};
       }
+      q_pending = false;   // the next copy waits for these reads (lgkmcnt) before it lands
     }
 
     // ---- S^T = K . Q^T ----
@@ -362,15 +385,13 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(AttnParams p) {
     }
 
     // ---- masks: tokens past the sequence, absent blocks (selects only) ----
-    const int s_eff = min(min(load_uniform(p.seq_lens, p.req_begin + cur.rr), p.max_seq_len),
-                          p.max_blocks_per_req * kBlock);
     const int tok0 = cur.b * kBlock;
-    const bool blk_ok = block_id(cur) >= 0;
+    const bool blk_ok = (okbits >> st_i) & 1u;
     unsigned vm0 = 0xFFFFFFFFu, vm1 = 0xFFFFFFFFu;
-    if (!blk_ok || tok0 + kBlock > s_eff) {
+    if (!blk_ok || tok0 + kBlock > cur.s_eff) {
       bool bad[4];
 #pragma unroll
-      for (int k = 0; k < 4; ++k) bad[k] = !blk_ok || tok0 + row_token(4 * q4 + k) >= s_eff;
+      for (int k = 0; k < 4; ++k) bad[k] = !blk_ok || tok0 + row_token(4 * q4 + k) >= cur.s_eff;
       vm0 = (bad[0] ? 0u : 0x0000FFFFu) | (bad[1] ? 0u : 0xFFFF0000u);
       vm1 = (bad[2] ? 0u : 0x0000FFFFu) | (bad[3] ? 0u : 0xFFFF0000u);
 #pragma unroll
@@ -447,7 +468,6 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(AttnParams p) {
     if (cur.b == cur.nb - 1 || i == n - 1) {
       const bool whole = seg_b0 == 0 && cur.b == cur.nb - 1;
       const int64_t slot = (int64_t)worker * 2 + (seg == 0 ? 0 : 1);
-      const int q_row = load_uniform(p.qsl, p.req_begin + cur.rr);
 #pragma unroll
       for (int ht = 0; ht < HT; ++ht) {
         float lt = l_run[ht];
@@ -458,7 +478,7 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(AttnParams p) {
           if (whole) {
             const float inv = (lt > 0.f) ? p.v_scale / lt : 0.f;
             unsigned short* orow = static_cast<unsigned short*>(p.out) +
-                                   (int64_t)q_row * p.out_row_stride +
+                                   (int64_t)cur.q_row * p.out_row_stride +
                                    (int64_t)(cur.kvh * G + hig) * D;
 #pragma unroll
             for (int m = 0; m < NM; ++m) {
@@ -588,20 +608,28 @@ __global__ __launch_bounds__(64) void decode_reduce_kernel(AttnParams p) {
   for (int e = 0; e < DPL; ++e) orow[lane + 64 * e] = Mfma<CT>::from_float(o[e] * inv);
 }
 
-// Ring depth for one instantiation: the configured depth where four waves'
-// rings fit the LDS, else less.
+// Waves per workgroup and ring depth for one instantiation: two column tiles
+// of fp8 (G > 16) make the per-block math long for a 4 KB block, so eight
+// waves per compute unit share the work; otherwise four.  The ring is as deep
+// as the configured depth where it fits the LDS.
+template <int D, int KVB, int HT>
+constexpr int waves_per_wg() { return decode_waves_per_cu(HT == 2 ? 32 : 16, KVB == 1 ? kFP8 : kF16); }
+
 template <int D, int KVB, int HT>
 constexpr int ring_depth() {
-  constexpr int stage = 2 * Ring<D, KVB>::kBlkBytes + HT * 16 * D * 2;
-  constexpr int fit = kLdsBudget / (kWaves * stage);
+  constexpr int wv = waves_per_wg<D, KVB, HT>();
+  constexpr int stage = 2 * Ring<D, KVB>::kBlkBytes;
+  constexpr int qcap = HT * 16 * D * 2;
+  constexpr int fit = (kLdsBudget / wv - qcap) / stage;
   return kStages < fit ? kStages : fit;
 }
 
 template <int D, typename CT, int KVB, int HT>
 hipError_t launch_typed(const AttnParams& p, hipStream_t stream) {
-  dim3 grid((unsigned)((p.num_workers + kWaves - 1) / kWaves));
-  hipLaunchKernelGGL((decode_kernel<D, CT, KVB, HT, ring_depth<D, KVB, HT>()>), grid,
-                     dim3(kThreads), 0, stream, p);
+  constexpr int WV = waves_per_wg<D, KVB, HT>();
+  dim3 grid((unsigned)((p.num_workers + WV - 1) / WV));
+  hipLaunchKernelGGL((decode_kernel<D, CT, KVB, HT, ring_depth<D, KVB, HT>(), WV>), grid,
+                     dim3(64 * WV), 0, stream, p);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   dim3 rgrid((unsigned)p.num_q_heads, (unsigned)p.num_reqs);

@@ -65,6 +65,13 @@ struct AttnParams {
   float* ws_ml;       // [num_workers, 2, G, 2] their running max (log2 units) and sum
 };
 
+// Decode waves per workgroup (= per compute unit: one resident workgroup of
+// independent waves).  fp8 with G > 16 (two MFMA column tiles, 4 KB blocks)
+// has the longest math per block and uses eight; everything else four.
+constexpr int decode_waves_per_cu(int group, int cache_dtype) {
+  return (group > 16 && cache_dtype == kFP8) ? 8 : 4;
+}
+
 hipError_t launch_metadata(const MetadataParams& p, hipStream_t stream);
 hipError_t launch_cache_write(const CacheWriteParams& p, int act_dtype, int cache_dtype,
                               hipStream_t stream);
