@@ -19,19 +19,24 @@ Sources (web pages; every function cites the part it follows):
 * "vLLM 推理全流程深度解析" (vLLM inference deep dive): the BlockManager block
   allocation example, the ``prepare_input_tensors`` slot-mapping example, the
   ``reshape_and_cache`` kernel description, the PagedAttention decode kernel
-  signature and the KV-cache quantization remark.
+  signature, the KV-cache quantization remark and the ``LlamaAttention``
+  listing (RoPE on Q and K before the cache write).
+* "Tour: One forward pass", stop 9 (the rotary embedding: a lookup in
+  ``cos_sin_cache`` by position, then the rotation of each head).
 
 Arithmetic is float64 unless the format itself fixes the precision (the fp8
-encoder's single float32 multiply).  Modules:
+encoder's single float32 multiply) or the reading of the pages fixes it (the
+rotary embedding's float32 steps, pinned to the float64 rotation).  Modules:
 
 * ``codecs``     fp16 / bf16 / OCP e4m3fn bit decoders and the e4m3fn encoder.
 * ``metadata``   query_start_loc, seq_lens, positions, slot_mapping.
 * ``cache``      the slot_mapping scatter into ``[num_blocks, block_size, Hkv, D]``.
 * ``attention``  gather through the block table + dense causal softmax(QK^T*scale)V.
+* ``rope``       rotary position embedding of Q and K fused with the cache write.
 
 Every function here is pinned by ``tests/test_oracle_*.py`` against values the
 pages print, closed forms, library routines or brute force; none is
 "parity unpinned".
 """
 
-from . import codecs, metadata, cache, attention  # noqa: F401
+from . import codecs, metadata, cache, attention, rope  # noqa: F401

@@ -102,6 +102,54 @@ def e4m3fn_encode(x_f32, inv_scale_f32):
     return codes.astype(np.uint8)
 
 
+def f32_to_bf16_bits(x_f32):
+    """float32 values -> bfloat16 bit patterns, round to nearest, ties to even.
+
+    Written out as the definition: the two bfloat16 neighbours of x are the
+    float32 bit patterns with the low 16 bits cleared (toward zero) and that
+    plus one bfloat16 ulp (away from zero); pick the nearer, and on a tie the
+    one whose last kept bit is 0.  The neighbour past the largest finite value
+    is infinity, which for rounding counts as 2**128 (IEEE overflow rule).
+    NaN becomes a quiet NaN of the same sign; infinities stay.
+    """
+    x = np.asarray(x_f32, dtype=np.float32)
+    bits = x.view(np.uint32).astype(np.uint64)
+    sign = bits & 0x80000000
+    mag = bits & 0x7FFFFFFF
+    lo = mag & 0x7FFF0000                     # toward zero
+    hi = lo + 0x10000                         # away from zero (0x7F800000 = inf)
+
+    def value(b):
+        # magnitude of a float32 bit pattern as float64; 0x7F800000 counts as 2**128
+        f = b.astype(np.uint32).view(np.float32).astype(np.float64)
+        return np.where(b == 0x7F800000, 2.0 ** 128, f)
+
+    with np.errstate(invalid="ignore"):        # NaN inputs are handled below
+        v = mag.astype(np.uint32).view(np.float32).astype(np.float64)
+        d_lo = v - value(lo)
+        d_hi = value(hi) - v
+    lo_even = ((lo >> 16) & 1) == 0
+    pick_hi = (d_hi < d_lo) | ((d_hi == d_lo) & ~lo_even)
+    out = np.where(pick_hi, hi, lo)
+    is_nan = mag > 0x7F800000
+    is_inf = mag == 0x7F800000
+    out = np.where(is_inf, 0x7F800000, out)
+    out = np.where(is_nan, 0x7FC00000, out)
+    return ((out | sign) >> 16).astype(np.uint16)
+
+
+def f32_to_act_bits(x_f32, dtype):
+    """float32 values -> stored bits of the activation dtype ('f16' or 'bf16'),
+    round to nearest even (fp16: IEEE binary16 conversion)."""
+    x = np.asarray(x_f32, dtype=np.float32)
+    if dtype == "f16":
+        with np.errstate(over="ignore"):
+            return x.astype(np.float16).view(np.uint16)
+    if dtype == "bf16":
+        return f32_to_bf16_bits(x)
+    raise ValueError(dtype)
+
+
 def decode(bits, dtype):
     """Decode stored bits of ``dtype`` ('f16', 'bf16', 'fp8_e4m3') to float64."""
     if dtype == "f16":
