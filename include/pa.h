@@ -9,6 +9,8 @@
  *   once per step   pa_metadata_build  -> query_start_loc, seq_lens,
  *                                          positions, slot_mapping
  *   per layer       pa_cache_write     -> scatter new K/V into the paged cache
+ *                   (or pa_rope_cache_write: rotate Q and K by position, then
+ *                    the same scatter, in one launch)
  *                   pa_decode          -> attention of 1-token requests
  *                   pa_prefill_varlen  -> causal attention of (chunked) prefills
  *
@@ -157,6 +159,43 @@ pa_status pa_cache_write(const pa_attn_desc* desc, int64_t num_tokens,
                          const int64_t* slot_mapping,
                          void* key_cache, void* value_cache, int64_t num_blocks,
                          void* stream);
+
+/*
+ * pa_rope_cache_write -- rotary position embedding of Q and K fused with the
+ * cache write ("Tour: One forward pass", stop 9: the rotary embedding rotates q
+ * and k by the positions of stop 3, a lookup in cos_sin_cache by position and
+ * then the rotation of each head; followed by stop 10's cache write).  One
+ * kernel launch.
+ *
+ * positions: int64 [num_tokens] (as built by pa_metadata_build).
+ * cos_sin_cache: float32 [max_position, rotary_dim], 16-byte aligned: row p
+ *   holds rotary_dim/2 cosines c_j then rotary_dim/2 sines s_j for position p
+ *   (the caller builds it, e.g. angle p * base^(-2j/rotary_dim)).
+ * rotary_dim: rotated leading dimensions of every head; a multiple of 16,
+ *   16 .. head_dim.  Dimensions from rotary_dim on are left unchanged.
+ * is_neox: 1 rotates the pairs (j, j + rotary_dim/2) (half-split layout),
+ *   0 the pairs (2j, 2j+1) (interleaved).
+ * query: act_dtype [num_tokens, num_q_heads, head_dim], row stride in
+ *   elements; rotated in place.
+ * key, value: act_dtype [num_tokens, num_kv_heads, head_dim] (not modified).
+ * For token t at position p in [0, max_position), each pair (a, b) of every
+ * query and key head becomes a*c - b*s, b*c + a*s, computed in float32 with
+ * every product and sum rounded once (no fused multiply-add), rounded to
+ * act_dtype (nearest even).  The rotated key and the value then go to the
+ * slot exactly as pa_cache_write would store them (fp8 caches: the rotated
+ * key rounded to act_dtype is encoded).  A token with a slot that is negative
+ * or past the pool has its query rotated and writes nothing; a token whose
+ * position is outside [0, max_position) is left entirely alone.
+ */
+pa_status pa_rope_cache_write(const pa_attn_desc* desc, int64_t num_tokens,
+                              const int64_t* positions, const float* cos_sin_cache,
+                              int64_t max_position, int32_t rotary_dim, int32_t is_neox,
+                              void* query, int64_t query_row_stride,
+                              const void* key, int64_t key_row_stride,
+                              const void* value, int64_t value_row_stride,
+                              const int64_t* slot_mapping,
+                              void* key_cache, void* value_cache, int64_t num_blocks,
+                              void* stream);
 
 /*
  * pa_decode -- attention of decode requests through their block tables

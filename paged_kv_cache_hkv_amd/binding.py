@@ -65,6 +65,8 @@ _SIGS = {
     "pa_status_string": [ctypes.c_int],
     "pa_metadata_build": [_I32, _I32, _I32, _I32, _I32, _P, _P, _P, _P, _P, _P, _P, _P],
     "pa_cache_write": [ctypes.POINTER(AttnDesc), _I64, _P, _I64, _P, _I64, _P, _P, _P, _I64, _P],
+    "pa_rope_cache_write": [ctypes.POINTER(AttnDesc), _I64, _P, _P, _I64, _I32, _I32, _P, _I64, _P,
+                            _I64, _P, _I64, _P, _P, _P, _I64, _P],
     "pa_decode": [ctypes.POINTER(AttnDesc), _I32, _I32, _P, _I64, _P, _P, _P, _I32, _P, _P, _I64,
                   _I32, _P, _SZ, _P, _I64, _P],
     "pa_decode_workspace_size": [ctypes.POINTER(AttnDesc), _I32, _I32, _I32, ctypes.POINTER(_SZ)],
@@ -135,6 +137,19 @@ def pa_cache_write(desc, key, value, slot_mapping, key_cache, value_cache, num_t
         ctypes.byref(desc), num_tokens, _ptr(key), _row_stride(key), _ptr(value),
         _row_stride(value), _ptr(slot_mapping), _ptr(key_cache), _ptr(value_cache),
         key_cache.shape[0], _stream(stream)), "pa_cache_write")
+
+
+def pa_rope_cache_write(desc, positions, cos_sin_cache, rotary_dim, is_neox, query, key, value,
+                        slot_mapping, key_cache, value_cache, num_tokens=None, stream=None):
+    """Rotate query (in place) and key by position, write rotated key and value to the cache."""
+    if num_tokens is None:
+        num_tokens = key.shape[0]
+    _check(load().pa_rope_cache_write(
+        ctypes.byref(desc), num_tokens, _ptr(positions), _ptr(cos_sin_cache),
+        cos_sin_cache.shape[0], rotary_dim, 1 if is_neox else 0, _ptr(query), _row_stride(query),
+        _ptr(key), _row_stride(key), _ptr(value), _row_stride(value), _ptr(slot_mapping),
+        _ptr(key_cache), _ptr(value_cache), key_cache.shape[0], _stream(stream)),
+        "pa_rope_cache_write")
 
 
 def pa_decode_workspace_size(desc, num_reqs, max_seq_len, max_blocks_per_req):

@@ -179,6 +179,67 @@ pa_status pa_cache_write(const pa_attn_desc* desc, int64_t num_tokens, const voi
                                          static_cast<hipStream_t>(stream)));
 }
 
+pa_status pa_rope_cache_write(const pa_attn_desc* desc, int64_t num_tokens,
+                              const int64_t* positions, const float* cos_sin_cache,
+                              int64_t max_position, int32_t rotary_dim, int32_t is_neox,
+                              void* query, int64_t query_row_stride, const void* key,
+                              int64_t key_row_stride, const void* value, int64_t value_row_stride,
+                              const int64_t* slot_mapping, void* key_cache, void* value_cache,
+                              int64_t num_blocks, void* stream) {
+  pa_status st = check_desc(desc);
+  if (st != PA_OK) return st;
+  if (num_tokens < 0 || num_blocks < 0 || max_position <= 0) return PA_ERR_INVALID_ARG;
+  if (rotary_dim < 2 || rotary_dim % 2 != 0 || rotary_dim > desc->head_dim) return PA_ERR_INVALID_ARG;
+  if (is_neox != 0 && is_neox != 1) return PA_ERR_INVALID_ARG;
+  if (rotary_dim % 16 != 0) return PA_ERR_UNSUPPORTED;
+  if (num_tokens == 0) return PA_OK;
+  if (!positions || !cos_sin_cache || !query || !key || !value || !slot_mapping || !key_cache ||
+      !value_cache) {
+    return PA_ERR_INVALID_ARG;
+  }
+  const int64_t qrow = (int64_t)desc->num_q_heads * desc->head_dim;
+  const int64_t kvrow = (int64_t)desc->num_kv_heads * desc->head_dim;
+  if (query_row_stride < qrow || key_row_stride < kvrow || value_row_stride < kvrow) {
+    return PA_ERR_INVALID_ARG;
+  }
+  if (!aligned16(query) || !aligned16(key) || !aligned16(value) || !aligned16(key_cache) ||
+      !aligned16(value_cache) || !aligned16(cos_sin_cache)) {
+    return PA_ERR_INVALID_ARG;
+  }
+  if ((query_row_stride * 2) % 16 != 0 || (key_row_stride * 2) % 16 != 0 ||
+      (value_row_stride * 2) % 16 != 0) {
+    return PA_ERR_INVALID_ARG;
+  }
+  const int64_t per_token = (int64_t)desc->num_q_heads * (rotary_dim / 16) +
+                            (int64_t)desc->num_kv_heads *
+                                (rotary_dim / 16 + (desc->head_dim - rotary_dim) / 8 + desc->head_dim / 8);
+  if (num_tokens * per_token > (int64_t)0x7FFFFFFF * 256) return PA_ERR_UNSUPPORTED;
+  pa::RopeParams p{};
+  p.num_tokens = num_tokens;
+  p.num_q_heads = desc->num_q_heads;
+  p.num_kv_heads = desc->num_kv_heads;
+  p.head_dim = desc->head_dim;
+  p.rotary_dim = rotary_dim;
+  p.is_neox = is_neox;
+  p.positions = positions;
+  p.cos_sin = cos_sin_cache;
+  p.max_position = max_position;
+  p.query = query;
+  p.query_row_stride = query_row_stride;
+  p.key = key;
+  p.key_row_stride = key_row_stride;
+  p.value = value;
+  p.value_row_stride = value_row_stride;
+  p.slot_mapping = slot_mapping;
+  p.key_cache = key_cache;
+  p.value_cache = value_cache;
+  p.num_slots = num_blocks * desc->block_size;
+  p.k_inv_scale = desc->cache_dtype == PA_FP8_E4M3 ? 1.0f / desc->k_scale : 1.0f;
+  p.v_inv_scale = desc->cache_dtype == PA_FP8_E4M3 ? 1.0f / desc->v_scale : 1.0f;
+  return from_hip(pa::launch_rope_cache_write(p, desc->act_dtype, desc->cache_dtype,
+                                              static_cast<hipStream_t>(stream)));
+}
+
 static pa_status check_attn_common(const pa_attn_desc* desc, int32_t req_begin, int32_t req_end,
                                    const void* q, int64_t q_row_stride,
                                    const int32_t* query_start_loc, const int32_t* seq_lens,

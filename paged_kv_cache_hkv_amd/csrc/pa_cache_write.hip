@@ -23,26 +23,6 @@ namespace {
 
 constexpr int kThreads = 256;
 
-// float32 -> e4m3fn code, round to nearest even, saturating.
-__device__ inline unsigned encode_e4m3fn(float y) {
-  const unsigned bits = __builtin_bit_cast(unsigned, y);
-  const unsigned sign = (bits >> 24) & 0x80u;
-  const unsigned abits = bits & 0x7FFFFFFFu;
-  if (abits > 0x7F800000u) return sign | 0x7Fu;           // NaN
-  if (abits >= 0x43E00000u) return sign | 0x7Eu;          // |y| >= 448 (and inf): saturate
-  if (abits < 0x3C800000u) {                              // |y| < 2^-6: subnormal grid 2^-9
-    const float a = __builtin_bit_cast(float, abits);
-    const float q = __builtin_rintf(a * 512.0f);          // exact scaling, RNE
-    return sign | (unsigned)q;                            // q in 0..8; 8 is 2^-6 (code 0x08)
-  }
-  // normal: keep 3 mantissa bits, round to nearest even on the dropped 20 bits
-  const unsigned lsb = (abits >> 20) & 1u;
-  const unsigned r = (abits + 0x7FFFFu + lsb) & ~0xFFFFFu;
-  const int e = (int)(r >> 23) - 127;                     // -6 .. 8
-  const unsigned m = (r >> 20) & 7u;
-  return sign | ((unsigned)(e + 7) << 3) | m;
-}
-
 template <typename T>
 __device__ inline float elem_to_float(unsigned short b) { return Mfma<T>::to_float(b); }
 

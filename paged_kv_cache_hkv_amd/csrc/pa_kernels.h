@@ -35,6 +35,25 @@ struct CacheWriteParams {
   float k_inv_scale, v_inv_scale;  // fp8 only
 };
 
+struct RopeParams {
+  int64_t num_tokens;
+  int32_t num_q_heads, num_kv_heads, head_dim, rotary_dim, is_neox;
+  const int64_t* positions;
+  const float* cos_sin;    // [max_position, rotary_dim]: cos half, then sin half
+  int64_t max_position;
+  void* query;             // [T, Hq, D] rotated in place
+  int64_t query_row_stride;  // elements
+  const void* key;
+  int64_t key_row_stride;
+  const void* value;
+  int64_t value_row_stride;
+  const int64_t* slot_mapping;
+  void* key_cache;
+  void* value_cache;
+  int64_t num_slots;
+  float k_inv_scale, v_inv_scale;  // fp8 only
+};
+
 struct AttnParams {
   // geometry
   int32_t num_q_heads, num_kv_heads, group, head_dim;
@@ -75,6 +94,8 @@ constexpr int decode_waves_per_cu(int group, int cache_dtype) {
 hipError_t launch_metadata(const MetadataParams& p, hipStream_t stream);
 hipError_t launch_cache_write(const CacheWriteParams& p, int act_dtype, int cache_dtype,
                               hipStream_t stream);
+hipError_t launch_rope_cache_write(const RopeParams& p, int act_dtype, int cache_dtype,
+                                   hipStream_t stream);
 // Returns hipErrorInvalidValue for a combination no kernel is built for.
 hipError_t launch_decode(const AttnParams& p, int act_dtype, int cache_dtype, hipStream_t stream);
 hipError_t launch_prefill(const AttnParams& p, int act_dtype, int cache_dtype, hipStream_t stream);

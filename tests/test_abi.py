@@ -132,3 +132,26 @@ def test_prefill_checks():
     assert f(out_stride=4092) == B.PA_ERR_INVALID_ARG
     assert f(mq=-1) == B.PA_ERR_INVALID_ARG
     assert f(mq=0) == B.PA_OK                                 # no query rows: nothing launched
+
+
+def test_rope_cache_write_checks():
+    lib = B.load()
+    d = _desc()
+
+    def f(T=4, rd=128, neox=1, maxpos=4096, cs=FAKE, q=FAKE, qs=4096, ks=1024, dd=d):
+        return lib.pa_rope_cache_write(ctypes.byref(dd), T, FAKE, cs, maxpos, rd, neox, q, qs,
+                                       FAKE, ks, FAKE, ks, FAKE, FAKE, FAKE, 100, None)
+    assert f(rd=0) == B.PA_ERR_INVALID_ARG
+    assert f(rd=7) == B.PA_ERR_INVALID_ARG          # odd
+    assert f(rd=256) == B.PA_ERR_INVALID_ARG        # > head_dim
+    assert f(rd=40) == B.PA_ERR_UNSUPPORTED         # even but not a multiple of 16
+    assert f(neox=2) == B.PA_ERR_INVALID_ARG
+    assert f(maxpos=0) == B.PA_ERR_INVALID_ARG
+    assert f(T=-1) == B.PA_ERR_INVALID_ARG
+    assert f(cs=None) == B.PA_ERR_INVALID_ARG
+    assert f(cs=ctypes.c_void_p((1 << 20) + 4)) == B.PA_ERR_INVALID_ARG   # table not 16-byte aligned
+    assert f(q=None) == B.PA_ERR_INVALID_ARG
+    assert f(qs=1024) == B.PA_ERR_INVALID_ARG       # query row stride < Hq*D
+    assert f(ks=100) == B.PA_ERR_INVALID_ARG
+    assert f(dd=_desc(head_dim=96)) == B.PA_ERR_UNSUPPORTED
+    assert f(T=0) == B.PA_OK                        # nothing to do
