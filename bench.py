@@ -17,8 +17,9 @@ Also reported on the same JSON line:
 * ``cpu_baseline``: the oracle on the host cores over a bounded sample of the
   same batch;
 * ``extra``: the other measured workloads (GQA decode, chunked-prefill mix,
-  long-context fp8 MQA decode), each call timed with events between 1 GiB
-  cache-flush writes.
+  long-context fp8 MQA decode), each call timed with events after a 1 GiB
+  cache-evicting read; besides attention and the cache write this times the
+  fused RoPE + cache write (rotary_dim = head_dim, half-split pairs).
 """
 
 import argparse
@@ -116,6 +117,9 @@ def bench_extra(name, iters, flush):
         names.append("prefill")
     fns.append(st.cache_write)
     names.append("cache_write")
+    table = rope_table(wl.max_seq_len, wl.head_dim, 10000.0, "cuda")
+    fns.append(lambda: st.rope_cache_write(table, wl.head_dim, True))
+    names.append("rope_cache_write")
     for _ in range(3):
         for f in fns:
             f()
@@ -123,6 +127,9 @@ def bench_extra(name, iters, flush):
     for nm, (med, p10, p90) in zip(names, times):
         rec[f"{nm}_ms"] = round(med, 4)
         rec[f"{nm}_ms_p10_p90"] = [round(p10, 4), round(p90, 4)]
+    rb = rope_bytes(wl, wl.head_dim)
+    rec["rope_cache_write_bytes"] = rb
+    rec["rope_cache_write_GBps"] = round(rb / (rec["rope_cache_write_ms"] * 1e-3) / 1e9, 1)
     if wl.num_decodes:
         kb = kv_bytes(wl, range(wl.num_decodes))
         gbs = kb / (rec["decode_ms"] * 1e-3) / 1e9
@@ -141,6 +148,25 @@ def bench_extra(name, iters, flush):
     del st, t
     torch.cuda.empty_cache()
     return rec
+
+
+def rope_table(max_position, rotary_dim, base, device):
+    """float32 [max_position, rotary_dim]: cos(p*f_j) then sin(p*f_j), f_j = base^(-2j/R),
+    angles in float64 (the caller-built table the fused call takes)."""
+    j = np.arange(rotary_dim // 2, dtype=np.float64)
+    ang = np.arange(max_position, dtype=np.float64)[:, None] * base ** (-2.0 * j / rotary_dim)
+    tab = np.concatenate([np.cos(ang), np.sin(ang)], axis=1).astype(np.float32)
+    return torch.from_numpy(tab).to(device)
+
+
+def rope_bytes(wl, rotary_dim):
+    """Algorithmic bytes of one fused RoPE + cache write over the batch's real tokens:
+    q rotated part read and written, k and v read, k and v cache rows written, the
+    token's cos/sin row, its position and slot."""
+    T, hq, hkv, d = wl.num_tokens, wl.num_q_heads, wl.num_kv_heads, wl.head_dim
+    e = 1 if wl.cache_fp8 else 2
+    per = 2 * hq * rotary_dim * 2 + 2 * hkv * d * 2 + 2 * hkv * d * e + rotary_dim * 4 + 16
+    return T * per
 
 
 def take_snapshot(wl, t):
@@ -178,6 +204,9 @@ def main():
     ap.add_argument("--extra-iters", type=int, default=20)
     ap.add_argument("--no-extra", action="store_true")
     ap.add_argument("--no-cpu", action="store_true")
+    ap.add_argument("--fused-rope", action="store_true",
+                    help="each step rotates q and k by position in the cache-write launch "
+                         "(pa_rope_cache_write, rotary_dim = head_dim) instead of pa_cache_write")
     ap.add_argument("--copy-bytes", type=int, default=0,
                     help="first run a plain device-to-device copy of this many bytes three times "
                          "(the known-size kernel that calibrates rocprofv3 FETCH_SIZE/WRITE_SIZE)")
@@ -201,15 +230,22 @@ def main():
     snap = None if args.no_cpu else take_snapshot(wl, t)
     st = PagedAttentionStep(wl, t)
     stream = torch.cuda.current_stream()
+    if args.fused_rope:
+        table = rope_table(wl.max_seq_len, wl.head_dim, 10000.0, "cuda")
+        write = lambda: st.rope_cache_write(table, wl.head_dim, True)
+    else:
+        write = st.cache_write
     for _ in range(args.warmup):
-        st.run()
+        st.metadata()
+        write()
+        st.attention()
     torch.cuda.synchronize()
 
     ev = []
     t0 = time.perf_counter()
     for _ in range(args.steps):
         st.metadata()
-        st.cache_write()
+        write()
         a = torch.cuda.Event(enable_timing=True)
         b = torch.cuda.Event(enable_timing=True)
         a.record(stream)
@@ -242,7 +278,8 @@ def main():
                    "num_q_heads": wl.num_q_heads, "num_kv_heads": wl.num_kv_heads,
                    "head_dim": wl.head_dim, "block_size": wl.block_size,
                    "pool_blocks": wl.pool_blocks, "kv_bytes_per_step": kb,
-                   "step": "metadata + cache_write + decode (+ prefill when present)",
+                   "step": ("metadata + rope_cache_write" if args.fused_rope else
+                            "metadata + cache_write") + " + decode (+ prefill when present)",
                    "parallelism": "single GPU"},
         "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS,
                      "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),

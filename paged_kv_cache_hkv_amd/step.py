@@ -53,6 +53,14 @@ class PagedAttentionStep:
         B.pa_cache_write(self.desc, t.k_new, t.v_new, self.slot_mapping, t.key_cache,
                          t.value_cache, num_tokens=self.T_pad, stream=stream)
 
+    def rope_cache_write(self, cos_sin, rotary_dim, is_neox=True, stream=None):
+        """The fused alternative to ``cache_write``: rotate q (in place) and k by
+        position, then write the rotated k and v to the cache."""
+        t = self.t
+        B.pa_rope_cache_write(self.desc, self.positions, cos_sin, rotary_dim, is_neox, t.q,
+                              t.k_new, t.v_new, self.slot_mapping, t.key_cache, t.value_cache,
+                              num_tokens=self.T_pad, stream=stream)
+
     def decode(self, stream=None):
         if self.num_decodes == 0:
             return
