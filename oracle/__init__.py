@@ -23,6 +23,9 @@ Sources (web pages; every function cites the part it follows):
   listing (RoPE on Q and K before the cache write).
 * "Tour: One forward pass", stop 9 (the rotary embedding: a lookup in
   ``cos_sin_cache`` by position, then the rotation of each head).
+* "vLLM 推理全流程深度解析": the scheduler output's ``blocks_to_swap_in``,
+  ``blocks_to_swap_out`` and ``blocks_to_copy`` lists, swapping to host memory
+  and block sharing between sequences.
 
 Arithmetic is float64 unless the format itself fixes the precision (the fp8
 encoder's single float32 multiply) or the reading of the pages fixes it (the
@@ -33,10 +36,11 @@ rotary embedding's float32 steps, pinned to the float64 rotation).  Modules:
 * ``cache``      the slot_mapping scatter into ``[num_blocks, block_size, Hkv, D]``.
 * ``attention``  gather through the block table + dense causal softmax(QK^T*scale)V.
 * ``rope``       rotary position embedding of Q and K fused with the cache write.
+* ``blocks``     block copy and swap between block pools.
 
 Every function here is pinned by ``tests/test_oracle_*.py`` against values the
 pages print, closed forms, library routines or brute force; none is
 "parity unpinned".
 """
 
-from . import codecs, metadata, cache, attention, rope  # noqa: F401
+from . import codecs, metadata, cache, attention, rope, blocks  # noqa: F401
