@@ -13,6 +13,9 @@
  *                    the same scatter, in one launch)
  *                   pa_decode          -> attention of 1-token requests
  *                   pa_prefill_varlen  -> causal attention of (chunked) prefills
+ *   per step, when the scheduler asks for it
+ *                   pa_copy_blocks     -> swap blocks out to / in from host
+ *                                         memory, copy shared blocks
  *
  * Conventions shared by every call
  * --------------------------------
@@ -196,6 +199,43 @@ pa_status pa_rope_cache_write(const pa_attn_desc* desc, int64_t num_tokens,
                               const int64_t* slot_mapping,
                               void* key_cache, void* value_cache, int64_t num_blocks,
                               void* stream);
+
+/*
+ * pa_copy_blocks -- copy whole cache blocks (K and V) from one block pool to
+ * another by a list of (source block, destination block) pairs.  Serves the
+ * three pair lists of the scheduler output in "vLLM 推理全流程深度解析":
+ * blocks_to_swap_out (device pool -> host pool, when GPU memory runs short),
+ * blocks_to_swap_in (host pool -> device pool) and blocks_to_copy (inside one
+ * device pool: the private copy of a block that sequences share, e.g. beam
+ * candidates sharing the prompt's blocks).  One kernel launch for all pairs.
+ *
+ * src_key_cache, src_value_cache: the source pool, [src_num_blocks,
+ *   block_size, num_kv_heads, head_dim] of cache_dtype each.
+ * dst_key_cache, dst_value_cache: the destination pool, [dst_num_blocks, ...]
+ *   of the same element type and block shape (the same pointers as the source
+ *   for a copy inside one pool).
+ * block_pairs: int64 [num_pairs][2], (source block, destination block).
+ * Memory: each of the five buffers may be device memory or pinned host memory
+ *   (hipHostMalloc, torch's pin_memory) that the device can map; the kernel
+ *   moves the bytes itself.  Pageable or managed memory is rejected with
+ *   PA_ERR_INVALID_ARG (checked by a pointer-attribute query before launch).
+ *   Host buffers must stay pinned and untouched by the host until the work on
+ *   `stream` has finished.
+ * Result: destination block d of both caches holds the bytes of source block
+ *   s, for every pair with 0 <= s < src_num_blocks and 0 <= d < dst_num_blocks;
+ *   other pairs are skipped; no other byte of the destination is written.
+ *   Destinations must be distinct and, inside one pool, must not be sources
+ *   of other pairs (such pairs race; the result is then undefined).
+ * Alignment: cache pointers 16-byte aligned, block_pairs 8-byte aligned.
+ * Errors: PA_ERR_INVALID_ARG for a negative count or size, a null or
+ *   misaligned pointer, memory the device cannot reach; PA_ERR_UNSUPPORTED for
+ *   more than 2^30 - 1 pairs.  num_pairs == 0 returns PA_OK, enqueues nothing.
+ */
+pa_status pa_copy_blocks(const pa_attn_desc* desc,
+                         const void* src_key_cache, const void* src_value_cache,
+                         int64_t src_num_blocks,
+                         void* dst_key_cache, void* dst_value_cache, int64_t dst_num_blocks,
+                         const int64_t* block_pairs, int64_t num_pairs, void* stream);
 
 /*
  * pa_decode -- attention of decode requests through their block tables

@@ -67,6 +67,7 @@ _SIGS = {
     "pa_cache_write": [ctypes.POINTER(AttnDesc), _I64, _P, _I64, _P, _I64, _P, _P, _P, _I64, _P],
     "pa_rope_cache_write": [ctypes.POINTER(AttnDesc), _I64, _P, _P, _I64, _I32, _I32, _P, _I64, _P,
                             _I64, _P, _I64, _P, _P, _P, _I64, _P],
+    "pa_copy_blocks": [ctypes.POINTER(AttnDesc), _P, _P, _I64, _P, _P, _I64, _P, _I64, _P],
     "pa_decode": [ctypes.POINTER(AttnDesc), _I32, _I32, _P, _I64, _P, _P, _P, _I32, _P, _P, _I64,
                   _I32, _P, _SZ, _P, _I64, _P],
     "pa_decode_workspace_size": [ctypes.POINTER(AttnDesc), _I32, _I32, _I32, ctypes.POINTER(_SZ)],
@@ -150,6 +151,18 @@ def pa_rope_cache_write(desc, positions, cos_sin_cache, rotary_dim, is_neox, que
         _ptr(key), _row_stride(key), _ptr(value), _row_stride(value), _ptr(slot_mapping),
         _ptr(key_cache), _ptr(value_cache), key_cache.shape[0], _stream(stream)),
         "pa_rope_cache_write")
+
+
+def pa_copy_blocks(desc, src_key_cache, src_value_cache, dst_key_cache, dst_value_cache,
+                   block_pairs, num_pairs=None, stream=None):
+    """Copy block s of the source pool to block d of the destination pool for each
+    (s, d) row of block_pairs (int64 [n, 2]); pools on the device or in pinned host memory."""
+    if num_pairs is None:
+        num_pairs = block_pairs.shape[0]
+    _check(load().pa_copy_blocks(
+        ctypes.byref(desc), _ptr(src_key_cache), _ptr(src_value_cache), src_key_cache.shape[0],
+        _ptr(dst_key_cache), _ptr(dst_value_cache), dst_key_cache.shape[0], _ptr(block_pairs),
+        num_pairs, _stream(stream)), "pa_copy_blocks")
 
 
 def pa_decode_workspace_size(desc, num_reqs, max_seq_len, max_blocks_per_req):

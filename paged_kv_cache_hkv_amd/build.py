@@ -21,6 +21,7 @@ SOURCES = [
     "pa_api.cpp",
     "pa_metadata.hip",
     "pa_cache_write.hip",
+    "pa_blocks.hip",
     "pa_rope.hip",
     "pa_decode.hip",
     "pa_prefill.hip",

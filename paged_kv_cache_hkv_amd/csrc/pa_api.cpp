@@ -1,6 +1,7 @@
 // C ABI of libpa.so (declared in include/pa.h): host-side argument checks,
-// split-K planning and kernel launches.  Every check runs before any HIP call,
-// so a rejected call enqueues nothing.
+// split-K planning and kernel launches.  Every check runs before any launch
+// (the only HIP calls before it are queries), so a rejected call enqueues
+// nothing.
 #include "pa.h"
 
 #include <hip/hip_runtime.h>
@@ -88,6 +89,33 @@ pa_status from_hip(hipError_t e) {
   if (e == hipSuccess) return PA_OK;
   if (e == hipErrorInvalidValue) return PA_ERR_UNSUPPORTED;
   return PA_ERR_HIP;
+}
+
+// The address at which the device reaches `ptr`: device memory as it is,
+// pinned host memory (hipHostMalloc) through the device mapping the runtime
+// reports for it.  False for anything else (pageable host memory, managed
+// memory, unknown pointers).  Queries only.
+bool device_address(const void* ptr, const void** out) {
+  hipPointerAttribute_t a{};
+  if (hipPointerGetAttributes(&a, ptr) != hipSuccess) {
+    (void)hipGetLastError();   // clear the query's error so no later call reports it
+    return false;
+  }
+  if (a.type == hipMemoryTypeDevice && !a.isManaged) {
+    *out = ptr;
+    return true;
+  }
+  if (a.type == hipMemoryTypeHost && !a.isManaged) {
+    // succeeds only for pinned host memory the runtime has mapped for the device
+    void* dev = nullptr;
+    if (hipHostGetDevicePointer(&dev, const_cast<void*>(ptr), 0) != hipSuccess || dev == nullptr) {
+      (void)hipGetLastError();
+      return false;
+    }
+    *out = dev;
+    return true;
+  }
+  return false;
 }
 
 float scale_log2(const pa_attn_desc* d) {
@@ -238,6 +266,43 @@ pa_status pa_rope_cache_write(const pa_attn_desc* desc, int64_t num_tokens,
   p.v_inv_scale = desc->cache_dtype == PA_FP8_E4M3 ? 1.0f / desc->v_scale : 1.0f;
   return from_hip(pa::launch_rope_cache_write(p, desc->act_dtype, desc->cache_dtype,
                                               static_cast<hipStream_t>(stream)));
+}
+
+pa_status pa_copy_blocks(const pa_attn_desc* desc, const void* src_key_cache,
+                         const void* src_value_cache, int64_t src_num_blocks, void* dst_key_cache,
+                         void* dst_value_cache, int64_t dst_num_blocks, const int64_t* block_pairs,
+                         int64_t num_pairs, void* stream) {
+  pa_status st = check_desc(desc);
+  if (st != PA_OK) return st;
+  if (src_num_blocks < 0 || dst_num_blocks < 0 || num_pairs < 0) return PA_ERR_INVALID_ARG;
+  if (num_pairs == 0) return PA_OK;
+  if (!src_key_cache || !src_value_cache || !dst_key_cache || !dst_value_cache || !block_pairs) {
+    return PA_ERR_INVALID_ARG;
+  }
+  if (!aligned16(src_key_cache) || !aligned16(src_value_cache) || !aligned16(dst_key_cache) ||
+      !aligned16(dst_value_cache) || (reinterpret_cast<uintptr_t>(block_pairs) & 7u) != 0) {
+    return PA_ERR_INVALID_ARG;
+  }
+  if (num_pairs > 0x3FFFFFFF) return PA_ERR_UNSUPPORTED;   // grid x = 2 * num_pairs
+  const int64_t block_bytes = (int64_t)desc->block_size * desc->num_kv_heads * desc->head_dim *
+                              elem_bytes(desc->cache_dtype);
+  if (pa::copy_blocks_slices(block_bytes) > kMaxGridYZ) return PA_ERR_UNSUPPORTED;
+  pa::CopyBlocksParams p{};
+  const void* dev[5];
+  const void* host[5] = {src_key_cache, src_value_cache, dst_key_cache, dst_value_cache, block_pairs};
+  for (int i = 0; i < 5; ++i) {
+    if (!device_address(host[i], &dev[i])) return PA_ERR_INVALID_ARG;
+  }
+  p.src_key = dev[0];
+  p.src_value = dev[1];
+  p.src_blocks = src_num_blocks;
+  p.dst_key = const_cast<void*>(dev[2]);
+  p.dst_value = const_cast<void*>(dev[3]);
+  p.dst_blocks = dst_num_blocks;
+  p.pairs = static_cast<const int64_t*>(dev[4]);
+  p.num_pairs = num_pairs;
+  p.block_bytes = block_bytes;
+  return from_hip(pa::launch_copy_blocks(p, static_cast<hipStream_t>(stream)));
 }
 
 static pa_status check_attn_common(const pa_attn_desc* desc, int32_t req_begin, int32_t req_end,

@@ -54,6 +54,18 @@ struct RopeParams {
   float k_inv_scale, v_inv_scale;  // fp8 only
 };
 
+struct CopyBlocksParams {
+  const void* src_key;     // device-visible addresses of the two pools
+  const void* src_value;
+  int64_t src_blocks;
+  void* dst_key;
+  void* dst_value;
+  int64_t dst_blocks;
+  const int64_t* pairs;    // [num_pairs][2]: (source block, destination block)
+  int64_t num_pairs;
+  int64_t block_bytes;     // block_size * num_kv_heads * head_dim * element bytes, a multiple of 16
+};
+
 struct AttnParams {
   // geometry
   int32_t num_q_heads, num_kv_heads, group, head_dim;
@@ -96,6 +108,9 @@ hipError_t launch_cache_write(const CacheWriteParams& p, int act_dtype, int cach
                               hipStream_t stream);
 hipError_t launch_rope_cache_write(const RopeParams& p, int act_dtype, int cache_dtype,
                                    hipStream_t stream);
+// Workgroups per (pair, K or V) of the block copy: grid y of launch_copy_blocks.
+int64_t copy_blocks_slices(int64_t block_bytes);
+hipError_t launch_copy_blocks(const CopyBlocksParams& p, hipStream_t stream);
 // Returns hipErrorInvalidValue for a combination no kernel is built for.
 hipError_t launch_decode(const AttnParams& p, int act_dtype, int cache_dtype, hipStream_t stream);
 hipError_t launch_prefill(const AttnParams& p, int act_dtype, int cache_dtype, hipStream_t stream);

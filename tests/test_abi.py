@@ -155,3 +155,23 @@ def test_rope_cache_write_checks():
     assert f(ks=100) == B.PA_ERR_INVALID_ARG
     assert f(dd=_desc(head_dim=96)) == B.PA_ERR_UNSUPPORTED
     assert f(T=0) == B.PA_OK                        # nothing to do
+
+
+def test_copy_blocks_checks():
+    lib = B.load()
+    d = _desc()
+
+    def f(sk=FAKE, dk=FAKE, pairs=FAKE, n=4, snb=100, dnb=100, dd=d):
+        return lib.pa_copy_blocks(ctypes.byref(dd), sk, FAKE, snb, dk, FAKE, dnb, pairs, n, None)
+    assert f(n=-1) == B.PA_ERR_INVALID_ARG
+    assert f(snb=-1) == B.PA_ERR_INVALID_ARG
+    assert f(dnb=-5) == B.PA_ERR_INVALID_ARG
+    assert f(sk=None) == B.PA_ERR_INVALID_ARG
+    assert f(pairs=None) == B.PA_ERR_INVALID_ARG
+    assert f(dk=ctypes.c_void_p((1 << 20) + 8)) == B.PA_ERR_INVALID_ARG   # cache not 16-byte aligned
+    assert f(pairs=ctypes.c_void_p((1 << 20) + 4)) == B.PA_ERR_INVALID_ARG  # pairs not 8-byte aligned
+    assert f(n=1 << 31) == B.PA_ERR_UNSUPPORTED
+    assert f(dd=_desc(num_kv_heads=0)) == B.PA_ERR_INVALID_ARG
+    assert f(n=0, sk=None) == B.PA_OK             # nothing to do: no pointer is looked at
+    # an address no allocation owns: rejected by the pointer query, nothing launched
+    assert f() == B.PA_ERR_INVALID_ARG
