@@ -19,7 +19,8 @@ Also reported on the same JSON line:
 * ``extra``: the other measured workloads (GQA decode, chunked-prefill mix,
   long-context fp8 MQA decode), each call timed with events after a 1 GiB
   cache-evicting read; besides attention and the cache write this times the
-  fused RoPE + cache write (rotary_dim = head_dim, half-split pairs).
+  fused RoPE + cache write (rotary_dim = head_dim, half-split pairs) and, on
+  the GQA pool, the block copy / swap out / swap in of 4096 blocks.
 """
 
 import argparse
@@ -145,6 +146,8 @@ def bench_extra(name, iters, flush):
         rec["prefill_tok_per_s"] = round(toks / sec, 1)
         rec["prefill_TFLOPs"] = round(fl / sec / 1e12, 1)
         rec["prefill_mfma_frac"] = round(fl / sec / 1e12 / BF16_PEAK_TFLOPS, 4)
+    if name == "decode_gqa":
+        rec["copy_blocks"] = bench_blocks(wl, t, st.desc, iters, flush)
     del st, t
     torch.cuda.empty_cache()
     return rec
@@ -167,6 +170,47 @@ def rope_bytes(wl, rotary_dim):
     e = 1 if wl.cache_fp8 else 2
     per = 2 * hq * rotary_dim * 2 + 2 * hkv * d * 2 + 2 * hkv * d * e + rotary_dim * 4 + 16
     return T * per
+
+
+def bench_blocks(wl, t, desc, iters, flush, n_pairs=4096):
+    """pa_copy_blocks on the workload's pool: n_pairs blocks copied inside the
+    device pool, swapped out to a pinned host pool and swapped back in; beside
+    them, torch's contiguous copy of the same bytes between pinned host memory
+    and the device (the host link's rate for one large transfer)."""
+    nb = t.key_cache.shape[0]
+    rng = np.random.default_rng(11)
+    perm = rng.permutation(nb)
+    blk = t.key_cache[0].numel() * t.key_cache.element_size()
+    shape = (n_pairs,) + tuple(t.key_cache.shape[1:])
+    host_k = torch.empty(shape, dtype=t.key_cache.dtype, pin_memory=True)
+    host_v = torch.empty(shape, dtype=t.value_cache.dtype, pin_memory=True)
+    dev_buf = torch.empty(shape, dtype=t.key_cache.dtype, device="cuda")
+    host_ids = np.arange(n_pairs)
+    copy_pairs = torch.from_numpy(np.stack([perm[:n_pairs], perm[n_pairs:2 * n_pairs]], 1)).cuda()
+    out_pairs = torch.from_numpy(np.stack([perm[:n_pairs], host_ids], 1)).cuda()
+    in_pairs = torch.from_numpy(np.stack([host_ids, perm[2 * n_pairs:3 * n_pairs]], 1)).cuda()
+    kc, vc = t.key_cache, t.value_cache
+    fns = [
+        lambda: B.pa_copy_blocks(desc, kc, vc, kc, vc, copy_pairs),
+        lambda: B.pa_copy_blocks(desc, kc, vc, host_k, host_v, out_pairs),
+        lambda: B.pa_copy_blocks(desc, host_k, host_v, kc, vc, in_pairs),
+        lambda: host_k.copy_(dev_buf, non_blocking=True),
+        lambda: dev_buf.copy_(host_k, non_blocking=True),
+    ]
+    for f in fns:
+        f()
+    times = time_calls(fns, iters, flush)
+    moved = 2 * n_pairs * blk                       # K and V blocks
+    rec = {"pairs": n_pairs, "block_bytes": blk, "bytes_per_call": moved}
+    for nm, (med, p10, p90), nbytes in zip(
+            ["copy", "swap_out", "swap_in", "torch_d2h_contiguous", "torch_h2d_contiguous"], times,
+            [moved, moved, moved, n_pairs * blk, n_pairs * blk]):
+        rec[f"{nm}_ms"] = round(med, 4)
+        rec[f"{nm}_GBps"] = round(nbytes / (med * 1e-3) / 1e9, 1)
+    # the device copy reads and writes every byte in HBM
+    rec["copy_hbm_frac"] = round(2 * moved / (rec["copy_ms"] * 1e-3) / 1e9 / HBM_PEAK_GBS, 4)
+    del host_k, host_v, dev_buf
+    return rec
 
 
 def take_snapshot(wl, t):
