@@ -26,6 +26,18 @@ Readings where the pages are silent: the alignment of the causal mask for a
 cached prefix is bottom-right (it follows from the positions); ``scale`` is
 ``1/sqrt(head_size)`` unless the caller passes another; query head ``h`` maps to
 K/V head ``h // G`` (contiguous groups).
+
+Mask variants.  "Tour: One forward pass", stop 10, shows the kernel call with
+``alibi_slopes`` and ``window_size`` arguments, and "vLLM MHA Code Path"
+(Worked Trace step 10) speaks of the causal/window rules; "vLLM 推理全流程深度解析"
+lists ALiBi beside RoPE as a position encoding that uses the token positions.
+The pages define neither, so the plain readings are taken:
+* sliding window ``W`` (0 = none): query at position ``p`` attends keys
+  ``j`` with ``p - W < j <= p`` -- the ``W`` most recent positions, itself
+  included;
+* ALiBi: query head ``h`` adds ``slope[h] * (j - p)`` (zero for the key at the
+  query's own position, more negative the older the key) to the scaled score
+  ``q . k * scale`` before the softmax; the caller gives the slopes.
 """
 
 import math
@@ -48,11 +60,14 @@ def gather_request_kv(key_cache_f64, value_cache_f64, block_table_row, seq_len, 
     return k, v
 
 
-def causal_attention(q, k, v, num_computed, scale):
+def causal_attention(q, k, v, num_computed, scale, sliding_window=0, alibi_slopes=None):
     """Dense causal attention of one request in float64.
 
     q: [n, Hq, D]; k, v: [s, Hkv, D] with s = num_computed + n.
-    Row i attends keys 0 .. num_computed + i.  Returns [n, Hq, D].
+    Row i (position p = num_computed + i) attends keys 0 .. p, or only
+    p - sliding_window + 1 .. p when sliding_window > 0; with alibi_slopes
+    ([Hq]) head h adds slope[h] * (j - p) to the score of key j.
+    Returns [n, Hq, D].
     """
     n, hq, d = q.shape
     s, hkv, _ = k.shape
@@ -63,9 +78,13 @@ def causal_attention(q, k, v, num_computed, scale):
     key_idx = np.arange(s)[None, :]
     last_key = (num_computed + np.arange(n))[:, None]
     allowed = key_idx <= last_key                         # [n, s]
+    if sliding_window > 0:
+        allowed &= key_idx > last_key - sliding_window
     for h in range(hq):
         kv = h // g
         scores = (q[:, h, :] @ k[:, kv, :].T) * scale     # [n, s]
+        if alibi_slopes is not None:
+            scores = scores + float(alibi_slopes[h]) * (key_idx - last_key)
         scores = np.where(allowed, scores, -np.inf)
         mx = scores.max(axis=1, keepdims=True)
         p = np.exp(scores - mx)
@@ -85,7 +104,7 @@ def decode_cache(cache_bits, cache_dtype, scale=1.0):
 
 def paged_attention(q, key_cache, value_cache, block_tables, query_start_loc, seq_lens,
                     block_size, scale=None, requests=None, cache_dtype=None,
-                    k_scale=1.0, v_scale=1.0):
+                    k_scale=1.0, v_scale=1.0, sliding_window=0, alibi_slopes=None):
     """Attention of a batch over the paged cache, one request at a time.
 
     q: float64 [T, Hq, D] (already decoded).
@@ -93,6 +112,7 @@ def paged_attention(q, key_cache, value_cache, block_tables, query_start_loc, se
       raw bits when ``cache_dtype`` is given ('f16' | 'bf16' | 'fp8_e4m3'); raw
       bits are decoded per request, so a large pool is never widened at once.
     requests: iterable of request indices to compute (default: all).
+    sliding_window, alibi_slopes: the mask variants of ``causal_attention``.
     Returns {r: float64 [n_r, Hq, D]}.
     """
     d = q.shape[2]
@@ -117,5 +137,5 @@ def paged_attention(q, key_cache, value_cache, block_tables, query_start_loc, se
             vb = decode_cache(value_cache[ids], cache_dtype, v_scale)
             local = np.arange(nb)
             k, v = gather_request_kv(kb, vb, local, s, block_size)
-        result[r] = causal_attention(q[start:end], k, v, c, scale)
+        result[r] = causal_attention(q[start:end], k, v, c, scale, sliding_window, alibi_slopes)
     return result
