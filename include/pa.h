@@ -96,6 +96,21 @@ typedef enum pa_dtype {
  * (see pa_decode); 0 lets the library choose (four per compute unit of the
  * current device).  Otherwise 1 .. 2^20; the result does not depend on it
  * beyond float32 rounding.
+ *
+ * Mask variants of pa_decode and pa_prefill_varlen (the alibi_slopes and
+ * window_size arguments of the attention call in stop 10 of "Tour: One
+ * forward pass"; the causal/window rules of step 10 of the worked trace in
+ * "vLLM MHA Code Path"):
+ * - sliding_window W > 0: the query at position p attends only keys j with
+ *   p - W < j <= p (its W most recent positions, itself included); blocks
+ *   wholly before the window are not read.  0 = plain causal attention.
+ * - alibi_slopes: when not NULL, query head h adds slope[h] * (j - p) to the
+ *   scaled score softmax_scale * q.k of key j (fp8: the scale-corrected
+ *   score) before the softmax.  The array stays owned by the caller and must
+ *   live until the calls that use this descriptor have finished; 4-byte
+ *   aligned.
+ * Both use the query position p = seq_len - query_len + i for row i of a
+ * request (the decode row: p = seq_len - 1).
  */
 typedef struct pa_attn_desc {
   int32_t num_q_heads;
@@ -108,6 +123,8 @@ typedef struct pa_attn_desc {
   float k_scale;
   float v_scale;
   int32_t decode_workers;
+  int32_t sliding_window;     /* 0: none; W > 0: see below */
+  const float* alibi_slopes;  /* NULL: none; else device float32 [num_q_heads] */
 } pa_attn_desc;
 
 /* Human-readable name of a status code (static storage). */

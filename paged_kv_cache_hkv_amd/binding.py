@@ -39,18 +39,25 @@ class AttnDesc(ctypes.Structure):
         ("k_scale", ctypes.c_float),
         ("v_scale", ctypes.c_float),
         ("decode_workers", ctypes.c_int32),
+        ("sliding_window", ctypes.c_int32),
+        ("alibi_slopes", ctypes.c_void_p),
     ]
 
 
 def make_desc(num_q_heads, num_kv_heads, head_dim, block_size=16, act_dtype=PA_BF16,
               cache_dtype=None, softmax_scale=None, k_scale=1.0, v_scale=1.0,
-              decode_workers=0):
+              decode_workers=0, sliding_window=0, alibi_slopes=None):
+    """alibi_slopes: float32 device tensor [num_q_heads] or None; the descriptor
+    keeps a reference so the memory outlives it."""
     if cache_dtype is None:
         cache_dtype = act_dtype
     if softmax_scale is None:
         softmax_scale = head_dim ** -0.5
-    return AttnDesc(num_q_heads, num_kv_heads, head_dim, block_size, act_dtype, cache_dtype,
-                    softmax_scale, k_scale, v_scale, decode_workers)
+    d = AttnDesc(num_q_heads, num_kv_heads, head_dim, block_size, act_dtype, cache_dtype,
+                 softmax_scale, k_scale, v_scale, decode_workers, sliding_window,
+                 None if alibi_slopes is None else alibi_slopes.data_ptr())
+    d._alibi_ref = alibi_slopes
+    return d
 
 
 _lib = None

@@ -44,6 +44,8 @@ pa_status check_desc(const pa_attn_desc* d) {
     }
   }
   if (d->decode_workers < 0 || d->decode_workers > kMaxDecodeWorkers) return PA_ERR_INVALID_ARG;
+  if (d->sliding_window < 0) return PA_ERR_INVALID_ARG;
+  if ((reinterpret_cast<uintptr_t>(d->alibi_slopes) & 3u) != 0) return PA_ERR_INVALID_ARG;
   return PA_OK;
 }
 
@@ -355,6 +357,9 @@ static pa::AttnParams make_params(const pa_attn_desc* desc, int32_t req_begin, i
   p.out_row_stride = out_row_stride;
   p.scale_log2 = scale_log2(desc);
   p.v_scale = desc->cache_dtype == PA_FP8_E4M3 ? desc->v_scale : 1.0f;
+  p.window_left = desc->sliding_window > 0 ? desc->sliding_window - 1 : pa::kNoWindow;
+  p.alibi = desc->alibi_slopes;
+  p.masked = desc->sliding_window > 0 || desc->alibi_slopes != nullptr;
   return p;
 }
 

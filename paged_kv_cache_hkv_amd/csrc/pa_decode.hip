@@ -52,6 +52,14 @@
 // fp8 (OCP e4m3fn) caches are widened to bf16/fp16 exactly in registers with
 // the gfx950 packed converts; the K scale is folded into the score scale and
 // the V scale into the final division.
+//
+// Mask variants (the alibi_slopes and window_size arguments of the attention
+// call in stop 10 of "Tour: One forward pass"): with a sliding window of W
+// keys a request streams only the blocks from its window's first key on (the
+// stream, the worker ranges and the reduce all count those blocks), and keys
+// before the window inside the first block are masked; ALiBi adds
+// slope[h] * (key - query position) to each score in log2 units.  Both live in
+// a separate instantiation (MASK), so the plain kernel carries neither.
 #include "pa_device.h"
 #include "pa_kernels.h"
 
@@ -61,6 +69,7 @@ namespace {
 
 constexpr int kBlock = 16;                // tokens per cache block
 constexpr float kRescaleLog2 = 8.f;       // lazy rescale threshold (log2 units)
+constexpr float kLog2e = 1.4426950408889634f;
 constexpr int kLdsBudget = 160 * 1024;    // LDS of one compute unit
 #ifndef PA_DECODE_STAGES
 #define PA_DECODE_STAGES 3
@@ -116,8 +125,14 @@ __device__ inline u32x2 lds_read_tr16(const unsigned char* p) {
   return __builtin_bit_cast(u32x2, __builtin_amdgcn_ds_read_tr16_b64_v4bf16(lp));
 }
 
+// First key a decode row of s keys may see (its position is s - 1), and the
+// first block holding one: 0 without a sliding window.
+__device__ inline int first_key(const AttnParams& p, int s) { return max(0, s - 1 - p.window_left); }
+__device__ inline int first_block(const AttnParams& p, int s) { return first_key(p, s) / kBlock; }
+
 // Cache blocks request rr (index within the call) streams: 0 for a request
-// that is not a decode (query length != 1) or has no keys.  `uniform`: rr is
+// that is not a decode (query length != 1) or has no keys; with a sliding
+// window only the blocks from the window's first key on.  `uniform`: rr is
 // the same in every lane (scalar loads).
 __device__ inline int stream_blocks(const AttnParams& p, int rr, bool uniform) {
   const int r = p.req_begin + rr;
@@ -133,7 +148,7 @@ __device__ inline int stream_blocks(const AttnParams& p, int rr, bool uniform) {
   }
   if (q1 - q0 != 1) return 0;
   s = min(min(s, p.max_seq_len), p.max_blocks_per_req * kBlock);
-  return s > 0 ? (s + kBlock - 1) / kBlock : 0;
+  return s > 0 ? (s + kBlock - 1) / kBlock - first_block(p, s) : 0;
 }
 
 __device__ inline int64_t readlane64(int64_t v, int l) {
@@ -160,10 +175,13 @@ __device__ inline int64_t wave_scan(int64_t v) {
 __device__ inline int64_t range_begin(int64_t w, int64_t T, int64_t W) { return w * T / W; }
 
 // Position in the stream: request (index within the call), K/V head, block
-// of that head; and the request's block count, key count and query row.
+// of that head counted from b0 (the first block the request streams: 0, or
+// the window's first block); and the request's streamed block count, key
+// count, first visible key and query row.
 struct Cursor {
   int rr, kvh, b, nb;
   int s_eff, q_row;
+  int b0, lo;
 };
 
 // Fill the request fields of c for request c.rr (wave-uniform loads).
@@ -174,7 +192,9 @@ __device__ inline void load_request(const AttnParams& p, Cursor& c) {
   const int s = min(min(load_uniform(p.seq_lens, r), p.max_seq_len), p.max_blocks_per_req * kBlock);
   c.q_row = q0;
   c.s_eff = s;
-  c.nb = (q1 - q0 == 1 && s > 0) ? (s + kBlock - 1) / kBlock : 0;
+  c.lo = first_key(p, s);
+  c.b0 = c.lo / kBlock;
+  c.nb = (q1 - q0 == 1 && s > 0) ? (s + kBlock - 1) / kBlock - c.b0 : 0;
 }
 
 // Advance by one unit (wave-uniform); skips requests that stream nothing.
@@ -192,7 +212,7 @@ __device__ inline void advance(const AttnParams& p, Cursor& c) {
   } while (c.nb == 0);
 }
 
-template <int D, typename CT, int KVB, int HT, int S, int WV>
+template <int D, typename CT, int KVB, int HT, int S, int WV, bool MASK>
 __global__ __launch_bounds__(64 * WV) void decode_kernel(AttnParams p) {
   using M = Mfma<CT>;
   using vec8 = typename M::vec8;
@@ -226,7 +246,7 @@ __global__ __launch_bounds__(64 * WV) void decode_kernel(AttnParams p) {
   }
   const int64_t g0 = range_begin(worker, T, W);
   const int64_t n = range_begin(worker + 1, T, W) - g0;
-  Cursor cur{0, 0, 0, 0, 0, 0};
+  Cursor cur{0, 0, 0, 0, 0, 0, 0, 0};
   {
     // worker 0 also publishes the exclusive prefix for the reduce kernel
     int64_t run = 0;
@@ -292,7 +312,8 @@ __global__ __launch_bounds__(64 * WV) void decode_kernel(AttnParams p) {
         if (k + 16 * lane < qbytes) lds_dma16(qb, (unsigned)(k + 16 * lane), q_m0 + k);
       q_pending = true;
     }
-    int id = load_uniform(p.block_tables, (int64_t)(p.req_begin + ic.rr) * p.max_blocks_per_req + ic.b);
+    int id = load_uniform(p.block_tables,
+                          (int64_t)(p.req_begin + ic.rr) * p.max_blocks_per_req + ic.b0 + ic.b);
     id = (id >= 0 && (int64_t)id < num_blocks) ? id : -1;
     okbits = (okbits & ~(1u << st)) | ((id >= 0 ? 1u : 0u) << st);
     const int64_t boff = (int64_t)(id < 0 ? 0 : id) * blk_stride + (int64_t)ic.kvh * D * KVB;
@@ -335,6 +356,7 @@ __global__ __launch_bounds__(64 * WV) void decode_kernel(AttnParams p) {
   const float c2 = p.scale_log2;
   vec8 qop[HT][KS];
   float m_used[HT], l_run[HT];
+  float slope2[HT];     // ALiBi slope of this lane's head, in log2 units
   f32x4 acc[HT][NM];
   int seg = 0;          // segments this worker has finished
   int seg_b0 = 0;       // first block of the current segment
@@ -359,6 +381,18 @@ __global__ __launch_bounds__(64 * WV) void decode_kernel(AttnParams p) {
         }
         m_used[ht] = -INFINITY;
         l_run[ht] = 0.f;
+        if constexpr (MASK) {
+          // the group's slopes by scalar loads (a vector load here would be
+          // counted with the ring's copies), each lane keeping its head's
+          slope2[ht] = 0.f;
+          if (p.alibi != nullptr) {
+            const int32_t* sl = reinterpret_cast<const int32_t*>(p.alibi) + cur.kvh * G;
+            for (int h = ht * 16; h < min(G, ht * 16 + 16); ++h) {
+              const float v = __builtin_bit_cast(float, load_uniform(sl, h));
+              slope2[ht] = (hig == h) ? v * kLog2e : slope2[ht];
+            }
+          }
+        }
 #pragma unroll
         for (int m = 0; m < NM; ++m) acc[ht][m] = f32x4{0.f, 0.f, 0.f, 0.f};
       }
@@ -384,14 +418,18 @@ __global__ __launch_bounds__(64 * WV) void decode_kernel(AttnParams p) {
       for (int ht = 0; ht < HT; ++ht) sc[ht] = M::mma16(kop, qop[ht][s], sc[ht]);
     }
 
-    // ---- masks: tokens past the sequence, absent blocks (selects only) ----
-    const int tok0 = cur.b * kBlock;
+    // ---- masks: tokens past the sequence or before the window, absent
+    // blocks (selects only) ----
+    const int tok0 = (cur.b0 + cur.b) * kBlock;
     const bool blk_ok = (okbits >> st_i) & 1u;
     unsigned vm0 = 0xFFFFFFFFu, vm1 = 0xFFFFFFFFu;
-    if (!blk_ok || tok0 + kBlock > cur.s_eff) {
+    if (!blk_ok || tok0 + kBlock > cur.s_eff || (MASK && tok0 < cur.lo)) {
       bool bad[4];
 #pragma unroll
-      for (int k = 0; k < 4; ++k) bad[k] = !blk_ok || tok0 + row_token(4 * q4 + k) >= cur.s_eff;
+      for (int k = 0; k < 4; ++k) {
+        const int tok = tok0 + row_token(4 * q4 + k);
+        bad[k] = !blk_ok || tok >= cur.s_eff || (MASK && tok < cur.lo);
+      }
       vm0 = (bad[0] ? 0u : 0x0000FFFFu) | (bad[1] ? 0u : 0xFFFF0000u);
       vm1 = (bad[2] ? 0u : 0x0000FFFFu) | (bad[3] ? 0u : 0xFFFF0000u);
 #pragma unroll
@@ -407,6 +445,12 @@ __global__ __launch_bounds__(64 * WV) void decode_kernel(AttnParams p) {
       float x[4];
 #pragma unroll
       for (int k = 0; k < 4; ++k) x[k] = sc[ht][k] * c2;
+      if constexpr (MASK) {
+        // ALiBi: slope * (key - query position), the query at position s - 1
+#pragma unroll
+        for (int k = 0; k < 4; ++k)
+          x[k] += slope2[ht] * (float)(tok0 + row_token(4 * q4 + k) - (cur.s_eff - 1));
+      }
       // A head's reference max only moves when one of its scores exceeds it
       // by 2^8; each lane tests its own 4 scores, and only when some lane
       // does (rare after a segment's first block) is the head max formed
@@ -627,9 +671,13 @@ constexpr int ring_depth() {
 template <int D, typename CT, int KVB, int HT>
 hipError_t launch_typed(const AttnParams& p, hipStream_t stream) {
   constexpr int WV = waves_per_wg<D, KVB, HT>();
+  constexpr int S = ring_depth<D, KVB, HT>();
   dim3 grid((unsigned)((p.num_workers + WV - 1) / WV));
-  hipLaunchKernelGGL((decode_kernel<D, CT, KVB, HT, ring_depth<D, KVB, HT>(), WV>), grid,
-                     dim3(64 * WV), 0, stream, p);
+  if (p.masked) {
+    hipLaunchKernelGGL((decode_kernel<D, CT, KVB, HT, S, WV, true>), grid, dim3(64 * WV), 0, stream, p);
+  } else {
+    hipLaunchKernelGGL((decode_kernel<D, CT, KVB, HT, S, WV, false>), grid, dim3(64 * WV), 0, stream, p);
+  }
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   dim3 rgrid((unsigned)p.num_q_heads, (unsigned)p.num_reqs);

@@ -66,6 +66,8 @@ struct CopyBlocksParams {
   int64_t block_bytes;     // block_size * num_kv_heads * head_dim * element bytes, a multiple of 16
 };
 
+constexpr int32_t kNoWindow = 1 << 30;
+
 struct AttnParams {
   // geometry
   int32_t num_q_heads, num_kv_heads, group, head_dim;
@@ -86,6 +88,12 @@ struct AttnParams {
   // scalars
   float scale_log2;   // softmax_scale * k_scale * log2(e)
   float v_scale;      // 1 unless the cache is fp8
+  // mask variants: keys j < p - window_left are masked for the query at
+  // position p (kNoWindow when there is no window); alibi (may be null):
+  // per query head slope of the bias slope * (j - p) on the scaled score
+  int32_t window_left;
+  const float* alibi;
+  bool masked;        // window or ALiBi present: the kernels' masked variants run
   int32_t max_seq_len;
   int32_t max_query_len;
   // decode: the flattened (request, K/V head, block) key stream is cut into

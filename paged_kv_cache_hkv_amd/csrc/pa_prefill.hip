@@ -32,6 +32,12 @@
 // overflows).  The next tile's global loads are issued before the current
 // tile's math and land in the other LDS buffer after it.
 // fp8 caches are widened to bf16/fp16 when the tile is written to LDS.
+// Mask variants (MASK instantiations; the alibi_slopes and window_size
+// arguments of the same call): a sliding window starts the key loop at the
+// first tile any query of the workgroup may see and skips a wave's math on
+// tiles wholly before its queries' windows; ALiBi adds slope * (key - query
+// position) to each score, applied together with the window mask when the
+// scores are moved to log2 units (window_alibi).
 #include "pa_device.h"
 #include "pa_kernels.h"
 
@@ -44,6 +50,24 @@ constexpr int kThreads = 64 * kWaves;
 constexpr int kBlock = 16;
 constexpr int kTileK = 64;          // keys per LDS tile
 constexpr float kRescaleLog2 = 8.f; // lazy rescale threshold (log2 units)
+constexpr float kLog2e = 1.4426950408889634f;
+
+// Mask variants (sliding window, ALiBi) of one score tile, in place: keys
+// before a query's window get -inf, then every score is moved to log2 units
+// with its ALiBi bias, slope * (key - query position).  The caller's softmax
+// then runs with a unit scale.  Lane layout as in the kernels: element g of
+// subtile u is key k0 + 32u + 8(g/4) + 4*half + g%4 of the lane's query.
+__device__ inline void window_alibi(f32x16 (&sc)[2], int k0, int half, int qpos, int window_left,
+                                    float scale_log2, float slope2) {
+#pragma unroll
+  for (int u = 0; u < 2; ++u)
+#pragma unroll
+    for (int g = 0; g < 16; ++g) {
+      const int key = k0 + 32 * u + 8 * (g / 4) + 4 * half + (g % 4);
+      const float x = __builtin_fmaf(sc[u][g], scale_log2, slope2 * (float)(key - qpos));
+      sc[u][g] = (key < qpos - window_left) ? -INFINITY : x;
+    }
+}
 
 __device__ inline int swap_bits23(int k) {
   return (k & ~0xC) | ((k & 0x4) << 1) | ((k & 0x8) >> 1);
@@ -200,7 +224,7 @@ __device__ inline void store_tile(const TileRegs<D, KVB>& regs, unsigned short* 
   }
 }
 
-template <int D, typename CT, int KVB>
+template <int D, typename CT, int KVB, bool MASK>
 __global__ __launch_bounds__(kThreads, 2) void prefill_kernel(AttnParams p, int hpw) {
   using M = Mfma<CT>;
   using vec8 = typename M::vec8;
@@ -224,6 +248,8 @@ __global__ __launch_bounds__(kThreads, 2) void prefill_kernel(AttnParams p, int 
   s_eff = min(s_eff, p.max_blocks_per_req * kBlock);
   const int k_end = min(c + q_hi, s_eff);          // keys any query of the tile may see
   const int ntiles = (k_end + kTileK - 1) / kTileK;
+  // first key tile any query of the tile may see (a sliding window skips the rest)
+  const int kt0 = MASK ? max(0, c + max(q_hi - QB, 0) - p.window_left) / kTileK : 0;
 
   const int lane = threadIdx.x & 63;
   const int wave = wave_uniform(threadIdx.x >> 6);
@@ -259,7 +285,11 @@ __global__ __launch_bounds__(kThreads, 2) void prefill_kernel(AttnParams p, int 
   tc.s_eff = s_eff;
   tc.nblk = (s_eff + kBlock - 1) / kBlock;
 
-  const float c2 = p.scale_log2;
+  // masked variants move the scores to log2 units themselves (window_alibi)
+  const float c2 = MASK ? 1.f : p.scale_log2;
+  const float slope2 = (MASK && p.alibi != nullptr)
+                           ? __builtin_bit_cast(float, load_uniform(reinterpret_cast<const int32_t*>(p.alibi), qh)) * kLog2e
+                           : 0.f;
   f32x16 acc[DT];
 #pragma unroll
   for (int t = 0; t < DT; ++t) acc[t] = f32x16{};
@@ -268,16 +298,16 @@ __global__ __launch_bounds__(kThreads, 2) void prefill_kernel(AttnParams p, int 
   const int wave_last_pos = c + wq0 + 31;
 
   TileRegs<D, KVB> regs;
-  if (ntiles > 0) {
-    load_tile<D, KVB>(regs, tc, 0);
+  if (ntiles > kt0) {
+    load_tile<D, KVB>(regs, tc, kt0);
     store_tile<D, CT, KVB>(regs, Ks[0], Vt[0]);
   }
   __syncthreads();
-  for (int kt = 0; kt < ntiles; ++kt) {
-    const int buf = kt & 1;
+  for (int kt = kt0; kt < ntiles; ++kt) {
+    const int buf = (kt - kt0) & 1;
     if (kt + 1 < ntiles) load_tile<D, KVB>(regs, tc, kt + 1);
     const int k0 = kt * kTileK;
-    if (k0 <= wave_last_pos) {
+    if (k0 <= wave_last_pos && (!MASK || k0 + kTileK - 1 >= wave_first_pos - p.window_left)) {
       // ---- S^T (keys x queries), two 32-key subtiles ----
       f32x16 sc[2];
 #pragma unroll
@@ -304,6 +334,7 @@ __global__ __launch_bounds__(kThreads, 2) void prefill_kernel(AttnParams p, int 
             sc[u][g] = (key > qpos || key >= s_eff || !blk) ? -INFINITY : sc[u][g];
           }
       }
+      if constexpr (MASK) window_alibi(sc, k0, half, qpos, p.window_left, p.scale_log2, slope2);
       float mx = -INFINITY;
 #pragma unroll
       for (int u = 0; u < 2; ++u)
@@ -460,7 +491,7 @@ __device__ inline void fix_tile(const TileCtx& c, int kt, u32x4* Vl, int wave, i
   }
 }
 
-template <int D, typename CT>
+template <int D, typename CT, bool MASK>
 __global__ __launch_bounds__(kThreads, 2) void prefill_dma_kernel(AttnParams p, int hpw) {
   using M = Mfma<CT>;
   using vec8 = typename M::vec8;
@@ -489,6 +520,7 @@ __global__ __launch_bounds__(kThreads, 2) void prefill_dma_kernel(AttnParams p, 
   s_eff = min(s_eff, p.max_blocks_per_req * kBlock);
   const int k_end = min(c + q_hi, s_eff);
   const int ntiles = (k_end + kTileK - 1) / kTileK;
+  const int kt0 = MASK ? max(0, c + max(q_hi - QB, 0) - p.window_left) / kTileK : 0;
 
   const int lane = threadIdx.x & 63;
   const int wave = wave_uniform(threadIdx.x >> 6);
@@ -529,7 +561,10 @@ __global__ __launch_bounds__(kThreads, 2) void prefill_dma_kernel(AttnParams p, 
   const int ta = (lane & 15) >> 2, tb = lane & 3; // transposed-read row supplier (key a, d 4b)
   const int vswz = L::swv(ta);                    // keys ... + 4h + a share a's swizzle
 
-  const float c2 = p.scale_log2;
+  const float c2 = MASK ? 1.f : p.scale_log2;
+  const float slope2 = (MASK && p.alibi != nullptr)
+                           ? __builtin_bit_cast(float, load_uniform(reinterpret_cast<const int32_t*>(p.alibi), qh)) * kLog2e
+                           : 0.f;
   f32x16 acc[DT];
 #pragma unroll
   for (int t = 0; t < DT; ++t) acc[t] = f32x16{};
@@ -537,10 +572,10 @@ __global__ __launch_bounds__(kThreads, 2) void prefill_dma_kernel(AttnParams p, 
   const int wave_first_pos = c + wq0;
   const int wave_last_pos = c + wq0 + 31;
 
-  if (ntiles > 0) {
-    dma_tile<D>(tc, 0, K0, V0, wave, lane);
+  if (ntiles > kt0) {
+    dma_tile<D>(tc, kt0, K0, V0, wave, lane);
     __builtin_amdgcn_s_waitcnt(0);
-    fix_tile<D>(tc, 0, V0, wave, lane);
+    fix_tile<D>(tc, kt0, V0, wave, lane);
   }
   // Q (and tile 0) resident on every path into the loop, so the loop's first
   // MFMA never waits on the vector-memory counter while later DMAs are in flight
@@ -550,7 +585,7 @@ __global__ __launch_bounds__(kThreads, 2) void prefill_dma_kernel(AttnParams p, 
   auto tile_step = [&](int kt, const u32x4* K, const u32x4* V, u32x4* Kn, u32x4* Vn) {
     if (kt + 1 < ntiles) dma_tile<D>(tc, kt + 1, Kn, Vn, wave, lane);
     const int k0 = kt * kTileK;
-    if (k0 <= wave_last_pos) {
+    if (k0 <= wave_last_pos && (!MASK || k0 + kTileK - 1 >= wave_first_pos - p.window_left)) {
       // two independent accumulation chains (the 32-key subtiles), interleaved
       f32x16 sc[2] = {f32x16{}, f32x16{}};
 #pragma unroll
@@ -572,6 +607,7 @@ __global__ __launch_bounds__(kThreads, 2) void prefill_dma_kernel(AttnParams p, 
             sc[u][g] = (key > qpos || key >= s_eff || !blk) ? -INFINITY : sc[u][g];
           }
       }
+      if constexpr (MASK) window_alibi(sc, k0, half, qpos, p.window_left, p.scale_log2, slope2);
       float mx = -INFINITY;
 #pragma unroll
       for (int u = 0; u < 2; ++u)
@@ -627,7 +663,7 @@ __global__ __launch_bounds__(kThreads, 2) void prefill_dma_kernel(AttnParams p, 
     if (kt + 1 < ntiles) fix_tile<D>(tc, kt + 1, Vn, wave, lane);
     __syncthreads();
   };
-  for (int kt = 0; kt < ntiles; kt += 2) {
+  for (int kt = kt0; kt < ntiles; kt += 2) {
     tile_step(kt, K0, V0, K1, V1);
     if (kt + 1 < ntiles) tile_step(kt + 1, K1, V1, K0, V0);
   }
@@ -664,9 +700,17 @@ hipError_t launch_typed(const AttnParams& p, hipStream_t stream) {
   // x: query-head group, y: request, z: tile counted from the end of the request
   dim3 grid((unsigned)(p.num_q_heads / hpw), (unsigned)p.num_reqs, (unsigned)qtiles);
   if constexpr (KVB == 2) {
-    hipLaunchKernelGGL((prefill_dma_kernel<D, CT>), grid, dim3(kThreads), 0, stream, p, hpw);
+    if (p.masked) {
+      hipLaunchKernelGGL((prefill_dma_kernel<D, CT, true>), grid, dim3(kThreads), 0, stream, p, hpw);
+    } else {
+      hipLaunchKernelGGL((prefill_dma_kernel<D, CT, false>), grid, dim3(kThreads), 0, stream, p, hpw);
+    }
   } else {
-    hipLaunchKernelGGL((prefill_kernel<D, CT, KVB>), grid, dim3(kThreads), 0, stream, p, hpw);
+    if (p.masked) {
+      hipLaunchKernelGGL((prefill_kernel<D, CT, KVB, true>), grid, dim3(kThreads), 0, stream, p, hpw);
+    } else {
+      hipLaunchKernelGGL((prefill_kernel<D, CT, KVB, false>), grid, dim3(kThreads), 0, stream, p, hpw);
+    }
   }
   return hipGetLastError();
 }

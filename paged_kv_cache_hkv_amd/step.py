@@ -19,7 +19,8 @@ _ACT = {torch.float16: B.PA_F16, torch.bfloat16: B.PA_BF16}
 
 
 class PagedAttentionStep:
-    def __init__(self, wl, tensors, decode_workers=0, qsl_len=None):
+    def __init__(self, wl, tensors, decode_workers=0, qsl_len=None, sliding_window=0,
+                 alibi_slopes=None):
         self.wl = wl
         self.t = tensors
         dev = tensors.q.device
@@ -27,7 +28,8 @@ class PagedAttentionStep:
         cache = B.PA_FP8_E4M3 if wl.cache_fp8 else act
         self.desc = B.make_desc(wl.num_q_heads, wl.num_kv_heads, wl.head_dim, wl.block_size,
                                 act, cache, k_scale=tensors.k_scale, v_scale=tensors.v_scale,
-                                decode_workers=decode_workers)
+                                decode_workers=decode_workers, sliding_window=sliding_window,
+                                alibi_slopes=alibi_slopes)
         R = wl.num_reqs
         self.T_pad = tensors.q.shape[0]
         self.qsl = torch.empty(qsl_len or (R + 1), dtype=torch.int32, device=dev)

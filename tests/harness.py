@@ -60,7 +60,8 @@ class Snapshot:
         self.vbits = cache_bits(tensors.value_cache.index_select(0, idx), fp8)
 
 
-def oracle_outputs(wl, tensors, snapshot, requests, qsl_len=None):
+def oracle_outputs(wl, tensors, snapshot, requests, qsl_len=None, sliding_window=0,
+                   alibi_slopes=None):
     """Oracle rows {r: float64 [n_r, Hq, D]} for the given requests.
 
     Metadata and the scatter of the step's new K/V are the oracle's own; the
@@ -95,7 +96,8 @@ def oracle_outputs(wl, tensors, snapshot, requests, qsl_len=None):
             rows.append([])
     return OA.paged_attention(q, kc, vc, rows, qsl, seq_lens, bs, requests=requests,
                               cache_dtype=cache_dt, k_scale=tensors.k_scale,
-                              v_scale=tensors.v_scale)
+                              v_scale=tensors.v_scale, sliding_window=sliding_window,
+                              alibi_slopes=alibi_slopes)
 
 
 def gpu_rows(out, qsl, r):
