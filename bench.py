@@ -19,8 +19,9 @@ Also reported on the same JSON line:
 * ``extra``: the other measured workloads (GQA decode, chunked-prefill mix,
   long-context fp8 MQA decode), each call timed with events after a 1 GiB
   cache-evicting read; besides attention and the cache write this times the
-  fused RoPE + cache write (rotary_dim = head_dim, half-split pairs) and, on
-  the GQA pool, the block copy / swap out / swap in of 4096 blocks.
+  fused RoPE + cache write (rotary_dim = head_dim, half-split pairs), on the
+  GQA pool the block copy / swap out / swap in of 4096 blocks, and on the GQA
+  and mixed batches attention with a 1024-key sliding window and ALiBi.
 """
 
 import argparse
@@ -59,6 +60,57 @@ def prefill_flops(wl, reqs):
         c = int(wl.num_computed[r])
         tot += 4 * wl.num_q_heads * wl.head_dim * (n * c + n * (n + 1) // 2)
     return tot
+
+
+def window_kv_bytes(wl, reqs, window):
+    """KV bytes a decode must read under a sliding window: the last min(s, W) keys."""
+    e = 1 if wl.cache_fp8 else 2
+    s = np.minimum(wl.seq_lens_host[list(reqs)].astype(np.int64), window)
+    return int(s.sum()) * wl.num_kv_heads * wl.head_dim * 2 * e
+
+
+def window_prefill_flops(wl, reqs, window):
+    """Prefill flops over the pairs a sliding window leaves: query at position p
+    sees min(p + 1, W) keys."""
+    tot = 0
+    for r in reqs:
+        n, c = int(wl.query_lens[r]), int(wl.num_computed[r])
+        seen = np.minimum(np.arange(c, c + n, dtype=np.int64) + 1, window)
+        tot += 4 * wl.num_q_heads * wl.head_dim * int(seen.sum())
+    return tot
+
+
+def bench_masks(wl, t, iters, flush, window=1024):
+    """Decode / prefill with a sliding window and ALiBi slopes on the same batch."""
+    h = wl.num_q_heads
+    sl = torch.tensor([2.0 ** (-8.0 * (i + 1) / h) for i in range(h)], dtype=torch.float32,
+                      device="cuda")
+    st = PagedAttentionStep(wl, t, sliding_window=window, alibi_slopes=sl)
+    st.metadata()
+    fns, names = [], []
+    if wl.num_decodes:
+        fns.append(st.decode)
+        names.append("decode")
+    if wl.num_reqs > wl.num_decodes:
+        fns.append(st.prefill)
+        names.append("prefill")
+    for f in fns:
+        f()
+    rec = {"sliding_window": window, "alibi": True}
+    for nm, (med, p10, p90) in zip(names, time_calls(fns, iters, flush)):
+        rec[f"{nm}_ms"] = round(med, 4)
+    if wl.num_decodes:
+        kb = window_kv_bytes(wl, range(wl.num_decodes), window)
+        rec["decode_kv_bytes"] = kb
+        rec["decode_kv_GBps"] = round(kb / (rec["decode_ms"] * 1e-3) / 1e9, 1)
+        rec["decode_hbm_frac"] = round(kb / (rec["decode_ms"] * 1e-3) / 1e9 / HBM_PEAK_GBS, 4)
+    if wl.num_reqs > wl.num_decodes:
+        fl = window_prefill_flops(wl, range(wl.num_decodes, wl.num_reqs), window)
+        rec["prefill_flops"] = fl
+        rec["prefill_TFLOPs"] = round(fl / (rec["prefill_ms"] * 1e-3) / 1e12, 1)
+        rec["prefill_mfma_frac"] = round(fl / (rec["prefill_ms"] * 1e-3) / 1e12 / BF16_PEAK_TFLOPS, 4)
+    del st
+    return rec
 
 
 def src_sha(path):
@@ -148,6 +200,8 @@ def bench_extra(name, iters, flush):
         rec["prefill_mfma_frac"] = round(fl / sec / 1e12 / BF16_PEAK_TFLOPS, 4)
     if name == "decode_gqa":
         rec["copy_blocks"] = bench_blocks(wl, t, st.desc, iters, flush)
+    if name in ("decode_gqa", "chunked_prefill_mix"):
+        rec["window_alibi"] = bench_masks(wl, t, iters, flush)
     del st, t
     torch.cuda.empty_cache()
     return rec
