@@ -58,6 +58,11 @@ template <> struct Mfma<__bf16> {
   __device__ static inline unsigned short from_float(float f) {
     return __builtin_bit_cast(unsigned short, (__bf16)f);
   }
+  // acc + lo + hi of a dword holding two bf16 values (v_dot2c_f32_bf16 by ones)
+  __device__ static inline float sum2(unsigned pk, float acc) {
+    const bf16x2 one = {(__bf16)1.0f, (__bf16)1.0f};
+    return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, pk), one, acc, false);
+  }
   __device__ static inline float to_float(unsigned short b) {
     return __builtin_bit_cast(float, ((unsigned)b) << 16);
   }
@@ -82,6 +87,10 @@ template <> struct Mfma<_Float16> {
   }
   __device__ static inline unsigned short from_float(float f) {
     return __builtin_bit_cast(unsigned short, (_Float16)f);
+  }
+  __device__ static inline float sum2(unsigned pk, float acc) {
+    const f16x2 one = {(_Float16)1.0f, (_Float16)1.0f};
+    return __builtin_amdgcn_fdot2(__builtin_bit_cast(f16x2, pk), one, acc, false);
   }
   __device__ static inline float to_float(unsigned short b) {
     return (float)__builtin_bit_cast(_Float16, b);
@@ -119,6 +128,20 @@ __device__ inline float shfl_xor(float v, int mask) {
 // max / sum of a value over lanes l and l ^ 32.
 __device__ inline float pair32_max(float v) { return fmaxf(v, shfl_xor(v, 32)); }
 __device__ inline float pair32_sum(float v) { return v + shfl_xor(v, 32); }
+// The same with v_permlane32_swap (gfx950): no LDS round trip.  With both
+// operands equal, the two results hold the low and the high half of the wave
+// broadcast over both halves, so combining them gives every lane the value of
+// its pair, bit-identical in both lanes.
+__device__ inline float pair32_max_swap(float v) {
+  const unsigned u = __builtin_bit_cast(unsigned, v);
+  const auto r = __builtin_amdgcn_permlane32_swap(u, u, false, false);
+  return fmaxf(__builtin_bit_cast(float, (unsigned)r[0]), __builtin_bit_cast(float, (unsigned)r[1]));
+}
+__device__ inline float pair32_sum_swap(float v) {
+  const unsigned u = __builtin_bit_cast(unsigned, v);
+  const auto r = __builtin_amdgcn_permlane32_swap(u, u, false, false);
+  return __builtin_bit_cast(float, (unsigned)r[0]) + __builtin_bit_cast(float, (unsigned)r[1]);
+}
 
 __device__ inline int wave_uniform(int v) { return __builtin_amdgcn_readfirstlane(v); }
 
@@ -150,9 +173,20 @@ __device__ inline unsigned lds_offset(const void* p) {
 // stay safe: transfers it does not count only make its counted waits stricter.
 // NT: non-temporal (data read once, e.g. a K/V stream): measurably higher
 // HBM throughput for streams that are not re-read.
-template <bool NT = false>
+// WAIT_LDS = false drops the leading lgkmcnt wait, for callers whose own
+// barriers already order the copy after every read of the buffer's previous
+// contents (scalar loads in flight are then not waited for either).
+template <bool NT = false, bool WAIT_LDS = true>
 __device__ inline void lds_dma16(const void* base, unsigned voff, unsigned m0) {
-  if constexpr (NT) {
+  if constexpr (!WAIT_LDS) {
+    asm volatile(
+        "s_mov_b32 m0, %2\n\t"
+        "s_nop 0\n\t"
+        "global_load_lds_dwordx4 %0, %1"
+        :
+        : "v"(voff), "s"(base), "s"(m0)
+        : "memory");
+  } else if constexpr (NT) {
     asm volatile(
         "s_waitcnt lgkmcnt(0)\n\t"
         "s_mov_b32 m0, %2\n\t"

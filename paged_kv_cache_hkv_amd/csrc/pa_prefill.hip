@@ -10,18 +10,21 @@
 // tile in registers and LDS ("vLLM 推理全流程深度解析", FlashAttention keeps
 // softmax and matmul in on-chip memory and never writes the score matrix out).
 //
-// Work decomposition.  A workgroup of 4 waves owns (request, group of `hpw`
-// query heads sharing one K/V head, tile of 128/hpw queries); wave w takes
-// query head w % hpw and 32 queries.  Tiles are numbered from the END of each
-// request and dispatched in that order, so the tiles with the most keys start
-// first (longest-first scheduling over uneven chunks).  All 4 waves share each
-// 64-key K/V tile, double-buffered in LDS (one barrier per tile):
-//   * Ks[key][d] row-major, rows padded by 16 bytes: the 16-byte reads of 32
-//     different rows hit distinct banks;
-//   * Vt[d][key'] transposed, key' = key with bits 2 and 3 swapped, so the 8
-//     keys one lane feeds into one MFMA step are adjacent (one 16-byte read).
-//     Each thread moves 4 consecutive keys x 8 d and writes 8-byte rows, so
-//     the transposing stores are free of bank conflicts too.
+// Work decomposition.  A workgroup owns (request, group of `hpw` query heads
+// sharing one K/V head, tile of queries); each wave takes one query head and
+// 32 queries.  Tiles are numbered from the END of each request and dispatched
+// in that order, so the tiles with the most keys start first (longest-first
+// scheduling over uneven chunks).  All waves of a workgroup share each 64-key
+// K/V tile in LDS.  Two kernels:
+//   * 16-bit caches (prefill_pp_kernel): 8 waves, 256/hpw queries, K/V tiles
+//     copied global -> LDS by DMA into 4-stage rings, and two groups of 4
+//     waves alternating between the MFMA phase and the softmax phase (see
+//     the kernel's own comment);
+//   * fp8 caches (prefill_kernel): 4 waves, 128/hpw queries, tiles staged
+//     through registers and widened to bf16/fp16 when written to LDS
+//     (double-buffered, one barrier per tile): K row-major with padded rows,
+//     V transposed (key bits 2 and 3 swapped so the 8 keys one lane feeds
+//     into one MFMA step are adjacent).
 // Per tile a wave computes S^T = K . Q^T (v_mfma_f32_32x32x16, keys x queries)
 // so each lane holds 32 scores of ONE query: the row max needs one exchange
 // with the lane 32 apart and every rescale is lane-local.  The probabilities,
@@ -29,15 +32,15 @@
 // Softmax in exp2 form with the scale folded into one FMA; the accumulator is
 // only rescaled when a row's running max grows by more than 2^8 (exact up to
 // rounding: the reference max of a softmax is arbitrary as long as nothing
-// overflows).  The next tile's global loads are issued before the current
-// tile's math and land in the other LDS buffer after it.
-// fp8 caches are widened to bf16/fp16 when the tile is written to LDS.
+// overflows).
 // Mask variants (MASK instantiations; the alibi_slopes and window_size
 // arguments of the same call): a sliding window starts the key loop at the
 // first tile any query of the workgroup may see and skips a wave's math on
 // tiles wholly before its queries' windows; ALiBi adds slope * (key - query
 // position) to each score, applied together with the window mask when the
 // scores are moved to log2 units (window_alibi).
+#include <type_traits>
+
 #include "pa_device.h"
 #include "pa_kernels.h"
 
@@ -406,9 +409,9 @@ __global__ __launch_bounds__(kThreads, 2) void prefill_kernel(AttnParams p, int 
 }
 
 // ---------------------------------------------------------------------------
-// 16-bit caches: the same math, with the K/V tiles moved global -> LDS by the
-// DMA path (global_load_lds, 16 bytes per lane, no registers or address math
-// in the loop) and V read back transposed with ds_read_b64_tr_b16.
+// 16-bit caches: K/V tiles are moved global -> LDS by the DMA path
+// (global_load_lds, 16 bytes per lane, no registers) and V is read back
+// transposed with ds_read_b64_tr_b16.
 //
 // LDS layout: per tile, K and V are each [64 keys][D/8 16-byte chunks] with
 // the chunks of key k stored at position (chunk ^ sw(k)); one DMA wave
@@ -432,7 +435,6 @@ struct LdsTile {
   static constexpr int CPR = D / 8;                 // 16-byte chunks per key row
   static constexpr int kPos = kTileK * CPR;         // 16-byte positions per tile (K or V)
   static constexpr int kInst = kPos / 64;           // DMA wave instructions per tile (K or V)
-  static constexpr int kInstPerWave = kInst / kWaves;
   __device__ static inline int swk(int key) { return D == 128 ? (key & 15) : ((key >> 1) & 7); }
   __device__ static inline int swv(int key) { return D == 128 ? 4 * (key & 3) : 4 * ((key >> 1) & 1); }
 };
@@ -447,71 +449,79 @@ __device__ inline u32x2 lds_read_tr16(const u32x4* base, int pos16, int byte_off
   return __builtin_bit_cast(u32x2, __builtin_amdgcn_ds_read_tr16_b64_v4bf16(lp));
 }
 
-// Issue the DMA of tile kt into (Kl, Vl).  Each wave issues kInstPerWave
-// instructions per tensor; instruction `inst` covers positions inst*64 ..
-// inst*64+63, i.e. 64/CPR consecutive keys of one cache block.
-template <int D>
-__device__ inline void dma_tile(const TileCtx& c, int kt, u32x4* Kl, u32x4* Vl, int wave, int lane) {
-  using L = LdsTile<D>;
-  constexpr int kKeysPerInst = 64 / L::CPR;   // consecutive keys of one cache block
-#pragma unroll
-  for (int i = 0; i < L::kInstPerWave; ++i) {
-    const int inst = i * kWaves + wave;
-    const int p = inst * 64 + lane;
-    const int key = p / L::CPR;
-    const int pos = p % L::CPR;
-    const int gkey = kt * kTileK + key;
-    // the instruction's block, from uniform values only (a scalar table read)
-    const int id = block_id(c, (kt * kTileK + inst * kKeysPerInst) / kBlock);
-    const bool ok = id >= 0 && gkey < c.s_eff;
-    const int64_t row = (int64_t)id * c.blk_stride + (int64_t)(gkey % kBlock) * c.tok_stride +
-                        c.head_off;
-    const int64_t koff = ok ? row + (int64_t)((pos ^ L::swk(key)) * 16) : 0;
-    const int64_t voff = ok ? row + (int64_t)((pos ^ L::swv(key)) * 16) : 0;
-    __builtin_amdgcn_global_load_lds(c.kc + koff, (lds_void*)(Kl + inst * 64), 16, 0, 0);
-    __builtin_amdgcn_global_load_lds(c.vc + voff, (lds_void*)(Vl + inst * 64), 16, 0, 0);
-  }
+// ---------------------------------------------------------------------------
+// 16-bit caches: eight waves in two groups of four (one wave of each group on
+// every SIMD) that alternate between a matrix phase and a softmax phase, so
+// the MFMAs of one group run while the other group computes its softmax.
+//
+// Per wave and 64-key tile j the work splits into
+//   M(j): S_j = K_j . Q^T and O^T += V_{j-1}^T . P_{j-1}^T (MFMA, LDS reads)
+//   V(j): P_j from S_j (mask, row max, lazy rescale, exp2, bf16/fp16 pack,
+//         row sum), then the copies of K tile j+3 and V tile j+2 are issued
+// and every wave runs M(j), barrier, V(j), barrier.  Group B passes one extra
+// barrier before its loop (group A one after it), so between two consecutive
+// barriers one group is in M and the other in V.
+// K and V tiles live in two rings of four LDS stages (tile t in stage
+// (t - first tile) % 4) with the LdsTile layout above, filled by global -> LDS
+// copies issued from inline assembly (untracked by the compiler) and retired
+// by explicit vmcnt waits: a copy issued in V(j) is waited for at the end of
+// M(j+2), and the barrier after that wait publishes it.  Stage reuse: K tile
+// t+4 is issued in V(t+1), after every wave has passed M(t), the last read of
+// K tile t; V tile t+4 in V(t+2), after every M(t+1).  Each wave copies the
+// rows of one block of every tile, so it needs one table entry per tile: a
+// scalar load issued one V phase ahead of its use (no vector load the
+// compiler would wait for behind the copies in flight).  The workgroup checks
+// its table entries once up front; only rows holding ids outside the pool
+// test block presence per tile.
+constexpr int kPPWaves = 8;
+constexpr int kPPThreads = 64 * kPPWaves;
+constexpr int kPPStages = 4;
+
+// Workgroup barrier that leaves the copies in flight: only this wave's LDS
+// operations (and scalar loads) are waited for when `lds` is set.
+template <bool LDS>
+__device__ inline void barrier_nowait() {
+  if constexpr (LDS) asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+  __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");
 }
 
-// After this wave's DMA of tile kt has landed (s_waitcnt by the caller): zero
-// the V positions of keys the tile lacks.  Each lane clears exactly the
-// positions its own DMA instructions wrote, so no other wave's transfer can
-// land on a cleared position afterwards.
-template <int D>
-__device__ inline void fix_tile(const TileCtx& c, int kt, u32x4* Vl, int wave, int lane) {
-  using L = LdsTile<D>;
-  const int key0 = kt * kTileK;
-  const unsigned okmask = tile_okmask(c, kt);
-  if (key0 + kTileK <= c.s_eff && okmask == 0xFu) return;   // full tile: nothing to do
+// Present blocks of key tile t as a 4-bit mask (block b present: inside the
+// sequence's blocks and a pool id).  Only rows holding entries outside the
+// pool take this path; all other tiles have every block present.
+__device__ inline unsigned tile_okmask(const int32_t* bt_row, int nblk, int nb32, int t) {
+  unsigned ok = 0;
 #pragma unroll
-  for (int i = 0; i < L::kInstPerWave; ++i) {
-    const int p = (i * kWaves + wave) * 64 + lane;
-    const int key = p / L::CPR;
-    if (key0 + key >= c.s_eff || !((okmask >> (key / kBlock)) & 1u)) Vl[p] = u32x4{0u, 0u, 0u, 0u};
+  for (int b = 0; b < 4; ++b) {
+    const int id = load_uniform(bt_row, min(4 * t + b, nblk - 1));
+    ok |= ((4 * t + b < nblk) & (id >= 0) & (id < nb32)) ? (1u << b) : 0u;
   }
+  return ok;
 }
 
 template <int D, typename CT, bool MASK>
-__global__ __launch_bounds__(kThreads, 2) void prefill_dma_kernel(AttnParams p, int hpw) {
+__global__ __launch_bounds__(kPPThreads) void prefill_pp_kernel(AttnParams p, int hpw) {
   using M = Mfma<CT>;
   using vec8 = typename M::vec8;
   using L = LdsTile<D>;
-  constexpr int QS = D / 16;      // QK MFMA steps (16 d each)
-  constexpr int DT = D / 32;      // 32-row d tiles of O^T
+  constexpr int QS = D / 16;                 // QK MFMA steps (16 d each)
+  constexpr int DT = D / 32;                 // 32-row d tiles of O^T
+  constexpr int NS = kPPStages;
+  constexpr int IPW = L::kInst / kPPWaves;   // copy instructions per wave per tile (K and V each)
+  constexpr int KPI = 64 / L::CPR;           // keys per copy instruction
+  constexpr int PPS = 4 * DT / QS;           // PV MFMAs per QK step
+  static_assert(IPW * kPPWaves == L::kInst && PPS * QS == 4 * DT, "tile shape");
+  static_assert(2 * IPW * KPI == kBlock, "two waves copy each block of a tile");
+  constexpr unsigned kTileBytes = L::kPos * 16;
 
-  // Double buffer as four distinct arrays, named by constants only: the
-  // compiler then knows a read of the current tile cannot alias the DMA of the
-  // next one and does not make the read wait for that transfer.
-  __shared__ u32x4 K0[L::kPos];
-  __shared__ u32x4 V0[L::kPos];
-  __shared__ u32x4 K1[L::kPos];
-  __shared__ u32x4 V1[L::kPos];
+  __shared__ u32x4 Kr[NS * L::kPos];
+  __shared__ u32x4 Vr[NS * L::kPos];
 
   const int r = p.req_begin + blockIdx.y;
   const int q_first = p.qsl[r];
   const int n = p.qsl[r + 1] - q_first;
-  const int QB = 128 / hpw;
-  const int q_hi = n - (int)blockIdx.z * QB;      // tile j covers queries [q_hi - QB, q_hi)
+  const int QB = (32 * kPPWaves) / hpw;
+  const int q_hi = n - (int)blockIdx.z * QB;      // tile z covers queries [q_hi - QB, q_hi)
   if (q_hi <= 0) return;
   const int G = p.group;
   const int s_all = p.seq_lens[r];
@@ -524,39 +534,99 @@ __global__ __launch_bounds__(kThreads, 2) void prefill_dma_kernel(AttnParams p, 
 
   const int lane = threadIdx.x & 63;
   const int wave = wave_uniform(threadIdx.x >> 6);
+  const int grp = wave >> 2;
   const int half = lane >> 5;
   const int l32 = lane & 31;
   const int qh = blockIdx.x * hpw + (wave % hpw);
   const int kvh = qh / G;
-  const int wq0 = q_hi - QB + (wave / hpw) * 32;
-  const int qi = wq0 + l32;
+  const int wq0 = q_hi - QB + (wave / hpw) * 32;   // first query of the wave (may be < 0)
+  const int qi = wq0 + l32;                        // this lane's query
   const bool q_ok = qi >= 0;
   const int qpos = c + qi;
+  const int wave_first_pos = c + wq0;
+  const int wave_last_pos = c + wq0 + 31;
 
+  // Q as the B operand of S^T = K . Q^T: B[k = 8*half + e][col = l32] = Q[qi][16 s + 8 half + e]
   vec8 qop[QS];
   {
     const CT* qrow = static_cast<const CT*>(p.q) + (int64_t)(q_first + (q_ok ? qi : 0)) * p.q_row_stride +
                      (int64_t)qh * D;
 #pragma unroll
-    for (int s = 0; s < QS; ++s) {
+    for (int s = 0; s < QS; ++s)
       qop[s] = q_ok ? __builtin_bit_cast(vec8, ld16(qrow + 16 * s + 8 * half))
                     : __builtin_bit_cast(vec8, u32x4{0u, 0u, 0u, 0u});
-    }
+    // consume Q here, so the compiler retires these loads before the loop: a
+    // wait it placed inside the loop would also wait for every copy in flight
+#pragma unroll
+    for (int s = 0; s < QS; ++s) asm volatile("" : : "v"(__builtin_bit_cast(u32x4, qop[s])));
   }
 
-  TileCtx tc;
-  tc.kc = static_cast<const unsigned char*>(p.key_cache);
-  tc.vc = static_cast<const unsigned char*>(p.value_cache);
-  tc.bt_row = p.block_tables + (int64_t)r * p.max_blocks_per_req;
-  tc.tok_stride = (int64_t)p.num_kv_heads * D * 2;
-  tc.blk_stride = tc.tok_stride * kBlock;
-  tc.head_off = (int64_t)kvh * D * 2;
-  tc.num_blocks = p.num_blocks;
-  tc.s_eff = s_eff;
-  tc.nblk = (s_eff + kBlock - 1) / kBlock;
+  const int32_t* bt_row = p.block_tables + (int64_t)r * p.max_blocks_per_req;
+  const int nblk = (s_eff + kBlock - 1) / kBlock;
+  const int nb32 = (int)min(p.num_blocks, (int64_t)0x7FFFFFFF);
+  const int64_t tok_stride = (int64_t)p.num_kv_heads * D * 2;
+  const int64_t blk_stride = tok_stride * kBlock;
+  const unsigned char* kbase = static_cast<const unsigned char*>(p.key_cache) + (int64_t)kvh * D * 2;
+  const unsigned char* vbase = static_cast<const unsigned char*>(p.value_cache) + (int64_t)kvh * D * 2;
+
+  // One pass over the table entries the workgroup's tiles use: when all of
+  // them are pool ids (the normal case) every block of every tile is present,
+  // and keys past the sequence are handled by the length tests alone.
+  bool my_ok = true;
+  for (int b = 4 * kt0 + (int)threadIdx.x; b < nblk; b += kPPThreads) {
+    const int id = bt_row[b];
+    my_ok &= (id >= 0) & (id < nb32);
+  }
+  const bool rowok = __syncthreads_and(my_ok);
+  auto okmask = [&](int t) __attribute__((always_inline)) {
+    return rowok ? 0xFu : tile_okmask(bt_row, nblk, nb32, t);
+  };
+
+  // copy roles (tile-invariant): instruction i of this wave fills positions
+  // inst*64 .. inst*64+63 of a tile, inst = wave*IPW + i: keys of block
+  // wave/2 of the tile only, so a wave needs one block id per tile
+  const int cb = wave >> 1;
+  unsigned koff[IPW], voff[IPW];
+#pragma unroll
+  for (int i = 0; i < IPW; ++i) {
+    const int pidx = (wave * IPW + i) * 64 + lane;
+    const int key = pidx / L::CPR, pos = pidx % L::CPR;
+    const unsigned row = (unsigned)((key % kBlock) * tok_stride);
+    koff[i] = row + (unsigned)((pos ^ L::swk(key)) * 16);
+    voff[i] = row + (unsigned)((pos ^ L::swv(key)) * 16);
+  }
+  const unsigned kr0 = lds_offset(Kr), vr0 = lds_offset(Vr);
+  // this wave's table entry for tile t (index clamped into the sequence), and
+  // the id its copies use (absent -> block 0: masked keys, zeroed V rows)
+  auto raw_id = [&](int t) __attribute__((always_inline)) {
+    return load_uniform(bt_row, min(4 * t + cb, nblk - 1));
+  };
+  auto copy_id = [&](int raw, int t) __attribute__((always_inline)) {
+    return ((4 * t + cb < nblk) & (raw >= 0) & (raw < nb32)) ? raw : 0;
+  };
+  auto copy_tile = [&](const unsigned char* base, const unsigned (&off)[IPW], int id,
+                       unsigned lds0) __attribute__((always_inline)) {
+    const unsigned char* src = base + (int64_t)id * blk_stride;
+#pragma unroll
+    for (int i = 0; i < IPW; ++i)
+      lds_dma16<false, false>(src, off[i], lds0 + (unsigned)(wave * IPW + i) * 1024u);
+  };
+  // after the copy of V tile t has landed: zero the rows of keys the tile
+  // lacks (past the sequence, absent blocks), each lane exactly the positions
+  // its own copies wrote
+  auto fix_v = [&](int t, u32x4* Vs) __attribute__((always_inline)) {
+    if (kTileK * t + kTileK <= s_eff && rowok) return;
+    const unsigned ok = okmask(t);
+#pragma unroll
+    for (int i = 0; i < IPW; ++i) {
+      const int pidx = (wave * IPW + i) * 64 + lane;
+      const int key = pidx / L::CPR;
+      if (kTileK * t + key >= s_eff || !((ok >> (key / kBlock)) & 1u)) Vs[pidx] = u32x4{0u, 0u, 0u, 0u};
+    }
+  };
 
   // lane roles in the LDS reads (tile-invariant)
-  const int kswz = L::swk(l32);                  // key 32u + l32 has the swizzle of l32
+  const int kswz = L::swk(l32);                   // key 32u + l32 has the swizzle of l32
   const int g16 = lane >> 4;                      // 16-lane group
   const int ta = (lane & 15) >> 2, tb = lane & 3; // transposed-read row supplier (key a, d 4b)
   const int vswz = L::swv(ta);                    // keys ... + 4h + a share a's swizzle
@@ -569,106 +639,185 @@ __global__ __launch_bounds__(kThreads, 2) void prefill_dma_kernel(AttnParams p, 
 #pragma unroll
   for (int t = 0; t < DT; ++t) acc[t] = f32x16{};
   float m_used = -INFINITY, l_run = 0.f;
-  const int wave_first_pos = c + wq0;
-  const int wave_last_pos = c + wq0 + 31;
+  f32x16 sc[2];
+  u32x4 pk[4];    // P of the previous tile, two 16-bit values per dword: pk[2u + v] feeds PV step (u, v)
+#pragma unroll
+  for (int i = 0; i < 4; ++i) pk[i] = u32x4{0u, 0u, 0u, 0u};
 
-  if (ntiles > kt0) {
-    dma_tile<D>(tc, kt0, K0, V0, wave, lane);
-    __builtin_amdgcn_s_waitcnt(0);
-    fix_tile<D>(tc, kt0, V0, wave, lane);
-  }
-  // Q (and tile 0) resident on every path into the loop, so the loop's first
-  // MFMA never waits on the vector-memory counter while later DMAs are in flight
-  __builtin_amdgcn_s_waitcnt(0);
-  __syncthreads();
-  // one tile: start the next tile's DMA into (Kn, Vn), compute from (K, V)
-  auto tile_step = [&](int kt, const u32x4* K, const u32x4* V, u32x4* Kn, u32x4* Vn) {
-    if (kt + 1 < ntiles) dma_tile<D>(tc, kt + 1, Kn, Vn, wave, lane);
-    const int k0 = kt * kTileK;
-    if (k0 <= wave_last_pos && (!MASK || k0 + kTileK - 1 >= wave_first_pos - p.window_left)) {
-      // two independent accumulation chains (the 32-key subtiles), interleaved
-      f32x16 sc[2] = {f32x16{}, f32x16{}};
+  auto active = [&](int t) __attribute__((always_inline)) {
+    const int k0 = t * kTileK;
+    return k0 <= wave_last_pos && (!MASK || k0 + kTileK - 1 >= wave_first_pos - p.window_left);
+  };
+
+  // M phase: S_j (QK) and O += V_{j-1} P_{j-1} (PV), the two MFMA chains interleaved
+  auto mphase = [&](const u32x4* Kt, const u32x4* Vt) __attribute__((always_inline)) {
+    sc[0] = f32x16{};
+    sc[1] = f32x16{};
 #pragma unroll
-      for (int s = 0; s < QS; ++s) {
-#pragma unroll
-        for (int u = 0; u < 2; ++u) {
-          const vec8 kop = __builtin_bit_cast(vec8, K[(32 * u + l32) * L::CPR + ((2 * s + half) ^ kswz)]);
-          sc[u] = M::mma32(kop, qop[s], sc[u]);
-        }
-      }
-      const unsigned okmask = tile_okmask(tc, kt);
-      if (k0 + kTileK - 1 > wave_first_pos || k0 + kTileK > s_eff || okmask != 0xFu) {
-#pragma unroll
-        for (int u = 0; u < 2; ++u)
-#pragma unroll
-          for (int g = 0; g < 16; ++g) {
-            const int key = k0 + 32 * u + 8 * (g / 4) + 4 * half + (g % 4);
-            const bool blk = (okmask >> (2 * u + (g >= 8 ? 1 : 0))) & 1u;
-            sc[u][g] = (key > qpos || key >= s_eff || !blk) ? -INFINITY : sc[u][g];
-          }
-      }
-      if constexpr (MASK) window_alibi(sc, k0, half, qpos, p.window_left, p.scale_log2, slope2);
-      float mx = -INFINITY;
-#pragma unroll
-      for (int u = 0; u < 2; ++u)
-#pragma unroll
-        for (int g = 0; g < 16; ++g) mx = fmaxf(mx, sc[u][g]);
-      mx = pair32_max(mx);
-      const bool grow = (m_used == -INFINITY) ? (mx > -INFINITY) : ((mx - m_used) * c2 > kRescaleLog2);
-      if (__ballot(grow)) {
-        const float m_new = grow ? mx : m_used;
-        const float alpha = (m_used == -INFINITY) ? 0.f : fast_exp2((m_used - m_new) * c2);
-        l_run *= alpha;
-#pragma unroll
-        for (int t = 0; t < DT; ++t) acc[t] *= alpha;
-        m_used = m_new;
-      }
-      const float mref = (m_used == -INFINITY) ? 0.f : m_used * c2;
-      float psum = 0.f;
-#pragma unroll
-      for (int u = 0; u < 2; ++u)
-#pragma unroll
-        for (int g = 0; g < 16; ++g) {
-          const float e = fast_exp2(__builtin_fmaf(sc[u][g], c2, -mref));
-          sc[u][g] = e;
-          psum += e;
-        }
-      l_run += psum;
+    for (int s = 0; s < QS; ++s) {
 #pragma unroll
       for (int u = 0; u < 2; ++u) {
+        const vec8 kop = __builtin_bit_cast(vec8, Kt[(32 * u + l32) * L::CPR + ((2 * s + half) ^ kswz)]);
+        sc[u] = M::mma32(kop, qop[s], sc[u]);
+      }
 #pragma unroll
-        for (int v = 0; v < 2; ++v) {
-          const u32x4 pw{pack2<CT>(sc[u][8 * v + 0], sc[u][8 * v + 1]),
-                         pack2<CT>(sc[u][8 * v + 2], sc[u][8 * v + 3]),
-                         pack2<CT>(sc[u][8 * v + 4], sc[u][8 * v + 5]),
-                         pack2<CT>(sc[u][8 * v + 6], sc[u][8 * v + 7])};
-          const vec8 pop = __builtin_bit_cast(vec8, pw);
-          // keys of this step: 32u + 16v + 8r + 4h + a (h = lane/32), element e = 4r + a
-          const int key_r0 = 32 * u + 16 * v + 4 * half + ta;
-#pragma unroll
-          for (int t = 0; t < DT; ++t) {
-            const int chunk = 4 * t + 2 * (g16 & 1) + (tb >> 1);
-            const int byte_off = 8 * (tb & 1);
-            const u32x2 lo = lds_read_tr16(V, key_r0 * L::CPR + (chunk ^ vswz), byte_off);
-            const u32x2 hi = lds_read_tr16(V, (key_r0 + 8) * L::CPR + (chunk ^ vswz), byte_off);
-            const vec8 vop = __builtin_bit_cast(vec8, u32x4{lo[0], lo[1], hi[0], hi[1]});
-            acc[t] = M::mma32(vop, pop, acc[t]);
-          }
-        }
+      for (int e = 0; e < PPS; ++e) {
+        const int pv = s * PPS + e;
+        const int uv = pv / DT, t = pv % DT;
+        // keys of this step: 32u + 16v + 8r + 4h + a (h = lane/32), element e = 4r + a
+        const int key_r0 = 32 * (uv >> 1) + 16 * (uv & 1) + 4 * half + ta;
+        const int chunk = 4 * t + 2 * (g16 & 1) + (tb >> 1);
+        const int byte_off = 8 * (tb & 1);
+        const u32x2 lo = lds_read_tr16(Vt, key_r0 * L::CPR + (chunk ^ vswz), byte_off);
+        const u32x2 hi = lds_read_tr16(Vt, (key_r0 + 8) * L::CPR + (chunk ^ vswz), byte_off);
+        const vec8 vop = __builtin_bit_cast(vec8, u32x4{lo[0], lo[1], hi[0], hi[1]});
+        acc[t] = M::mma32(vop, __builtin_bit_cast(vec8, pk[uv]), acc[t]);
       }
     }
-    // unconditional, so the compiler sees no transfer pending past this point
-    // on any path and does not make the next tile's reads wait for later DMAs
-    __builtin_amdgcn_s_waitcnt(0);
-    if (kt + 1 < ntiles) fix_tile<D>(tc, kt + 1, Vn, wave, lane);
-    __syncthreads();
+    // issue order: LDS reads run ahead of the MFMAs that consume them
+    constexpr int kReads = 2 * QS + 8 * DT;
+    constexpr int kMfma = 2 * QS + 4 * DT;
+    constexpr int kLead = 6;
+    constexpr int kPer = (kReads - kLead + kMfma - 1) / kMfma;
+    __builtin_amdgcn_sched_group_barrier(0x100, kLead, 0);
+#pragma unroll
+    for (int i = 0; i < kMfma; ++i) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+      __builtin_amdgcn_sched_group_barrier(0x100, kPer, 0);
+    }
   };
-  for (int kt = kt0; kt < ntiles; kt += 2) {
-    tile_step(kt, K0, V0, K1, V1);
-    if (kt + 1 < ntiles) tile_step(kt + 1, K1, V1, K0, V0);
+
+  // V phase softmax of tile j: scores in sc -> probabilities in pk, row sums in l_run
+  auto softmax = [&](int j) __attribute__((always_inline)) {
+    const int k0 = j * kTileK;
+    if (k0 + kTileK - 1 > wave_first_pos || k0 + kTileK > s_eff) {
+      // element g of subtile u is key k0 + 4 half + (32u + 8(g/4) + g%4):
+      // masked past the query's position and past the sequence
+      const int lim = min(qpos, s_eff - 1) - (k0 + 4 * half);
+#pragma unroll
+      for (int u = 0; u < 2; ++u)
+#pragma unroll
+        for (int g = 0; g < 16; ++g)
+          sc[u][g] = (32 * u + 8 * (g / 4) + (g % 4) > lim) ? -INFINITY : sc[u][g];
+    }
+    if (!rowok) {
+      const unsigned okj = okmask(j);
+      // absent blocks: block b of the tile holds elements 8(b%2) .. 8(b%2)+7 of subtile b/2
+#pragma unroll
+      for (int b = 0; b < 4; ++b)
+        if (!((okj >> b) & 1u)) {
+#pragma unroll
+          for (int g = 0; g < 8; ++g) sc[b >> 1][8 * (b & 1) + g] = -INFINITY;
+        }
+    }
+    if constexpr (MASK) window_alibi(sc, k0, half, qpos, p.window_left, p.scale_log2, slope2);
+    // row max as a tree (short dependency chains)
+    float m4[4];
+#pragma unroll
+    for (int k = 0; k < 4; ++k)
+      m4[k] = fmaxf(fmaxf(fmaxf(sc[k >> 1][8 * (k & 1) + 0], sc[k >> 1][8 * (k & 1) + 1]),
+                          fmaxf(sc[k >> 1][8 * (k & 1) + 2], sc[k >> 1][8 * (k & 1) + 3])),
+                    fmaxf(fmaxf(sc[k >> 1][8 * (k & 1) + 4], sc[k >> 1][8 * (k & 1) + 5]),
+                          fmaxf(sc[k >> 1][8 * (k & 1) + 6], sc[k >> 1][8 * (k & 1) + 7])));
+    float mx = fmaxf(fmaxf(m4[0], m4[1]), fmaxf(m4[2], m4[3]));
+    mx = pair32_max_swap(mx);
+    // lazy rescale: move the reference max only when it grew by more than 2^8
+    const bool grow = (m_used == -INFINITY) ? (mx > -INFINITY) : ((mx - m_used) * c2 > kRescaleLog2);
+    if (__ballot(grow)) {
+      const float m_new = grow ? mx : m_used;
+      const float alpha = (m_used == -INFINITY) ? 0.f : fast_exp2((m_used - m_new) * c2);
+      l_run *= alpha;
+#pragma unroll
+      for (int t = 0; t < DT; ++t) acc[t] *= alpha;
+      m_used = m_new;
+    }
+    const float mref = (m_used == -INFINITY) ? 0.f : m_used * c2;
+#pragma unroll
+    for (int u = 0; u < 2; ++u)
+#pragma unroll
+      for (int g = 0; g < 16; ++g) sc[u][g] = fast_exp2(__builtin_fmaf(sc[u][g], c2, -mref));
+    // pack to the MFMA operand; row sums of the rounded probabilities the PV
+    // product uses, in four independent chains
+    float ls[4] = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int u = 0; u < 2; ++u)
+#pragma unroll
+      for (int v = 0; v < 2; ++v) {
+        const u32x4 w{pack2<CT>(sc[u][8 * v + 0], sc[u][8 * v + 1]), pack2<CT>(sc[u][8 * v + 2], sc[u][8 * v + 3]),
+                      pack2<CT>(sc[u][8 * v + 4], sc[u][8 * v + 5]), pack2<CT>(sc[u][8 * v + 6], sc[u][8 * v + 7])};
+        pk[2 * u + v] = w;
+#pragma unroll
+        for (int k = 0; k < 4; ++k) ls[k] = M::sum2(w[k], ls[k]);
+      }
+    l_run += (ls[0] + ls[1]) + (ls[2] + ls[3]);
+  };
+
+  if (ntiles > kt0) {
+    // prologue: K tiles t0 .. t0+2 and V tiles t0 .. t0+1
+    const int id0 = copy_id(raw_id(kt0), kt0);
+    const int id1 = copy_id(raw_id(kt0 + 1), kt0 + 1);
+    const int id2 = copy_id(raw_id(kt0 + 2), kt0 + 2);
+    int raw_n = raw_id(kt0 + 3);      // tile j+3's entry, checked in V(j)
+    int id_v = id2;                   // tile j+2's id (its V copy in V(j))
+    copy_tile(kbase, koff, id0, kr0);
+    copy_tile(vbase, voff, id0, vr0);
+    if (kt0 + 1 < ntiles) {
+      copy_tile(kbase, koff, id1, kr0 + kTileBytes);
+      copy_tile(vbase, voff, id1, vr0 + kTileBytes);
+    }
+    if (kt0 + 2 < ntiles) copy_tile(kbase, koff, id2, kr0 + 2 * kTileBytes);
+    // the first M phase multiplies zero probabilities with V stage NS-1:
+    // clear it, so stale LDS contents cannot turn 0 * V into NaN
+    for (int i = threadIdx.x; i < L::kPos; i += kPPThreads)
+      Vr[(NS - 1) * L::kPos + i] = u32x4{0u, 0u, 0u, 0u};
+    wait_vmcnt<0>();
+    fix_v(kt0, Vr);
+    if (kt0 + 1 < ntiles) fix_v(kt0 + 1, Vr + L::kPos);
+    barrier_nowait<true>();
+
+    auto step = [&](auto st_c, int j) __attribute__((always_inline)) {
+      constexpr int ST = decltype(st_c)::value;
+      const u32x4* Kt = Kr + ST * L::kPos;
+      const u32x4* Vt = Vr + ((ST + NS - 1) % NS) * L::kPos;
+      // ---- M(j) ----
+      // one straight MFMA path (branches around MFMAs cost accumulator
+      // copies): a tile the wave does not need still runs, with zero
+      // probabilities (P of the first tile, of tiles past the wave's queries
+      // or before its window); its scores are discarded
+      mphase(Kt, Vt);
+      // retire the copies of V(j-2) (those of V(j-1) may stay in flight)
+      if (j - 1 >= kt0 && j + 2 < ntiles) wait_vmcnt<2 * IPW>();
+      else if (j - 1 >= kt0 && j + 1 < ntiles) wait_vmcnt<IPW>();
+      else wait_vmcnt<0>();
+      if (j >= kt0 + 2 && j < ntiles) fix_v(j, Vr + ST * L::kPos);
+      barrier_nowait<true>();
+      // ---- V(j) ----
+      const int id_k = copy_id(raw_n, j + 3);
+      raw_n = raw_id(j + 4);
+      if (j < ntiles && active(j)) {
+        softmax(j);
+      } else {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) pk[i] = u32x4{0u, 0u, 0u, 0u};
+      }
+      if (j + 3 < ntiles) copy_tile(kbase, koff, id_k, kr0 + (unsigned)((ST + 3) % NS) * kTileBytes);
+      if (j + 2 < ntiles) copy_tile(vbase, voff, id_v, vr0 + (unsigned)((ST + 2) % NS) * kTileBytes);
+      id_v = id_k;
+      barrier_nowait<false>();
+    };
+
+    if (grp == 1) barrier_nowait<false>();
+    for (int j = kt0; j <= ntiles; j += NS) {
+      step(std::integral_constant<int, 0>{}, j);
+      if (j + 1 <= ntiles) step(std::integral_constant<int, 1>{}, j + 1);
+      if (j + 2 <= ntiles) step(std::integral_constant<int, 2>{}, j + 2);
+      if (j + 3 <= ntiles) step(std::integral_constant<int, 3>{}, j + 3);
+    }
+    if (grp == 0) barrier_nowait<false>();
   }
 
-  const float lt = pair32_sum(l_run);
+  // ---- normalise and store: lane holds O[qi][32 t + 8 j + 4 half + i] ----
+  const float lt = pair32_sum_swap(l_run);
   if (!q_ok) return;
   const float inv = (lt > 0.f) ? p.v_scale / lt : 0.f;
   unsigned short* orow = static_cast<unsigned short*>(p.out) +
@@ -694,16 +843,16 @@ int heads_per_wg(int G) {
 template <int D, typename CT, int KVB>
 hipError_t launch_typed(const AttnParams& p, hipStream_t stream) {
   const int hpw = heads_per_wg(p.group);
-  const int QB = 128 / hpw;
+  const int QB = (KVB == 2 ? 32 * kPPWaves : 128) / hpw;
   const int qtiles = (p.max_query_len + QB - 1) / QB;
   if (qtiles == 0) return hipSuccess;
   // x: query-head group, y: request, z: tile counted from the end of the request
   dim3 grid((unsigned)(p.num_q_heads / hpw), (unsigned)p.num_reqs, (unsigned)qtiles);
   if constexpr (KVB == 2) {
     if (p.masked) {
-      hipLaunchKernelGGL((prefill_dma_kernel<D, CT, true>), grid, dim3(kThreads), 0, stream, p, hpw);
+      hipLaunchKernelGGL((prefill_pp_kernel<D, CT, true>), grid, dim3(kPPThreads), 0, stream, p, hpw);
     } else {
-      hipLaunchKernelGGL((prefill_dma_kernel<D, CT, false>), grid, dim3(kThreads), 0, stream, p, hpw);
+      hipLaunchKernelGGL((prefill_pp_kernel<D, CT, false>), grid, dim3(kPPThreads), 0, stream, p, hpw);
     }
   } else {
     if (p.masked) {
