@@ -517,11 +517,20 @@ __global__ __launch_bounds__(kPPThreads) void prefill_pp_kernel(AttnParams p, in
   __shared__ u32x4 Kr[NS * L::kPos];
   __shared__ u32x4 Vr[NS * L::kPos];
 
-  const int r = p.req_begin + blockIdx.y;
+  // Request-major numbering: consecutive workgroups are the query tiles of
+  // one request for consecutive head groups; workgroups are spread over the
+  // 8 XCDs by number, so with 8 (or a multiple of 8) head groups an XCD keeps
+  // the same K/V head and its L2 serves every query tile of the request the
+  // K/V stream it is reading.  Within a request the tiles run longest first.
+  const unsigned lin = blockIdx.x + gridDim.x * (blockIdx.y + gridDim.y * blockIdx.z);
+  const unsigned bx = lin % gridDim.x;
+  const unsigned bz = (lin / gridDim.x) % gridDim.z;
+  const unsigned by = lin / (gridDim.x * gridDim.z);
+  const int r = p.req_begin + (int)by;
   const int q_first = p.qsl[r];
   const int n = p.qsl[r + 1] - q_first;
   const int QB = (32 * kPPWaves) / hpw;
-  const int q_hi = n - (int)blockIdx.z * QB;      // tile z covers queries [q_hi - QB, q_hi)
+  const int q_hi = n - (int)bz * QB;      // tile z covers queries [q_hi - QB, q_hi)
   if (q_hi <= 0) return;
   const int G = p.group;
   const int s_all = p.seq_lens[r];
@@ -537,7 +546,7 @@ __global__ __launch_bounds__(kPPThreads) void prefill_pp_kernel(AttnParams p, in
   const int grp = wave >> 2;
   const int half = lane >> 5;
   const int l32 = lane & 31;
-  const int qh = blockIdx.x * hpw + (wave % hpw);
+  const int qh = (int)bx * hpw + (wave % hpw);
   const int kvh = qh / G;
   const int wq0 = q_hi - QB + (wave / hpw) * 32;   // first query of the wave (may be < 0)
   const int qi = wq0 + l32;                        // this lane's query
