@@ -28,10 +28,10 @@ Sources (web pages; every function cites the part it follows):
   and block sharing between sequences.
 
 Arithmetic is float64 unless the format itself fixes the precision (the fp8
-encoder's single float32 multiply) or the reading of the pages fixes it (the
+and int8 encoders' single float32 multiply) or the reading of the pages fixes it (the
 rotary embedding's float32 steps, pinned to the float64 rotation).  Modules:
 
-* ``codecs``     fp16 / bf16 / OCP e4m3fn bit decoders and the e4m3fn encoder.
+* ``codecs``     fp16 / bf16 / OCP e4m3fn / int8 bit decoders, the e4m3fn and int8 encoders.
 * ``metadata``   query_start_loc, seq_lens, positions, slot_mapping.
 * ``cache``      the slot_mapping scatter into ``[num_blocks, block_size, Hkv, D]``.
 * ``attention``  gather through the block table + dense causal softmax(QK^T*scale)V.

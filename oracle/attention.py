@@ -95,9 +95,10 @@ def causal_attention(q, k, v, num_computed, scale, sliding_window=0, alibi_slope
 
 
 def decode_cache(cache_bits, cache_dtype, scale=1.0):
-    """Stored cache bits -> float64 values (fp8 codes are multiplied by the scale)."""
+    """Stored cache bits -> float64 values (fp8 and int8 codes are multiplied
+    by the tensor's scale)."""
     vals = codecs.decode(cache_bits, cache_dtype)
-    if cache_dtype == "fp8_e4m3":
+    if cache_dtype in ("fp8_e4m3", "int8"):
         vals = vals * float(scale)
     return vals
 
@@ -109,7 +110,7 @@ def paged_attention(q, key_cache, value_cache, block_tables, query_start_loc, se
 
     q: float64 [T, Hq, D] (already decoded).
     key_cache/value_cache: float64 [num_blocks, block_size, Hkv, D] (decoded), or
-      raw bits when ``cache_dtype`` is given ('f16' | 'bf16' | 'fp8_e4m3'); raw
+      raw bits when ``cache_dtype`` is given ('f16' | 'bf16' | 'fp8_e4m3' | 'int8'); raw
       bits are decoded per request, so a large pool is never widened at once.
     requests: iterable of request indices to compute (default: all).
     sliding_window, alibi_slopes: the mask variants of ``causal_attention``.

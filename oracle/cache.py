@@ -9,9 +9,10 @@ each new token ``t`` with ``slot_mapping[t] >= 0`` (negative slots are skipped),
 pass", stop 10, and the worked decode trace of "vLLM MHA Code Path" (step 8)
 place this write before the attention read of the same layer.
 
-Caches are handled as raw bit patterns (uint16 for fp16/bf16, uint8 for fp8),
-so a write is a byte copy and can be compared bit for bit.  The fp8 path
-encodes with ``codecs.e4m3fn_encode`` from the float32 value of the input.
+Caches are handled as raw bit patterns (uint16 for fp16/bf16, uint8 for fp8
+and int8), so a write is a byte copy and can be compared bit for bit.  The fp8
+and int8 paths encode with ``codecs.e4m3fn_encode`` / ``codecs.int8_encode``
+from the float32 value of the input.
 """
 
 import numpy as np
@@ -43,6 +44,9 @@ def scatter(key_cache, value_cache, key, value, slot_mapping, block_size,
     elif cache_dtype == "fp8_e4m3":
         new_k = codecs.e4m3fn_encode(_to_f32(key[:num_tokens], act_dtype), k_inv_scale)
         new_v = codecs.e4m3fn_encode(_to_f32(value[:num_tokens], act_dtype), v_inv_scale)
+    elif cache_dtype == "int8":
+        new_k = codecs.int8_encode(_to_f32(key[:num_tokens], act_dtype), k_inv_scale).view(np.uint8)
+        new_v = codecs.int8_encode(_to_f32(value[:num_tokens], act_dtype), v_inv_scale).view(np.uint8)
     else:
         raise ValueError((act_dtype, cache_dtype))
     for t in range(num_tokens):

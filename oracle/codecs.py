@@ -12,6 +12,12 @@ Reading taken where the pages are silent: one float32 scale per tensor
 ``round_to_nearest_even(saturate(float32(x) * float32(1/scale)))`` with the
 single multiply done in IEEE float32, saturation to +-448 for every finite or
 infinite overflow, and NaN kept as NaN.
+
+The int8 cache (the pages' own example of KV-cache quantization) is read the
+same way: symmetric signed codes -127..127 (two's complement bytes; -128 is
+never produced), one float32 scale per tensor, a code means ``code * scale``,
+encoding ``round_to_nearest_even(saturate(float32(x) * float32(1/scale)))``
+with saturation to +-127; int8 has no NaN, and a NaN input becomes 0.
 """
 
 import numpy as np
@@ -102,6 +108,38 @@ def e4m3fn_encode(x_f32, inv_scale_f32):
     return codes.astype(np.uint8)
 
 
+INT8_MAX = 127
+
+
+def int8_encode(x_f32, inv_scale_f32):
+    """Encode float32 values as symmetric int8 codes with the per-tensor scale.
+
+    ``y = float32(x * inv_scale)`` (one IEEE float32 multiply); NaN gives 0;
+    ``y`` is clamped to [-127, 127] (127 is an integer, so clamping first and
+    rounding second equals rounding first and saturating second); then the
+    nearer of the two integers around ``y`` is chosen, and on a tie the even
+    one.  Returns int8 codes.
+    """
+    x = np.asarray(x_f32, dtype=np.float32)
+    with np.errstate(over="ignore", invalid="ignore"):
+        y = (x * np.float32(inv_scale_f32)).astype(np.float32)   # float32 multiply
+    y = y.astype(np.float64)
+    nan = np.isnan(y)
+    y = np.where(nan, 0.0, np.clip(y, -INT8_MAX, INT8_MAX))
+    lo = np.floor(y)                    # the integer at or below y
+    hi = lo + 1.0                       # the integer above
+    d_lo = y - lo
+    d_hi = hi - y
+    lo_even = np.mod(lo, 2.0) == 0.0
+    q = np.where((d_hi < d_lo) | ((d_hi == d_lo) & ~lo_even), hi, lo)
+    return q.astype(np.int8)
+
+
+def int8_to_f64(codes):
+    """Stored int8 code bytes (uint8 or int8) -> float64 code values."""
+    return np.asarray(codes).astype(np.uint8).view(np.int8).astype(np.float64)
+
+
 def f32_to_bf16_bits(x_f32):
     """float32 values -> bfloat16 bit patterns, round to nearest, ties to even.
 
@@ -151,11 +189,14 @@ def f32_to_act_bits(x_f32, dtype):
 
 
 def decode(bits, dtype):
-    """Decode stored bits of ``dtype`` ('f16', 'bf16', 'fp8_e4m3') to float64."""
+    """Decode stored bits of ``dtype`` ('f16', 'bf16', 'fp8_e4m3', 'int8') to
+    float64 (for the quantized formats: the code value, before the scale)."""
     if dtype == "f16":
         return f16_bits_to_f64(bits)
     if dtype == "bf16":
         return bf16_bits_to_f64(bits)
     if dtype == "fp8_e4m3":
         return e4m3fn_to_f64(bits)
+    if dtype == "int8":
+        return int8_to_f64(bits)
     raise ValueError(dtype)

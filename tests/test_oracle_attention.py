@@ -208,3 +208,49 @@ def test_scatter_fp8_encodes():
     assert np.array_equal(kc2[0, 5], want[0])
     assert np.array_equal(kc2[2, 8], want[2])
     assert np.count_nonzero(kc2) == np.count_nonzero(want[0]) + np.count_nonzero(want[2])
+
+
+def test_scatter_int8_encodes():
+    # expected codes from torch's per-tensor quantization (independent of the
+    # oracle's encoder), clipped to the symmetric range
+    rng = np.random.default_rng(5)
+    nb, bs, hkv, d = 4, 16, 1, 8
+    kc = np.zeros((nb, bs, hkv, d), np.uint8)
+    vc = np.full((nb, bs, hkv, d), 7, np.uint8)
+    kx = (rng.standard_normal((3, hkv, d)) * 3).astype(np.float32)
+    bits = torch.from_numpy(kx).to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
+    slots = np.array([5, -1, 40])
+    scale = np.float32(0.02)
+    inv = np.float32(1.0) / scale
+    kc2, vc2 = S.scatter(kc, vc, bits, bits, slots, bs, act_dtype="bf16", cache_dtype="int8",
+                         k_inv_scale=inv, v_inv_scale=inv)
+    xb = torch.from_numpy(bits.view(np.int16)).view(torch.bfloat16).to(torch.float32)
+    want = np.maximum(torch.quantize_per_tensor(xb, float(scale), 0, torch.qint8).int_repr().numpy(), -127)
+    assert np.array_equal(kc2[0, 5].view(np.int8), want[0])
+    assert np.array_equal(kc2[2, 8].view(np.int8), want[2])
+    assert np.array_equal(vc2[2, 8].view(np.int8), want[2])
+    # untouched slots keep their bytes (the padding token wrote nothing)
+    assert np.count_nonzero(kc2) == np.count_nonzero(want[0]) + np.count_nonzero(want[2])
+    assert np.sum(vc2 != 7) == np.sum(want[0] != 7) + np.sum(want[2] != 7)
+
+
+def test_int8_cache_attention_equals_sdpa_on_dequantized():
+    # an int8 cache with per-tensor scales attends like a float cache holding
+    # code * scale: checked against torch SDPA on the dequantized contiguous K/V
+    rng = np.random.default_rng(6)
+    hq, hkv, d, bs, pool = 4, 2, 16, 4, 32
+    comp, ql = [5, 0, 9], [1, 6, 3]
+    seq, rows, _, _, q = _paged_setup(rng, comp, ql, hq, hkv, d, bs, pool)
+    kcode = rng.integers(-127, 128, size=(pool, bs, hkv, d)).astype(np.int8)
+    vcode = rng.integers(-127, 128, size=(pool, bs, hkv, d)).astype(np.int8)
+    ks, vs = 0.013, 0.021
+    qsl = [0] + list(np.cumsum(ql))
+    scale = 1.0 / math.sqrt(d)
+    got = A.paged_attention(q, kcode.view(np.uint8), vcode.view(np.uint8), rows, qsl, seq, bs,
+                            cache_dtype="int8", k_scale=ks, v_scale=vs)
+    for r in range(len(seq)):
+        ids = rows[r]
+        k = kcode[ids].reshape(-1, hkv, d)[:seq[r]].astype(np.float64) * ks
+        v = vcode[ids].reshape(-1, hkv, d)[:seq[r]].astype(np.float64) * vs
+        ref = _sdpa_reference(q[qsl[r]:qsl[r + 1]], k, v, comp[r], scale)
+        assert np.allclose(got[r], ref, rtol=0, atol=1e-12), r

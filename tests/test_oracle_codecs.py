@@ -105,3 +105,61 @@ def test_e4m3fn_roundtrip_all_codes():
     back = C.e4m3fn_encode(vals, np.float32(1.0))
     finite = np.isfinite(vals)
     assert np.array_equal(back[finite], codes[finite])
+
+
+# ---------------------------------------------------------------- int8 --
+# The pages name int8 as their example of KV-cache quantization ("vLLM 推理全流程
+# 深度解析", PagedAttention remark); the format is the symmetric one described
+# in oracle.codecs.  The independent reference is torch's per-tensor
+# quantization (qint8, zero point 0: round to nearest even of x * (1 / scale)
+# with saturation), whose only difference is that it also produces -128.
+
+def _torch_int8(x_f32, scale):
+    q = torch.quantize_per_tensor(torch.from_numpy(np.asarray(x_f32, np.float32)), float(scale), 0,
+                                  torch.qint8)
+    return np.maximum(q.int_repr().numpy(), -127)   # the symmetric range stops at -127
+
+
+@pytest.mark.parametrize("src", ["bf16", "f16"])
+@pytest.mark.parametrize("scale", [np.float32(0.125), np.float32(0.0137)])
+def test_int8_encoder_exhaustive_vs_torch(src, scale):
+    with np.errstate(invalid="ignore"):
+        x = C.decode(ALL16, src).astype(np.float32)
+    finite = np.isfinite(x)
+    mine = C.int8_encode(x, np.float32(1.0) / scale)
+    assert mine.dtype == np.int8
+    assert np.array_equal(mine[finite], _torch_int8(x[finite], scale))
+    # infinities saturate, NaN encodes as 0, -128 never appears
+    inf = np.isinf(x)
+    assert np.all(mine[inf] == np.sign(x[inf]) * 127)
+    assert np.all(mine[np.isnan(x)] == 0)
+    assert mine.min() >= -127
+
+
+def test_int8_encoder_ties_and_saturation():
+    enc = lambda v: int(C.int8_encode(np.array([v], np.float32), np.float32(1.0))[0])
+    assert [enc(v) for v in (0.5, 1.5, 2.5, -0.5, -1.5, -2.5)] == [0, 2, 2, 0, -2, -2]
+    assert [enc(v) for v in (0.49, 0.51, -0.51, 126.5, 126.6)] == [0, 1, -1, 126, 127]
+    assert enc(127.5) == 127 and enc(1e9) == 127 and enc(-127.5) == -127 and enc(-1e9) == -127
+    assert enc(float("inf")) == 127 and enc(float("-inf")) == -127 and enc(float("nan")) == 0
+    # the scale is applied as one float32 multiply before rounding
+    assert int(C.int8_encode(np.array([0.3], np.float32), np.float32(10.0))[0]) == 3
+
+
+def test_int8_codes_roundtrip_and_decoder_vs_torch():
+    codes = np.arange(-127, 128, dtype=np.int8)
+    assert np.array_equal(C.int8_encode(codes.astype(np.float32), np.float32(1.0)), codes)
+    raw = np.arange(256, dtype=np.uint8)
+    ref = torch.from_numpy(raw).view(torch.int8).to(torch.float64).numpy()
+    assert np.array_equal(C.int8_to_f64(raw), ref)
+    assert np.array_equal(C.decode(raw, "int8"), ref)
+
+
+def test_int8_error_bound():
+    # in range, the decoded value is within half a step of the input
+    rng = np.random.default_rng(0)
+    scale = np.float32(0.0137)
+    x = (rng.standard_normal(100000) * 0.5).astype(np.float32)
+    x = x[np.abs(x) < 127 * scale]
+    back = C.int8_to_f64(C.int8_encode(x, np.float32(1.0) / scale).view(np.uint8)) * float(scale)
+    assert np.max(np.abs(back - x.astype(np.float64))) <= float(scale) * 0.5 * (1 + 1e-6)
