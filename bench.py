@@ -17,7 +17,8 @@ Also reported on the same JSON line:
 * ``cpu_baseline``: the oracle on the host cores over a bounded sample of the
   same batch;
 * ``extra``: the other measured workloads (GQA decode, chunked-prefill mix,
-  long-context fp8 MQA decode), each call timed with events after a 1 GiB
+  long-context fp8 MQA decode, and the GQA decode, mixed batch and long MQA
+  decode again over an int8 cache), each call timed with events after a 1 GiB
   cache-evicting read; besides attention and the cache write this times the
   fused RoPE + cache write (rotary_dim = head_dim, half-split pairs), on the
   GQA pool the block copy / swap out / swap in of 4096 blocks, and on the GQA
@@ -48,7 +49,7 @@ PREFILL_SRC = os.path.join(ROOT, "paged_kv_cache_hkv_amd", "csrc", "pa_prefill.h
 
 
 def kv_bytes(wl, reqs):
-    e = 1 if wl.cache_fp8 else 2
+    e = wl.cache_elem_bytes
     s = wl.seq_lens_host[list(reqs)].astype(np.int64)
     return int(s.sum()) * wl.num_kv_heads * wl.head_dim * 2 * e
 
@@ -64,7 +65,7 @@ def prefill_flops(wl, reqs):
 
 def window_kv_bytes(wl, reqs, window):
     """KV bytes a decode must read under a sliding window: the last min(s, W) keys."""
-    e = 1 if wl.cache_fp8 else 2
+    e = wl.cache_elem_bytes
     s = np.minimum(wl.seq_lens_host[list(reqs)].astype(np.int64), window)
     return int(s.sum()) * wl.num_kv_heads * wl.head_dim * 2 * e
 
@@ -153,14 +154,16 @@ def time_calls(fn_list, iters, flush):
     return out
 
 
-def bench_extra(name, iters, flush):
+def bench_extra(name, iters, flush, kind=None):
     wl = S.CONFIGS[name]()
+    if kind is not None:
+        wl = S.with_cache(wl, kind)
     t = S.make_tensors(wl, "cuda", poison=False)
     st = PagedAttentionStep(wl, t)
     st.run()
     torch.cuda.synchronize()
-    rec = {"workload": name, "requests": wl.num_reqs, "decodes": wl.num_decodes,
-           "tokens": wl.num_tokens}
+    rec = {"workload": wl.name, "cache": wl.cache_kind, "requests": wl.num_reqs,
+           "decodes": wl.num_decodes, "tokens": wl.num_tokens}
     fns, names = [], []
     if wl.num_decodes:
         fns.append(st.decode)
@@ -198,9 +201,9 @@ def bench_extra(name, iters, flush):
         rec["prefill_tok_per_s"] = round(toks / sec, 1)
         rec["prefill_TFLOPs"] = round(fl / sec / 1e12, 1)
         rec["prefill_mfma_frac"] = round(fl / sec / 1e12 / BF16_PEAK_TFLOPS, 4)
-    if name == "decode_gqa":
+    if wl.name == "decode_gqa":
         rec["copy_blocks"] = bench_blocks(wl, t, st.desc, iters, flush)
-    if name in ("decode_gqa", "chunked_prefill_mix"):
+    if wl.name in ("decode_gqa", "chunked_prefill_mix"):
         rec["window_alibi"] = bench_masks(wl, t, iters, flush)
     del st, t
     torch.cuda.empty_cache()
@@ -221,7 +224,7 @@ def rope_bytes(wl, rotary_dim):
     q rotated part read and written, k and v read, k and v cache rows written, the
     token's cos/sin row, its position and slot."""
     T, hq, hkv, d = wl.num_tokens, wl.num_q_heads, wl.num_kv_heads, wl.head_dim
-    e = 1 if wl.cache_fp8 else 2
+    e = wl.cache_elem_bytes
     per = 2 * hq * rotary_dim * 2 + 2 * hkv * d * 2 + 2 * hkv * d * e + rotary_dim * 4 + 16
     return T * per
 
@@ -389,8 +392,10 @@ def main():
         del st
         flush = torch.empty(1 << 28, dtype=torch.float32, device="cuda")
         extra = []
-        for name in ("decode_gqa", "chunked_prefill_mix", "mqa_fp8_long"):
-            extra.append(bench_extra(name, args.extra_iters, flush))
+        for name, kind in (("decode_gqa", None), ("chunked_prefill_mix", None),
+                           ("mqa_fp8_long", None), ("decode_gqa", "int8"),
+                           ("chunked_prefill_mix", "int8"), ("mqa_fp8_long", "int8")):
+            extra.append(bench_extra(name, args.extra_iters, flush, kind))
             print(f"# {json.dumps(extra[-1])}", file=sys.stderr, flush=True)
         line["extra"] = extra
         del flush

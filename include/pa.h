@@ -73,7 +73,8 @@ typedef enum pa_status {
 typedef enum pa_dtype {
   PA_F16 = 0,       /* IEEE binary16 */
   PA_BF16 = 1,      /* bfloat16 */
-  PA_FP8_E4M3 = 2   /* OCP e4m3fn (max 448, no inf); cache only */
+  PA_FP8_E4M3 = 2,  /* OCP e4m3fn (max 448, no inf); cache only */
+  PA_INT8 = 3       /* symmetric signed int8 codes -127..127; cache only */
 } pa_dtype;
 
 /*
@@ -83,14 +84,17 @@ typedef enum pa_dtype {
  * G = num_q_heads / num_kv_heads, which covers MHA (G = 1), GQA and MQA
  * (num_kv_heads = 1) with one path ("vLLM MHA Code Path", "One Path Covers
  * MHA, GQA, and MQA").  Supported: head_dim 64 or 128; block_size 16;
- * act_dtype F16 or BF16; cache_dtype equal to act_dtype or FP8_E4M3; G <= 32
- * for decode.
+ * act_dtype F16 or BF16; cache_dtype equal to act_dtype, FP8_E4M3 or INT8;
+ * G <= 32 for decode.
  *
  * softmax_scale multiplies q.k (1/sqrt(head_dim) is the usual value).
- * k_scale / v_scale apply to an fp8 cache only: a stored code c means the
- * value c * scale.  The write path encodes float32(x) * (1.0f / scale)
- * (one float32 multiply, the reciprocal rounded once on the host) with
- * round-to-nearest-even and saturation to +-448; NaN stays NaN.
+ * k_scale / v_scale apply to a quantized (fp8 or int8) cache only: a stored
+ * code c means the value c * scale, one scale per tensor.  The write path
+ * encodes y = float32(x) * (1.0f / scale) (one float32 multiply, the
+ * reciprocal rounded once on the host) with round-to-nearest-even: fp8
+ * saturates to +-448 and keeps NaN; int8 saturates to +-127 (the code -128 is
+ * never written) and stores 0 for NaN.  KV-cache int8 is the quantization the
+ * "vLLM 推理全流程深度解析" PagedAttention section names as a throughput lever.
  *
  * decode_workers: number of waves pa_decode divides its key stream among
  * (see pa_decode); 0 lets the library choose (four per compute unit of the
@@ -105,8 +109,8 @@ typedef enum pa_dtype {
  *   p - W < j <= p (its W most recent positions, itself included); blocks
  *   wholly before the window are not read.  0 = plain causal attention.
  * - alibi_slopes: when not NULL, query head h adds slope[h] * (j - p) to the
- *   scaled score softmax_scale * q.k of key j (fp8: the scale-corrected
- *   score) before the softmax.  The array stays owned by the caller and must
+ *   scaled score softmax_scale * q.k of key j (fp8 / int8: the
+ *   scale-corrected score) before the softmax.  The array stays owned by the caller and must
  *   live until the calls that use this descriptor have finished; 4-byte
  *   aligned.
  * Both use the query position p = seq_len - query_len + i for row i of a
@@ -171,7 +175,7 @@ pa_status pa_metadata_build(int32_t num_reqs, int32_t block_size, int32_t max_bl
  *   other tokens (the -1 padding) are skipped.  Two tokens with one slot race.
  * key_cache, value_cache: cache_dtype [num_blocks, block_size, num_kv_heads,
  *   head_dim]; only the addressed slots are written, bit-exact copies (or
- *   fp8 encodings, see pa_attn_desc) of the inputs.
+ *   fp8 / int8 encodings, see pa_attn_desc) of the inputs.
  */
 pa_status pa_cache_write(const pa_attn_desc* desc, int64_t num_tokens,
                          const void* key, int64_t key_row_stride,
@@ -202,8 +206,8 @@ pa_status pa_cache_write(const pa_attn_desc* desc, int64_t num_tokens,
  * query and key head becomes a*c - b*s, b*c + a*s, computed in float32 with
  * every product and sum rounded once (no fused multiply-add), rounded to
  * act_dtype (nearest even).  The rotated key and the value then go to the
- * slot exactly as pa_cache_write would store them (fp8 caches: the rotated
- * key rounded to act_dtype is encoded).  A token with a slot that is negative
+ * slot exactly as pa_cache_write would store them (fp8 / int8 caches: the
+ * rotated key rounded to act_dtype is encoded).  A token with a slot that is negative
  * or past the pool has its query rotated and writes nothing; a token whose
  * position is outside [0, max_position) is left entirely alone.
  */

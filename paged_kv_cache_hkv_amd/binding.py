@@ -15,10 +15,10 @@ _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_HERE, "libpa.so")
 
 PA_OK, PA_ERR_INVALID_ARG, PA_ERR_UNSUPPORTED, PA_ERR_WORKSPACE_TOO_SMALL, PA_ERR_HIP = range(5)
-PA_F16, PA_BF16, PA_FP8_E4M3 = 0, 1, 2
+PA_F16, PA_BF16, PA_FP8_E4M3, PA_INT8 = 0, 1, 2, 3
 
 DTYPE_CODE = {torch.float16: PA_F16, torch.bfloat16: PA_BF16, torch.float8_e4m3fn: PA_FP8_E4M3,
-              torch.uint8: PA_FP8_E4M3}
+              torch.uint8: PA_FP8_E4M3, torch.int8: PA_INT8}
 
 
 class PaError(RuntimeError):

@@ -20,7 +20,10 @@ constexpr float kLog2e = 1.4426950408889634f;
 
 bool aligned16(const void* ptr) { return (reinterpret_cast<uintptr_t>(ptr) & 15u) == 0; }
 
-int elem_bytes(int dt) { return dt == PA_FP8_E4M3 ? 1 : 2; }
+// 8-bit codes with a per-tensor scale (fp8 e4m3fn or int8)
+bool quantized(int dt) { return dt == PA_FP8_E4M3 || dt == PA_INT8; }
+
+int elem_bytes(int dt) { return quantized(dt) ? 1 : 2; }
 
 pa_status check_desc(const pa_attn_desc* d) {
   if (d == nullptr) return PA_ERR_INVALID_ARG;
@@ -28,16 +31,16 @@ pa_status check_desc(const pa_attn_desc* d) {
   if (d->num_q_heads % d->num_kv_heads != 0) return PA_ERR_INVALID_ARG;
   if (d->head_dim <= 0 || d->block_size <= 0) return PA_ERR_INVALID_ARG;
   if (d->act_dtype != PA_F16 && d->act_dtype != PA_BF16) {
-    return d->act_dtype == PA_FP8_E4M3 ? PA_ERR_UNSUPPORTED : PA_ERR_INVALID_ARG;
+    return quantized(d->act_dtype) ? PA_ERR_UNSUPPORTED : PA_ERR_INVALID_ARG;
   }
-  if (d->cache_dtype != d->act_dtype && d->cache_dtype != PA_FP8_E4M3) {
+  if (d->cache_dtype != d->act_dtype && !quantized(d->cache_dtype)) {
     return (d->cache_dtype == PA_F16 || d->cache_dtype == PA_BF16) ? PA_ERR_UNSUPPORTED
                                                                   : PA_ERR_INVALID_ARG;
   }
   if (d->head_dim != 64 && d->head_dim != 128) return PA_ERR_UNSUPPORTED;
   if (d->block_size != kBlockSize) return PA_ERR_UNSUPPORTED;
   if (!std::isfinite(d->softmax_scale)) return PA_ERR_INVALID_ARG;
-  if (d->cache_dtype == PA_FP8_E4M3) {
+  if (quantized(d->cache_dtype)) {
     if (!(d->k_scale > 0.f) || !(d->v_scale > 0.f) || !std::isfinite(d->k_scale) ||
         !std::isfinite(d->v_scale)) {
       return PA_ERR_INVALID_ARG;
@@ -56,7 +59,9 @@ pa_status check_desc(const pa_attn_desc* d) {
 int decode_workers(const pa_attn_desc* d) {
   if (d->decode_workers > 0) return d->decode_workers;
   const int per_cu = pa::decode_waves_per_cu(d->num_q_heads / d->num_kv_heads,
-                                             d->cache_dtype == PA_FP8_E4M3 ? pa::kFP8 : pa::kF16);
+                                             d->cache_dtype == PA_FP8_E4M3 ? pa::kFP8
+                                             : d->cache_dtype == PA_INT8   ? pa::kINT8
+                                                                           : pa::kF16);
   int dev = 0, cus = 0;
   if (hipGetDevice(&dev) != hipSuccess ||
       hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
@@ -121,7 +126,7 @@ bool device_address(const void* ptr, const void** out) {
 }
 
 float scale_log2(const pa_attn_desc* d) {
-  const float ks = d->cache_dtype == PA_FP8_E4M3 ? d->k_scale : 1.0f;
+  const float ks = quantized(d->cache_dtype) ? d->k_scale : 1.0f;
   return d->softmax_scale * ks * kLog2e;
 }
 
@@ -203,8 +208,8 @@ pa_status pa_cache_write(const pa_attn_desc* desc, int64_t num_tokens, const voi
   p.key_cache = key_cache;
   p.value_cache = value_cache;
   p.num_slots = num_blocks * desc->block_size;
-  p.k_inv_scale = desc->cache_dtype == PA_FP8_E4M3 ? 1.0f / desc->k_scale : 1.0f;
-  p.v_inv_scale = desc->cache_dtype == PA_FP8_E4M3 ? 1.0f / desc->v_scale : 1.0f;
+  p.k_inv_scale = quantized(desc->cache_dtype) ? 1.0f / desc->k_scale : 1.0f;
+  p.v_inv_scale = quantized(desc->cache_dtype) ? 1.0f / desc->v_scale : 1.0f;
   return from_hip(pa::launch_cache_write(p, desc->act_dtype, desc->cache_dtype,
                                          static_cast<hipStream_t>(stream)));
 }
@@ -264,8 +269,8 @@ pa_status pa_rope_cache_write(const pa_attn_desc* desc, int64_t num_tokens,
   p.key_cache = key_cache;
   p.value_cache = value_cache;
   p.num_slots = num_blocks * desc->block_size;
-  p.k_inv_scale = desc->cache_dtype == PA_FP8_E4M3 ? 1.0f / desc->k_scale : 1.0f;
-  p.v_inv_scale = desc->cache_dtype == PA_FP8_E4M3 ? 1.0f / desc->v_scale : 1.0f;
+  p.k_inv_scale = quantized(desc->cache_dtype) ? 1.0f / desc->k_scale : 1.0f;
+  p.v_inv_scale = quantized(desc->cache_dtype) ? 1.0f / desc->v_scale : 1.0f;
   return from_hip(pa::launch_rope_cache_write(p, desc->act_dtype, desc->cache_dtype,
                                               static_cast<hipStream_t>(stream)));
 }
@@ -356,7 +361,7 @@ static pa::AttnParams make_params(const pa_attn_desc* desc, int32_t req_begin, i
   p.out = out;
   p.out_row_stride = out_row_stride;
   p.scale_log2 = scale_log2(desc);
-  p.v_scale = desc->cache_dtype == PA_FP8_E4M3 ? desc->v_scale : 1.0f;
+  p.v_scale = quantized(desc->cache_dtype) ? desc->v_scale : 1.0f;
   p.window_left = desc->sliding_window > 0 ? desc->sliding_window - 1 : pa::kNoWindow;
   p.alibi = desc->alibi_slopes;
   p.masked = desc->sliding_window > 0 || desc->alibi_slopes != nullptr;

@@ -13,7 +13,8 @@
 //
 // fp8 encode (OCP e4m3fn) is integer code of our own: y = float32(x) * inv_scale
 // in one float32 multiply, then round-to-nearest-even on the float32 bit
-// pattern with saturation to +-448 and NaN kept.
+// pattern with saturation to +-448 and NaN kept.  int8 encode: the same y,
+// rounded to the nearest even integer with saturation to +-127, NaN -> 0.
 #include "pa_device.h"
 #include "pa_kernels.h"
 
@@ -26,20 +27,23 @@ constexpr int kThreads = 256;
 template <typename T>
 __device__ inline float elem_to_float(unsigned short b) { return Mfma<T>::to_float(b); }
 
-template <typename T>
+// eight elements -> eight 8-bit codes (ENC 1: fp8 e4m3fn, 2: int8)
+template <typename T, int ENC>
 __device__ inline u32x2 encode8(const u32x4& v, float inv) {
   unsigned out[2] = {0u, 0u};
 #pragma unroll
   for (int k = 0; k < 8; ++k) {
     const unsigned w = v[k >> 1];
     const unsigned short h = (unsigned short)((k & 1) ? (w >> 16) : (w & 0xFFFFu));
-    const unsigned code = encode_e4m3fn(elem_to_float<T>(h) * inv);
+    const float y = elem_to_float<T>(h) * inv;
+    const unsigned code = ENC == 2 ? encode_int8(y) : encode_e4m3fn(y);
     out[k >> 2] |= code << (8 * (k & 3));
   }
   return u32x2{out[0], out[1]};
 }
 
-template <typename T, bool FP8>
+// ENC: 0 copy (cache in the activation dtype), 1 fp8 e4m3fn, 2 int8
+template <typename T, int ENC>
 __global__ __launch_bounds__(kThreads) void cache_write_kernel(CacheWriteParams p) {
   const bool is_v = blockIdx.y != 0;
   const int vec_per_row = p.row_elems >> 3;
@@ -55,21 +59,21 @@ __global__ __launch_bounds__(kThreads) void cache_write_kernel(CacheWriteParams 
   const u32x4 v = ld16(src + t * stride + (int64_t)c * 8);
   // cache row of the slot: [block, offset] flattened = slot
   const int64_t dst_elem = slot * p.row_elems + (int64_t)c * 8;
-  if constexpr (FP8) {
+  if constexpr (ENC != 0) {
     unsigned char* dst = static_cast<unsigned char*>(is_v ? p.value_cache : p.key_cache);
-    st8(dst + dst_elem, encode8<T>(v, is_v ? p.v_inv_scale : p.k_inv_scale));
+    st8(dst + dst_elem, encode8<T, ENC>(v, is_v ? p.v_inv_scale : p.k_inv_scale));
   } else {
     unsigned short* dst = static_cast<unsigned short*>(is_v ? p.value_cache : p.key_cache);
     st16(dst + dst_elem, v);
   }
 }
 
-template <typename T, bool FP8>
+template <typename T, int ENC>
 hipError_t launch_typed(const CacheWriteParams& p, hipStream_t stream) {
   const int64_t total = p.num_tokens * (p.row_elems >> 3);
   if (total == 0) return hipSuccess;
   const int64_t blocks = (total + kThreads - 1) / kThreads;
-  hipLaunchKernelGGL((cache_write_kernel<T, FP8>), dim3((unsigned)blocks, 2), dim3(kThreads), 0,
+  hipLaunchKernelGGL((cache_write_kernel<T, ENC>), dim3((unsigned)blocks, 2), dim3(kThreads), 0,
                      stream, p);
   return hipGetLastError();
 }
@@ -78,10 +82,12 @@ hipError_t launch_typed(const CacheWriteParams& p, hipStream_t stream) {
 
 hipError_t launch_cache_write(const CacheWriteParams& p, int act_dtype, int cache_dtype,
                               hipStream_t stream) {
-  if (act_dtype == kF16 && cache_dtype == kF16) return launch_typed<_Float16, false>(p, stream);
-  if (act_dtype == kBF16 && cache_dtype == kBF16) return launch_typed<__bf16, false>(p, stream);
-  if (act_dtype == kF16 && cache_dtype == kFP8) return launch_typed<_Float16, true>(p, stream);
-  if (act_dtype == kBF16 && cache_dtype == kFP8) return launch_typed<__bf16, true>(p, stream);
+  if (act_dtype == kF16 && cache_dtype == kF16) return launch_typed<_Float16, 0>(p, stream);
+  if (act_dtype == kBF16 && cache_dtype == kBF16) return launch_typed<__bf16, 0>(p, stream);
+  if (act_dtype == kF16 && cache_dtype == kFP8) return launch_typed<_Float16, 1>(p, stream);
+  if (act_dtype == kBF16 && cache_dtype == kFP8) return launch_typed<__bf16, 1>(p, stream);
+  if (act_dtype == kF16 && cache_dtype == kINT8) return launch_typed<_Float16, 2>(p, stream);
+  if (act_dtype == kBF16 && cache_dtype == kINT8) return launch_typed<__bf16, 2>(p, stream);
   return hipErrorInvalidValue;
 }
 

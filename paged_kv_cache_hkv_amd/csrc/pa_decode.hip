@@ -49,9 +49,10 @@
 //     caches) or row reads re-paired by byte permutes (fp8), so a lane's
 //     accumulators all belong to one head and every rescale is lane-local.
 //
-// fp8 (OCP e4m3fn) caches are widened to bf16/fp16 exactly in registers with
-// the gfx950 packed converts; the K scale is folded into the score scale and
-// the V scale into the final division.
+// 8-bit caches -- fp8 (OCP e4m3fn) or int8 codes -- are widened to bf16/fp16
+// exactly in registers (fp8 with the gfx950 packed converts, int8 by way of
+// float32: every code -127..127 is exact); the K scale is folded into the
+// score scale and the V scale into the final division.
 //
 // Mask variants (the alibi_slopes and window_size arguments of the attention
 // call in stop 10 of "Tour: One forward pass"): with a sliding window of W
@@ -212,7 +213,7 @@ __device__ inline void advance(const AttnParams& p, Cursor& c) {
   } while (c.nb == 0);
 }
 
-template <int D, typename CT, int KVB, int HT, int S, int WV, bool MASK>
+template <int D, typename CT, int KVB, bool I8, int HT, int S, int WV, bool MASK>
 __global__ __launch_bounds__(64 * WV) void decode_kernel(AttnParams p) {
   using M = Mfma<CT>;
   using vec8 = typename M::vec8;
@@ -411,8 +412,8 @@ __global__ __launch_bounds__(64 * WV) void decode_kernel(AttnParams p) {
       } else {
         const u32x4 w = *reinterpret_cast<const u32x4*>(st + kread[s / 2]);
         const unsigned d0 = w[2 * (s % 2)], d1 = w[2 * (s % 2) + 1];
-        kop = __builtin_bit_cast(vec8, u32x4{M::from_fp8x2(d0, false), M::from_fp8x2(d0, true),
-                                             M::from_fp8x2(d1, false), M::from_fp8x2(d1, true)});
+        kop = __builtin_bit_cast(vec8, u32x4{widen8x2<CT, I8>(d0, false), widen8x2<CT, I8>(d0, true),
+                                             widen8x2<CT, I8>(d1, false), widen8x2<CT, I8>(d1, true)});
       }
 #pragma unroll
       for (int ht = 0; ht < HT; ++ht) sc[ht] = M::mma16(kop, qop[ht][s], sc[ht]);
@@ -501,7 +502,7 @@ __global__ __launch_bounds__(64 * WV) void decode_kernel(AttnParams p) {
         const unsigned sel = (m & 2) ? 0x07030602u : 0x05010400u;
         const unsigned x01 = perm(w[1][m / 4], w[0][m / 4], sel);
         const unsigned x23 = perm(w[3][m / 4], w[2][m / 4], sel);
-        u32x2 a{M::from_fp8x2(x01, (m & 1) != 0), M::from_fp8x2(x23, (m & 1) != 0)};
+        u32x2 a{widen8x2<CT, I8>(x01, (m & 1) != 0), widen8x2<CT, I8>(x23, (m & 1) != 0)};
         a = u32x2{a[0] & vm0, a[1] & vm1};
 #pragma unroll
         for (int ht = 0; ht < HT; ++ht) acc[ht][m] = M::mma16k16(a, pop[ht], acc[ht][m]);
@@ -668,15 +669,15 @@ constexpr int ring_depth() {
   return kStages < fit ? kStages : fit;
 }
 
-template <int D, typename CT, int KVB, int HT>
+template <int D, typename CT, int KVB, bool I8, int HT>
 hipError_t launch_typed(const AttnParams& p, hipStream_t stream) {
   constexpr int WV = waves_per_wg<D, KVB, HT>();
   constexpr int S = ring_depth<D, KVB, HT>();
   dim3 grid((unsigned)((p.num_workers + WV - 1) / WV));
   if (p.masked) {
-    hipLaunchKernelGGL((decode_kernel<D, CT, KVB, HT, S, WV, true>), grid, dim3(64 * WV), 0, stream, p);
+    hipLaunchKernelGGL((decode_kernel<D, CT, KVB, I8, HT, S, WV, true>), grid, dim3(64 * WV), 0, stream, p);
   } else {
-    hipLaunchKernelGGL((decode_kernel<D, CT, KVB, HT, S, WV, false>), grid, dim3(64 * WV), 0, stream, p);
+    hipLaunchKernelGGL((decode_kernel<D, CT, KVB, I8, HT, S, WV, false>), grid, dim3(64 * WV), 0, stream, p);
   }
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
@@ -685,19 +686,21 @@ hipError_t launch_typed(const AttnParams& p, hipStream_t stream) {
   return hipGetLastError();
 }
 
-template <int D, typename CT, int KVB>
+template <int D, typename CT, int KVB, bool I8>
 hipError_t launch_heads(const AttnParams& p, hipStream_t stream) {
-  if (p.group <= 16) return launch_typed<D, CT, KVB, 1>(p, stream);
-  if (p.group <= 32) return launch_typed<D, CT, KVB, 2>(p, stream);
+  if (p.group <= 16) return launch_typed<D, CT, KVB, I8, 1>(p, stream);
+  if (p.group <= 32) return launch_typed<D, CT, KVB, I8, 2>(p, stream);
   return hipErrorInvalidValue;
 }
 
 template <int D>
 hipError_t launch_dim(const AttnParams& p, int act, int cache, hipStream_t stream) {
-  if (act == kF16 && cache == kF16) return launch_heads<D, _Float16, 2>(p, stream);
-  if (act == kBF16 && cache == kBF16) return launch_heads<D, __bf16, 2>(p, stream);
-  if (act == kF16 && cache == kFP8) return launch_heads<D, _Float16, 1>(p, stream);
-  if (act == kBF16 && cache == kFP8) return launch_heads<D, __bf16, 1>(p, stream);
+  if (act == kF16 && cache == kF16) return launch_heads<D, _Float16, 2, false>(p, stream);
+  if (act == kBF16 && cache == kBF16) return launch_heads<D, __bf16, 2, false>(p, stream);
+  if (act == kF16 && cache == kFP8) return launch_heads<D, _Float16, 1, false>(p, stream);
+  if (act == kBF16 && cache == kFP8) return launch_heads<D, __bf16, 1, false>(p, stream);
+  if (act == kF16 && cache == kINT8) return launch_heads<D, _Float16, 1, true>(p, stream);
+  if (act == kBF16 && cache == kINT8) return launch_heads<D, __bf16, 1, true>(p, stream);
   return hipErrorInvalidValue;
 }
 

@@ -107,6 +107,32 @@ __device__ inline unsigned pack2(float lo, float hi) {
   return __builtin_bit_cast(unsigned, __builtin_convertvector(f32x2{lo, hi}, t2));
 }
 
+// Two 8-bit cache codes -- bytes 2*hi and 2*hi+1 of src -- widened exactly to
+// two 16-bit values of T (one dword, low value first): OCP e4m3fn codes with
+// the packed gfx950 convert, or symmetric int8 codes (every integer in
+// -127..127 is exact in bf16 and fp16).  The cache scale is applied elsewhere.
+template <typename T, bool I8>
+__device__ inline unsigned widen8x2(unsigned src, bool hi_word) {
+  if constexpr (I8) {
+    const int sh = hi_word ? 16 : 0;
+    const float a = (float)(int)(signed char)(src >> sh);
+    const float b = (float)(int)(signed char)(src >> (sh + 8));
+    return pack2<T>(a, b);
+  } else {
+    return Mfma<T>::from_fp8x2(src, hi_word);
+  }
+}
+
+// float32 -> symmetric int8 code (two's complement byte): round to nearest
+// even, saturating to +-127 (-128 is never produced); NaN gives 0.  Clamping
+// first and rounding second equals rounding first and saturating second
+// because +-127 are integers.
+__device__ inline unsigned encode_int8(float y) {
+  if (!(y == y)) return 0u;
+  const float r = __builtin_rintf(fminf(fmaxf(y, -127.f), 127.f));
+  return (unsigned)(int)r & 0xFFu;
+}
+
 // 2^x with the hardware v_exp_f32 (results below 2^-126 flush to zero, which
 // only ever affects softmax weights that are negligible against the max).
 __device__ inline float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }

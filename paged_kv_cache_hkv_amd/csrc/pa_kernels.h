@@ -7,7 +7,7 @@
 
 namespace pa {
 
-enum DType : int { kF16 = 0, kBF16 = 1, kFP8 = 2 };
+enum DType : int { kF16 = 0, kBF16 = 1, kFP8 = 2, kINT8 = 3 };
 
 struct MetadataParams {
   int32_t num_reqs, block_size, max_blocks_per_req, num_tokens_padded, qsl_len;
@@ -105,10 +105,11 @@ struct AttnParams {
 };
 
 // Decode waves per workgroup (= per compute unit: one resident workgroup of
-// independent waves).  fp8 with G > 16 (two MFMA column tiles, 4 KB blocks)
-// has the longest math per block and uses eight; everything else four.
+// independent waves).  8-bit caches (fp8, int8) with G > 16 (two MFMA column
+// tiles, 4 KB blocks) have the longest math per block and use eight;
+// everything else four.
 constexpr int decode_waves_per_cu(int group, int cache_dtype) {
-  return (group > 16 && cache_dtype == kFP8) ? 8 : 4;
+  return (group > 16 && (cache_dtype == kFP8 || cache_dtype == kINT8)) ? 8 : 4;
 }
 
 hipError_t launch_metadata(const MetadataParams& p, hipStream_t stream);

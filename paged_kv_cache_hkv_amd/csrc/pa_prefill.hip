@@ -172,7 +172,7 @@ __device__ inline void load_tile(TileRegs<D, KVB>& regs, const TileCtx& c, int k
   }
 }
 
-template <int D, typename CT, int KVB>
+template <int D, typename CT, int KVB, bool I8>
 __device__ inline void store_tile(const TileRegs<D, KVB>& regs, unsigned short* Ks,
                                   unsigned short* Vt) {
   using TS = TileShape<D, KVB>;
@@ -189,11 +189,11 @@ __device__ inline void store_tile(const TileRegs<D, KVB>& regs, unsigned short* 
       } else {
         const u32x4& w = regs.k[j];
         *reinterpret_cast<u32x4*>(dst) =
-            u32x4{M::from_fp8x2(w[0], false), M::from_fp8x2(w[0], true),
-                  M::from_fp8x2(w[1], false), M::from_fp8x2(w[1], true)};
+            u32x4{widen8x2<CT, I8>(w[0], false), widen8x2<CT, I8>(w[0], true),
+                  widen8x2<CT, I8>(w[1], false), widen8x2<CT, I8>(w[1], true)};
         *reinterpret_cast<u32x4*>(dst + 8) =
-            u32x4{M::from_fp8x2(w[2], false), M::from_fp8x2(w[2], true),
-                  M::from_fp8x2(w[3], false), M::from_fp8x2(w[3], true)};
+            u32x4{widen8x2<CT, I8>(w[2], false), widen8x2<CT, I8>(w[2], true),
+                  widen8x2<CT, I8>(w[3], false), widen8x2<CT, I8>(w[3], true)};
       }
     }
   }
@@ -216,7 +216,7 @@ __device__ inline void store_tile(const TileRegs<D, KVB>& regs, unsigned short* 
         for (int m = 0; m < 8; ++m) {   // d pair (2m, 2m+1) of the 16-element chunk
           unsigned cv[4];
 #pragma unroll
-          for (int i = 0; i < 4; ++i) cv[i] = M::from_fp8x2(v[i][m >> 1], (m & 1) != 0);
+          for (int i = 0; i < 4; ++i) cv[i] = widen8x2<CT, I8>(v[i][m >> 1], (m & 1) != 0);
           const u32x2 lo{perm(cv[1], cv[0], 0x05040100u), perm(cv[3], cv[2], 0x05040100u)};
           const u32x2 hi{perm(cv[1], cv[0], 0x07060302u), perm(cv[3], cv[2], 0x07060302u)};
           *reinterpret_cast<u32x2*>(Vt + (ch * 16 + 2 * m) * TS::VROW + col) = lo;
@@ -227,7 +227,7 @@ __device__ inline void store_tile(const TileRegs<D, KVB>& regs, unsigned short* 
   }
 }
 
-template <int D, typename CT, int KVB, bool MASK>
+template <int D, typename CT, int KVB, bool I8, bool MASK>
 __global__ __launch_bounds__(kThreads, 2) void prefill_kernel(AttnParams p, int hpw) {
   using M = Mfma<CT>;
   using vec8 = typename M::vec8;
@@ -303,7 +303,7 @@ __global__ __launch_bounds__(kThreads, 2) void prefill_kernel(AttnParams p, int 
   TileRegs<D, KVB> regs;
   if (ntiles > kt0) {
     load_tile<D, KVB>(regs, tc, kt0);
-    store_tile<D, CT, KVB>(regs, Ks[0], Vt[0]);
+    store_tile<D, CT, KVB, I8>(regs, Ks[0], Vt[0]);
   }
   __syncthreads();
   for (int kt = kt0; kt < ntiles; ++kt) {
@@ -386,7 +386,7 @@ __global__ __launch_bounds__(kThreads, 2) void prefill_kernel(AttnParams p, int 
         }
       }
     }
-    if (kt + 1 < ntiles) store_tile<D, CT, KVB>(regs, Ks[buf ^ 1], Vt[buf ^ 1]);
+    if (kt + 1 < ntiles) store_tile<D, CT, KVB, I8>(regs, Ks[buf ^ 1], Vt[buf ^ 1]);
     __syncthreads();
   }
 
@@ -849,7 +849,7 @@ int heads_per_wg(int G) {
   return 1;
 }
 
-template <int D, typename CT, int KVB>
+template <int D, typename CT, int KVB, bool I8 = false>
 hipError_t launch_typed(const AttnParams& p, hipStream_t stream) {
   const int hpw = heads_per_wg(p.group);
   const int QB = (KVB == 2 ? 32 * kPPWaves : 128) / hpw;
@@ -865,9 +865,9 @@ hipError_t launch_typed(const AttnParams& p, hipStream_t stream) {
     }
   } else {
     if (p.masked) {
-      hipLaunchKernelGGL((prefill_kernel<D, CT, KVB, true>), grid, dim3(kThreads), 0, stream, p, hpw);
+      hipLaunchKernelGGL((prefill_kernel<D, CT, KVB, I8, true>), grid, dim3(kThreads), 0, stream, p, hpw);
     } else {
-      hipLaunchKernelGGL((prefill_kernel<D, CT, KVB, false>), grid, dim3(kThreads), 0, stream, p, hpw);
+      hipLaunchKernelGGL((prefill_kernel<D, CT, KVB, I8, false>), grid, dim3(kThreads), 0, stream, p, hpw);
     }
   }
   return hipGetLastError();
@@ -879,6 +879,8 @@ hipError_t launch_dim(const AttnParams& p, int act, int cache, hipStream_t strea
   if (act == kBF16 && cache == kBF16) return launch_typed<D, __bf16, 2>(p, stream);
   if (act == kF16 && cache == kFP8) return launch_typed<D, _Float16, 1>(p, stream);
   if (act == kBF16 && cache == kFP8) return launch_typed<D, __bf16, 1>(p, stream);
+  if (act == kF16 && cache == kINT8) return launch_typed<D, _Float16, 1, true>(p, stream);
+  if (act == kBF16 && cache == kINT8) return launch_typed<D, __bf16, 1, true>(p, stream);
   return hipErrorInvalidValue;
 }
 

@@ -76,28 +76,31 @@ __device__ inline void rotate8(const u32x4& xa, const u32x4& xb, const float* c,
   }
 }
 
-// 8 activation-dtype elements -> 8 e4m3fn codes of value * inv
-template <typename T>
+// 8 activation-dtype elements -> 8 codes of value * inv (ENC 1: e4m3fn,
+// 2: int8, as the cache write encodes them)
+template <typename T, int ENC>
 __device__ inline u32x2 encode8(const u32x4& v, float inv) {
   unsigned out[2] = {0u, 0u};
 #pragma unroll
   for (int k = 0; k < 8; ++k) {
     const unsigned short h = (unsigned short)(v[k >> 1] >> (16 * (k & 1)));
-    out[k >> 2] |= encode_e4m3fn(Mfma<T>::to_float(h) * inv) << (8 * (k & 3));
+    const float y = Mfma<T>::to_float(h) * inv;
+    out[k >> 2] |= (ENC == 2 ? encode_int8(y) : encode_e4m3fn(y)) << (8 * (k & 3));
   }
   return u32x2{out[0], out[1]};
 }
 
-template <typename T, bool FP8>
+// ENC: 0 copy (cache in the activation dtype), 1 fp8 e4m3fn, 2 int8
+template <typename T, int ENC>
 __device__ inline void store_chunk(void* cache, int64_t elem, const u32x4& v, float inv) {
-  if constexpr (FP8) {
-    st8(static_cast<unsigned char*>(cache) + elem, encode8<T>(v, inv));
+  if constexpr (ENC != 0) {
+    st8(static_cast<unsigned char*>(cache) + elem, encode8<T, ENC>(v, inv));
   } else {
     st16(static_cast<unsigned short*>(cache) + elem, v);
   }
 }
 
-template <typename T, bool FP8>
+template <typename T, int ENC>
 __global__ __launch_bounds__(kThreads) void rope_cache_write_kernel(RopeParams p) {
   const int D = p.head_dim, R = p.rotary_dim;
   const int R16 = R >> 4, P8 = (D - R) >> 3, D8 = D >> 3;
@@ -155,8 +158,8 @@ __global__ __launch_bounds__(kThreads) void rope_cache_write_kernel(RopeParams p
       st16(base + eb, yb);
     } else {
       const int64_t dst = slot * row + (int64_t)h * D;
-      store_chunk<T, FP8>(p.key_cache, dst + ea, ya, p.k_inv_scale);
-      store_chunk<T, FP8>(p.key_cache, dst + eb, yb, p.k_inv_scale);
+      store_chunk<T, ENC>(p.key_cache, dst + ea, ya, p.k_inv_scale);
+      store_chunk<T, ENC>(p.key_cache, dst + eb, yb, p.k_inv_scale);
     }
     return;
   }
@@ -167,7 +170,7 @@ __global__ __launch_bounds__(kThreads) void rope_cache_write_kernel(RopeParams p
     const int h = u / P8, e = R + 8 * (u % P8);
     const unsigned short* src = static_cast<const unsigned short*>(p.key) + t * p.key_row_stride +
                                 (int64_t)h * D + e;
-    store_chunk<T, FP8>(p.key_cache, slot * row + (int64_t)h * D + e, ld16(src), p.k_inv_scale);
+    store_chunk<T, ENC>(p.key_cache, slot * row + (int64_t)h * D + e, ld16(src), p.k_inv_scale);
     return;
   }
   u -= ukp;
@@ -176,18 +179,18 @@ __global__ __launch_bounds__(kThreads) void rope_cache_write_kernel(RopeParams p
     const int h = u / D8, e = 8 * (u % D8);
     const unsigned short* src = static_cast<const unsigned short*>(p.value) + t * p.value_row_stride +
                                 (int64_t)h * D + e;
-    store_chunk<T, FP8>(p.value_cache, slot * row + (int64_t)h * D + e, ld16(src), p.v_inv_scale);
+    store_chunk<T, ENC>(p.value_cache, slot * row + (int64_t)h * D + e, ld16(src), p.v_inv_scale);
   }
 }
 
-template <typename T, bool FP8>
+template <typename T, int ENC>
 hipError_t launch_typed(const RopeParams& p, hipStream_t stream) {
   const int R16 = p.rotary_dim >> 4, P8 = (p.head_dim - p.rotary_dim) >> 3, D8 = p.head_dim >> 3;
   const int64_t per_token = (int64_t)p.num_q_heads * R16 + (int64_t)p.num_kv_heads * (R16 + P8 + D8);
   const int64_t total = p.num_tokens * per_token;
   if (total == 0) return hipSuccess;
   const int64_t blocks = (total + kThreads - 1) / kThreads;
-  hipLaunchKernelGGL((rope_cache_write_kernel<T, FP8>), dim3((unsigned)blocks), dim3(kThreads), 0,
+  hipLaunchKernelGGL((rope_cache_write_kernel<T, ENC>), dim3((unsigned)blocks), dim3(kThreads), 0,
                      stream, p);
   return hipGetLastError();
 }
@@ -196,10 +199,12 @@ hipError_t launch_typed(const RopeParams& p, hipStream_t stream) {
 
 hipError_t launch_rope_cache_write(const RopeParams& p, int act_dtype, int cache_dtype,
                                    hipStream_t stream) {
-  if (act_dtype == kF16 && cache_dtype == kF16) return launch_typed<_Float16, false>(p, stream);
-  if (act_dtype == kBF16 && cache_dtype == kBF16) return launch_typed<__bf16, false>(p, stream);
-  if (act_dtype == kF16 && cache_dtype == kFP8) return launch_typed<_Float16, true>(p, stream);
-  if (act_dtype == kBF16 && cache_dtype == kFP8) return launch_typed<__bf16, true>(p, stream);
+  if (act_dtype == kF16 && cache_dtype == kF16) return launch_typed<_Float16, 0>(p, stream);
+  if (act_dtype == kBF16 && cache_dtype == kBF16) return launch_typed<__bf16, 0>(p, stream);
+  if (act_dtype == kF16 && cache_dtype == kFP8) return launch_typed<_Float16, 1>(p, stream);
+  if (act_dtype == kBF16 && cache_dtype == kFP8) return launch_typed<__bf16, 1>(p, stream);
+  if (act_dtype == kF16 && cache_dtype == kINT8) return launch_typed<_Float16, 2>(p, stream);
+  if (act_dtype == kBF16 && cache_dtype == kINT8) return launch_typed<__bf16, 2>(p, stream);
   return hipErrorInvalidValue;
 }
 

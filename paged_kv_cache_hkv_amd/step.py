@@ -25,7 +25,7 @@ class PagedAttentionStep:
         self.t = tensors
         dev = tensors.q.device
         act = _ACT[wl.act_dtype]
-        cache = B.PA_FP8_E4M3 if wl.cache_fp8 else act
+        cache = {"act": act, "fp8_e4m3": B.PA_FP8_E4M3, "int8": B.PA_INT8}[wl.cache_kind]
         self.desc = B.make_desc(wl.num_q_heads, wl.num_kv_heads, wl.head_dim, wl.block_size,
                                 act, cache, k_scale=tensors.k_scale, v_scale=tensors.v_scale,
                                 decode_workers=decode_workers, sliding_window=sliding_window,

@@ -2,7 +2,7 @@
 
 This module only draws inputs: request lengths, block tables and tensor
 values.  It holds none of the attention arithmetic (no slot mapping, no
-scatter, no softmax, no fp8 encoder of the method); tests and the benchmark
+scatter, no softmax, no 8-bit encoder of the method); tests and the benchmark
 feed what it draws both to the HIP library and to the oracle.
 
 Workloads (shapes follow the walkthrough pages and the five measured
@@ -31,10 +31,14 @@ activation dtype.  Every block a table lists is filled with such draws; all
 other pool blocks are filled with NaN (0x7F for fp8), so a kernel that reads
 outside the table shows up.  For fp8 caches the per-tensor scale is
 float32(amax / 448) of the drawn values and the stored codes come from
-torch's own float8_e4m3fn cast.
+torch's own float8_e4m3fn cast.  For int8 caches the scale is
+float32(amax / 127) and the stored codes are the drawn values divided by the
+scale, rounded by torch.round and clamped to -127..127: the generator's own
+quantisation (the codes and the scale are simply inputs); unused blocks hold
+-128, a code the write path never produces.
 """
 
-from dataclasses import dataclass, field
+from dataclasses import dataclass, field, replace
 
 import numpy as np
 import torch
@@ -48,7 +52,7 @@ class Workload:
     head_dim: int
     block_size: int
     act_dtype: torch.dtype
-    cache_fp8: bool
+    cache_kind: str               # "act" (the activation dtype), "fp8_e4m3" or "int8"
     pool_blocks: int
     num_computed: np.ndarray      # int32 [R]
     query_lens: np.ndarray        # int32 [R]
@@ -57,6 +61,22 @@ class Workload:
     seed: int
     num_tokens_padded: int = 0
     meta: dict = field(default_factory=dict)
+
+    @property
+    def cache_fp8(self):
+        return self.cache_kind == "fp8_e4m3"
+
+    @property
+    def cache_int8(self):
+        return self.cache_kind == "int8"
+
+    @property
+    def cache_8bit(self):
+        return self.cache_kind in ("fp8_e4m3", "int8")
+
+    @property
+    def cache_elem_bytes(self):
+        return 1 if self.cache_8bit else 2
 
     @property
     def num_reqs(self):
@@ -105,27 +125,33 @@ def block_tables_from_lengths(rng, lengths, block_size, pool_blocks, width=None)
     return table
 
 
-def _finish(name, rng, hq, hkv, d, bs, act, fp8, pool, comp, ql, num_decodes, seed, pad_to=None,
+def _kind(fp8=False, int8=False):
+    if fp8 and int8:
+        raise ValueError("one cache format at a time")
+    return "fp8_e4m3" if fp8 else ("int8" if int8 else "act")
+
+
+def _finish(name, rng, hq, hkv, d, bs, act, kind, pool, comp, ql, num_decodes, seed, pad_to=None,
             width=None, meta=None):
     comp = np.asarray(comp, dtype=np.int32)
     ql = np.asarray(ql, dtype=np.int32)
     lengths = comp.astype(np.int64) + ql
     bt = block_tables_from_lengths(rng, lengths, bs, pool, width)
     T = int(ql.sum())
-    return Workload(name, hq, hkv, d, bs, act, fp8, pool, comp, ql, num_decodes, bt, seed,
+    return Workload(name, hq, hkv, d, bs, act, kind, pool, comp, ql, num_decodes, bt, seed,
                     num_tokens_padded=pad_to if pad_to is not None else T, meta=meta or {})
 
 
 def walkthrough(seed=1):
     rng = np.random.default_rng(seed)
-    return _finish("walkthrough", rng, 8, 8, 64, 16, torch.float16, False, 2048,
+    return _finish("walkthrough", rng, 8, 8, 64, 16, torch.float16, "act", 2048,
                    [540, 129, 0], [1, 1, 298], 2, seed, pad_to=304)
 
 
 def decode_mha(seed=2):
     rng = np.random.default_rng(seed)
     comp = rng.integers(512, 4096, size=64, endpoint=True)
-    return _finish("decode_mha", rng, 32, 32, 128, 16, torch.float16, False, 65536,
+    return _finish("decode_mha", rng, 32, 32, 128, 16, torch.float16, "act", 65536,
                    comp, np.ones(64, np.int32), 64, seed)
 
 
@@ -138,7 +164,7 @@ def decode_gqa(seed=3):
     rng = np.random.default_rng(seed)
     comp = np.rint(np.exp(rng.uniform(np.log(1024), np.log(8192), size=256))).astype(np.int32)
     pool = _pool_twice(comp + 1, 16)
-    return _finish("decode_gqa", rng, 32, 8, 128, 16, torch.bfloat16, False, pool,
+    return _finish("decode_gqa", rng, 32, 8, 128, 16, torch.bfloat16, "act", pool,
                    comp, np.ones(256, np.int32), 256, seed)
 
 
@@ -154,14 +180,24 @@ def chunked_prefill_mix(seed=4, budget=8192, num_chunks=6):
     comp = np.concatenate([c_dec, c_pre]).astype(np.int32)
     ql = np.concatenate([np.ones(num_dec, np.int64), n]).astype(np.int32)
     pool = _pool_twice(comp.astype(np.int64) + ql, 16)
-    return _finish("chunked_prefill_mix", rng, 32, 8, 128, 16, torch.bfloat16, False, pool,
+    return _finish("chunked_prefill_mix", rng, 32, 8, 128, 16, torch.bfloat16, "act", pool,
                    comp, ql, num_dec, seed)
 
 
 def mqa_fp8_long(seed=5):
     rng = np.random.default_rng(seed)
-    return _finish("mqa_fp8_long", rng, 32, 1, 128, 16, torch.bfloat16, True, 131072,
+    return _finish("mqa_fp8_long", rng, 32, 1, 128, 16, torch.bfloat16, "fp8_e4m3", 131072,
                    np.full(32, 32768, np.int32), np.ones(32, np.int32), 32, seed)
+
+
+def with_cache(wl, kind):
+    """The same workload over another cache format ("act", "fp8_e4m3", "int8")."""
+    _kind(kind == "fp8_e4m3", kind == "int8")
+    if kind not in ("act", "fp8_e4m3", "int8"):
+        raise ValueError(kind)
+    base = wl.name.replace("_fp8", "")
+    suffix = "" if kind == "act" else "_" + kind.split("_")[0]
+    return replace(wl, cache_kind=kind, name=base + suffix)
 
 
 CONFIGS = {
@@ -174,7 +210,7 @@ CONFIGS = {
 
 
 def random_batch(seed, decode_cached=(), prefills=(), hq=8, hkv=2, d=128, act=torch.bfloat16,
-                 fp8=False, pool=None, pad=0, width=None, block_size=16):
+                 fp8=False, pool=None, pad=0, width=None, block_size=16, int8=False):
     """A small mixed batch: decodes (cached lengths) first, then (cached, new) prefills."""
     rng = np.random.default_rng(seed)
     comp = list(decode_cached) + [c for c, _ in prefills]
@@ -184,7 +220,8 @@ def random_batch(seed, decode_cached=(), prefills=(), hq=8, hkv=2, d=128, act=to
     if pool is None:
         pool = max(64, 2 * need + 16)
     T = int(sum(ql))
-    return _finish(f"random{seed}", rng, hq, hkv, d, block_size, act, fp8, pool, comp, ql,
+    return _finish(f"random{seed}", rng, hq, hkv, d, block_size, act, _kind(fp8, int8), pool,
+                   comp, ql,
                    len(decode_cached), seed, pad_to=T + pad, width=width)
 
 
@@ -193,7 +230,7 @@ class Tensors:
     q: torch.Tensor              # [T_pad, Hq, D] act dtype
     k_new: torch.Tensor          # [T_pad, Hkv, D] act dtype
     v_new: torch.Tensor
-    key_cache: torch.Tensor      # [NB, bs, Hkv, D] act dtype or uint8 (fp8 codes)
+    key_cache: torch.Tensor      # [NB, bs, Hkv, D] act dtype, uint8 (fp8 codes) or int8
     value_cache: torch.Tensor
     num_computed: torch.Tensor   # int32 [R]
     query_lens: torch.Tensor     # int32 [R]
@@ -222,11 +259,14 @@ def make_tensors(wl, device, poison=True, chunk_blocks=8192):
     used = np.unique(wl.block_tables[wl.block_tables >= 0]).astype(np.int64)
     used_t = torch.from_numpy(used).to(device)
     pool_shape = (wl.pool_blocks, bs, hkv, d)
-    if wl.cache_fp8:
-        kc = torch.empty(pool_shape, dtype=torch.uint8, device=device)
-        vc = torch.empty(pool_shape, dtype=torch.uint8, device=device)
-        kc.fill_(0x7F if poison else 0)
-        vc.fill_(0x7F if poison else 0)
+    if wl.cache_8bit:
+        fp8 = wl.cache_fp8
+        code_max = 448.0 if fp8 else 127.0
+        cdt = torch.uint8 if fp8 else torch.int8
+        kc = torch.empty(pool_shape, dtype=cdt, device=device)
+        vc = torch.empty(pool_shape, dtype=cdt, device=device)
+        kc.fill_((0x7F if fp8 else -128) if poison else 0)
+        vc.fill_((0x7F if fp8 else -128) if poison else 0)
         # amax over every drawn value of the tensor (pool blocks and new tokens)
         scales = []
         for cache, new32 in ((kc, k_new32), (vc, v_new32)):
@@ -236,14 +276,17 @@ def make_tensors(wl, device, poison=True, chunk_blocks=8192):
                 ids = used_t[lo:lo + chunk_blocks]
                 vals = _randn(gen, (ids.numel(), bs, hkv, d), device).to(act).float()
                 amax = torch.maximum(amax, vals.abs().max())
-            scale = float(np.float32(amax.item()) / np.float32(448.0))
+            scale = float(np.float32(amax.item()) / np.float32(code_max))
             gen.set_state(state)
             inv = np.float32(1.0) / np.float32(scale)
             for lo in range(0, used.size, chunk_blocks):
                 ids = used_t[lo:lo + chunk_blocks]
                 vals = _randn(gen, (ids.numel(), bs, hkv, d), device).to(act).float()
-                y = torch.clamp(vals * float(inv), -448.0, 448.0)
-                cache[ids] = y.to(torch.float8_e4m3fn).view(torch.uint8)
+                if fp8:
+                    y = torch.clamp(vals * float(inv), -448.0, 448.0)
+                    cache[ids] = y.to(torch.float8_e4m3fn).view(torch.uint8)
+                else:
+                    cache[ids] = torch.clamp(torch.round(vals / scale), -127, 127).to(torch.int8)
             scales.append(scale)
         k_scale, v_scale = scales
     else:

@@ -21,7 +21,13 @@ def act_name(dtype):
 
 
 def tol_of(wl):
+    # int8 codes are integers of at most 8 bits, exact in both bf16 and fp16, so
+    # an int8 cache adds no rounding beyond the activation dtype's
     return TOL["fp8"] if wl.cache_fp8 else TOL[act_name(wl.act_dtype)]
+
+
+def oracle_cache_dtype(wl):
+    return act_name(wl.act_dtype) if wl.cache_kind == "act" else wl.cache_kind
 
 
 def bits16(t):
@@ -32,8 +38,8 @@ def bits8(t):
     return t.detach().contiguous().view(torch.uint8).cpu().numpy()
 
 
-def cache_bits(t, fp8):
-    return bits8(t) if fp8 else bits16(t)
+def cache_bits(t, one_byte):
+    return bits8(t) if one_byte else bits16(t)
 
 
 def oracle_metadata(wl, qsl_len=None):
@@ -55,9 +61,9 @@ class Snapshot:
         self.ids = np.array(sorted(ids), dtype=np.int64)
         self.local = {int(b): i for i, b in enumerate(self.ids)}
         idx = torch.from_numpy(self.ids).to(tensors.key_cache.device)
-        fp8 = wl.cache_fp8
-        self.kbits = cache_bits(tensors.key_cache.index_select(0, idx), fp8)
-        self.vbits = cache_bits(tensors.value_cache.index_select(0, idx), fp8)
+        one = wl.cache_8bit
+        self.kbits = cache_bits(tensors.key_cache.index_select(0, idx), one)
+        self.vbits = cache_bits(tensors.value_cache.index_select(0, idx), one)
 
 
 def oracle_outputs(wl, tensors, snapshot, requests, qsl_len=None, sliding_window=0,
@@ -79,7 +85,7 @@ def oracle_outputs(wl, tensors, snapshot, requests, qsl_len=None, sliding_window
             local_slots.append(snapshot.local[s // bs] * bs + s % bs)
     T = max(wl.num_tokens_padded, wl.num_tokens)
     kb, vb = bits16(tensors.k_new[:T]), bits16(tensors.v_new[:T])
-    cache_dt = "fp8_e4m3" if wl.cache_fp8 else act
+    cache_dt = oracle_cache_dtype(wl)
     k_inv = np.float32(1.0) / np.float32(tensors.k_scale)
     v_inv = np.float32(1.0) / np.float32(tensors.v_scale)
     kc, vc = OC.scatter(snapshot.kbits, snapshot.vbits, kb, vb, local_slots, bs,

@@ -69,6 +69,10 @@ def _write(desc, num_tokens=4, key=FAKE, stride=1024, kc=FAKE):
     (dict(act_dtype=B.PA_F16, cache_dtype=B.PA_BF16), B.PA_ERR_UNSUPPORTED),
     (dict(cache_dtype=B.PA_FP8_E4M3, k_scale=0.0), B.PA_ERR_INVALID_ARG),
     (dict(cache_dtype=B.PA_FP8_E4M3, v_scale=float("nan")), B.PA_ERR_INVALID_ARG),
+    (dict(act_dtype=B.PA_INT8), B.PA_ERR_UNSUPPORTED),
+    (dict(cache_dtype=B.PA_INT8, k_scale=-1.0), B.PA_ERR_INVALID_ARG),
+    (dict(cache_dtype=B.PA_INT8, v_scale=float("inf")), B.PA_ERR_INVALID_ARG),
+    (dict(cache_dtype=4), B.PA_ERR_INVALID_ARG),
     (dict(decode_workers=-1), B.PA_ERR_INVALID_ARG),
     (dict(softmax_scale=float("inf")), B.PA_ERR_INVALID_ARG),
 ])

@@ -30,9 +30,9 @@ def _need_gpu():
 
 def _desc(wl, t):
     act = B.PA_F16 if wl.act_dtype == torch.float16 else B.PA_BF16
+    cache = {"act": act, "fp8_e4m3": B.PA_FP8_E4M3, "int8": B.PA_INT8}[wl.cache_kind]
     return B.make_desc(wl.num_q_heads, wl.num_kv_heads, wl.head_dim, wl.block_size, act,
-                       B.PA_FP8_E4M3 if wl.cache_fp8 else act, k_scale=t.k_scale,
-                       v_scale=t.v_scale)
+                       cache, k_scale=t.k_scale, v_scale=t.v_scale)
 
 
 def _pairs(rng, n_src, n_dst, n, same_pool=False):
@@ -59,6 +59,8 @@ WORKLOADS = {
     "walkthrough_f16": lambda: S.CONFIGS["walkthrough"](),
     "gqa_bf16_fp8": lambda: S.random_batch(41, [2, 3], [(5, 300), (0, 70)], hq=8, hkv=2, d=128,
                                            act=torch.bfloat16, fp8=True),
+    "mqa_f16_int8": lambda: S.random_batch(42, [2, 40], [(5, 300)], hq=8, hkv=1, d=64,
+                                           act=torch.float16, int8=True),
 }
 
 
@@ -68,7 +70,7 @@ def test_copy_inside_one_pool(name, pairs_on_host):
     _need_gpu()
     wl = WORKLOADS[name]()
     t = S.make_tensors(wl, DEV, poison=False)
-    fp8 = wl.cache_fp8
+    fp8 = wl.cache_8bit
     k0, v0 = cache_bits(t.key_cache, fp8), cache_bits(t.value_cache, fp8)
     nb = k0.shape[0]
     rng = np.random.default_rng(7)
@@ -88,7 +90,7 @@ def test_swap_out_then_in(name):
     _need_gpu()
     wl = WORKLOADS[name]()
     t = S.make_tensors(wl, DEV, poison=False)
-    fp8 = wl.cache_fp8
+    fp8 = wl.cache_8bit
     desc = _desc(wl, t)
     k0, v0 = cache_bits(t.key_cache, fp8), cache_bits(t.value_cache, fp8)
     nb = k0.shape[0]

@@ -2,10 +2,10 @@
 pa_prefill_varlen against the oracle (oracle/attention.py), through the C ABI.
 
 Same bars as the plain path: max-abs within 5e-3 (fp16), 2e-2 (bf16), 6e-2
-(fp8 K/V).  Windows from 1 key (the row's own value) through windows shorter
+(fp8 K/V), the activation dtype's for int8 K/V.  Windows from 1 key (the row's own value) through windows shorter
 than a block, spanning block and 64-key tile edges, to longer than every
 sequence; ALiBi alone and with a window; MHA, GQA, MQA with 32 query heads
-per K/V head; 16-bit and fp8 caches; chunked prefills with cached prefixes
+per K/V head; 16-bit, fp8 and int8 caches; chunked prefills with cached prefixes
 and decodes in one batch.
 """
 
@@ -56,10 +56,10 @@ def _check(wl, window, alibi, workers=0, requests=None):
     assert err <= tol, (wl.name, window, alibi, err, tol)
 
 
-def _mixed(seed, hq, hkv, act, fp8):
+def _mixed(seed, hq, hkv, act, fp8, int8=False):
     # decodes (cached lengths incl. block edges) then chunked prefills (cached, new)
     return S.random_batch(seed, [0, 15, 16, 63, 64, 200, 700], [(0, 1), (0, 70), (40, 129), (300, 33)],
-                          hq=hq, hkv=hkv, d=128, act=act, fp8=fp8, pad=3)
+                          hq=hq, hkv=hkv, d=128, act=act, fp8=fp8, int8=int8, pad=3)
 
 
 @pytest.mark.parametrize("window", [1, 7, 16, 64, 100, 5000])
@@ -96,3 +96,9 @@ def test_decode_gqa_full_size_sampled():
     ALiBi: sampled requests against the oracle."""
     wl = S.CONFIGS["decode_gqa"]()
     _check(wl, 1024, True, requests=[0, 37, 128, 255])
+
+
+@pytest.mark.parametrize("window,alibi", [(0, True), (33, True), (100, False)])
+@pytest.mark.parametrize("hq,hkv,act", [(8, 2, torch.bfloat16), (32, 1, torch.float16)])
+def test_int8_cache(window, alibi, hq, hkv, act):
+    _check(_mixed(60 + hq, hq, hkv, act, False, int8=True), window, alibi)

@@ -2,7 +2,8 @@
 
 Bars: metadata and cache bytes bit-exact; attention max-abs within 5e-3
 (fp16), 2e-2 (bf16), 6e-2 (fp8 K/V, the oracle dequantising the identical
-codes).  Small shapes compare every output row; the five measured workloads
+codes); int8 K/V keep the activation dtype's bar (every code is exact in
+bf16 and fp16, so the cache format adds no rounding of its own).  Small shapes compare every output row; the five measured workloads
 run at full size in the launch configuration the benchmark times, and compare
 sampled requests (the oracle computes them one by one).
 """
@@ -17,8 +18,8 @@ from paged_kv_cache_hkv_amd.step import PagedAttentionStep
 from oracle import cache as OC
 from oracle import codecs as OD
 
-from harness import (Snapshot, act_name, bits16, cache_bits, compare, oracle_metadata,
-                     oracle_outputs, tol_of)
+from harness import (Snapshot, act_name, bits16, cache_bits, compare, oracle_cache_dtype,
+                     oracle_metadata, oracle_outputs, tol_of)
 
 pytestmark = pytest.mark.gpu
 
@@ -78,16 +79,18 @@ def test_metadata_bit_exact(wl_fn):
 
 # ------------------------------------------------------------- cache write --
 
-@pytest.mark.parametrize("act,fp8", [(torch.float16, False), (torch.bfloat16, False),
-                                     (torch.bfloat16, True), (torch.float16, True)])
+@pytest.mark.parametrize("act,kind", [(torch.float16, "act"), (torch.bfloat16, "act"),
+                                      (torch.bfloat16, "fp8"), (torch.float16, "fp8"),
+                                      (torch.bfloat16, "int8"), (torch.float16, "int8")])
 @pytest.mark.parametrize("d", [64, 128])
-def test_cache_write_bit_exact(act, fp8, d):
+def test_cache_write_bit_exact(act, kind, d):
     _need_gpu()
     wl = S.random_batch(21 + d, [3, 16, 200], [(0, 37), (16, 16)], hq=8, hkv=4, d=d, act=act,
-                        fp8=fp8, pad=5)
+                        fp8=kind == "fp8", int8=kind == "int8", pad=5)
     t = S.make_tensors(wl, DEV, poison=True)
-    before_k = cache_bits(t.key_cache, fp8)
-    before_v = cache_bits(t.value_cache, fp8)
+    one = wl.cache_8bit
+    before_k = cache_bits(t.key_cache, one)
+    before_v = cache_bits(t.value_cache, one)
     step = PagedAttentionStep(wl, t)
     step.metadata()
     step.cache_write()
@@ -97,12 +100,12 @@ def test_cache_write_bit_exact(act, fp8, d):
     act_n = act_name(act)
     want_k, want_v = OC.scatter(before_k, before_v, bits16(t.k_new[:T]), bits16(t.v_new[:T]),
                                 slots, wl.block_size, act_dtype=act_n,
-                                cache_dtype="fp8_e4m3" if fp8 else act_n,
+                                cache_dtype=oracle_cache_dtype(wl),
                                 k_inv_scale=np.float32(1) / np.float32(t.k_scale),
                                 v_inv_scale=np.float32(1) / np.float32(t.v_scale), num_tokens=T)
     # every byte of the pool: written slots equal the oracle, all others unchanged
-    assert np.array_equal(cache_bits(t.key_cache, fp8), want_k)
-    assert np.array_equal(cache_bits(t.value_cache, fp8), want_v)
+    assert np.array_equal(cache_bits(t.key_cache, one), want_k)
+    assert np.array_equal(cache_bits(t.value_cache, one), want_v)
 
 
 def test_fp8_encode_exhaustive_on_gpu():
@@ -126,6 +129,29 @@ def test_fp8_encode_exhaustive_on_gpu():
             assert np.array_equal(got, want), (act, scale, np.nonzero(got != want)[0][:10])
 
 
+def test_int8_encode_exhaustive_on_gpu():
+    """All 65536 bf16 and fp16 inputs (NaN, infinities, ties included) through
+    pa_cache_write's int8 encoder vs the oracle's."""
+    _need_gpu()
+    for act in (torch.bfloat16, torch.float16):
+        for scale in (0.125, 0.0137, 3.0e-5):
+            bits = torch.arange(65536, dtype=torch.int32).to(torch.int16)
+            x = bits.view(act).reshape(512, 1, 128).to(DEV)
+            kc = torch.full((32, 16, 1, 128), -128, dtype=torch.int8, device=DEV)
+            vc = torch.full_like(kc, -128)
+            slots = torch.arange(512, dtype=torch.int64, device=DEV)
+            desc = B.make_desc(8, 1, 128, 16, B.PA_BF16 if act == torch.bfloat16 else B.PA_F16,
+                               B.PA_INT8, k_scale=scale, v_scale=scale)
+            B.pa_cache_write(desc, x, x, slots, kc, vc)
+            torch.cuda.synchronize()
+            got = kc.reshape(-1).cpu().numpy()
+            with np.errstate(invalid="ignore"):
+                xf = OD.decode(bits.numpy().view(np.uint16), act_name(act)).astype(np.float32)
+            want = OD.int8_encode(xf, np.float32(1) / np.float32(scale))
+            assert np.array_equal(got, want), (act, scale, np.nonzero(got != want)[0][:10])
+            assert np.array_equal(vc.reshape(-1).cpu().numpy(), want)
+
+
 # -------------------------------------------------------- attention parity --
 
 def test_walkthrough_parity():
@@ -138,17 +164,19 @@ def test_walkthrough_parity():
 
 SHAPES = [(8, 8, 64), (32, 8, 128), (32, 1, 128), (32, 32, 128), (16, 2, 64), (12, 4, 128),
           (24, 1, 64)]
-DTYPES = [(torch.float16, False), (torch.bfloat16, False), (torch.bfloat16, True),
-          (torch.float16, True)]
+DTYPES = [(torch.float16, "act"), (torch.bfloat16, "act"), (torch.bfloat16, "fp8"),
+          (torch.float16, "fp8"), (torch.bfloat16, "int8"), (torch.float16, "int8")]
 
 
 @pytest.mark.parametrize("hq,hkv,d", SHAPES)
-@pytest.mark.parametrize("act,fp8", DTYPES)
-def test_small_mixed_parity(hq, hkv, d, act, fp8):
-    seed = hq * 100 + hkv * 10 + d + (7 if fp8 else 0) + (3 if act == torch.float16 else 0)
+@pytest.mark.parametrize("act,kind", DTYPES)
+def test_small_mixed_parity(hq, hkv, d, act, kind):
+    seed = (hq * 100 + hkv * 10 + d + {"act": 0, "fp8": 7, "int8": 11}[kind]
+            + (3 if act == torch.float16 else 0))
     decodes = [0, 14, 15, 16, 31, 32, 33, 298, 540, 1000]
     prefills = [(0, 1), (0, 17), (7, 40), (16, 100), (100, 129), (0, 298), (33, 64)]
-    wl = S.random_batch(seed, decodes, prefills, hq=hq, hkv=hkv, d=d, act=act, fp8=fp8, pad=3)
+    wl = S.random_batch(seed, decodes, prefills, hq=hq, hkv=hkv, d=d, act=act,
+                        fp8=kind == "fp8", int8=kind == "int8", pad=3)
     _run_and_check(wl)
 
 
@@ -162,11 +190,17 @@ def test_long_decode_split_parity(workers):
     _run_and_check(wl, workers=workers)
 
 
-@pytest.mark.parametrize("name,nsample", [("decode_mha", 8), ("decode_gqa", 8),
-                                          ("chunked_prefill_mix", 10), ("mqa_fp8_long", 4)])
-def test_full_config_sampled(name, nsample):
+@pytest.mark.parametrize("name,nsample,kind", [
+    ("decode_mha", 8, None), ("decode_gqa", 8, None), ("chunked_prefill_mix", 10, None),
+    ("mqa_fp8_long", 4, None),
+    # the same shapes over an int8 cache
+    ("decode_gqa", 6, "int8"), ("chunked_prefill_mix", 6, "int8"), ("mqa_fp8_long", 3, "int8"),
+])
+def test_full_config_sampled(name, nsample, kind):
     """Full-size workload, as benchmarked; the oracle checks sampled requests."""
     wl = S.CONFIGS[name]()
+    if kind is not None:
+        wl = S.with_cache(wl, kind)
     rng = np.random.default_rng(1234)
     nd = wl.num_decodes
     req = set(rng.choice(nd, size=min(nsample, nd), replace=False).tolist()) if nd else set()

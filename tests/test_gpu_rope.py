@@ -16,7 +16,7 @@ from oracle import rope as OR
 from paged_kv_cache_hkv_amd import binding as B
 from paged_kv_cache_hkv_amd import synth as S
 
-from harness import act_name, bits16, cache_bits, oracle_metadata
+from harness import act_name, bits16, cache_bits, oracle_cache_dtype, oracle_metadata
 
 pytestmark = pytest.mark.gpu
 DEV = "cuda"
@@ -41,15 +41,16 @@ def _check(wl, rotary_dim, neox, base=10000.0, max_position=None, bad_positions=
         pos[i] = v
     table = OR.cos_sin_table(max_position, rotary_dim, base)
     act = act_name(wl.act_dtype)
-    fp8 = wl.cache_fp8
-    cache_dt = "fp8_e4m3" if fp8 else act
+    fp8 = wl.cache_8bit          # one-byte cache elements
+    cache_dt = oracle_cache_dtype(wl)
+    cache_code = {"act": B.PA_F16 if act == "f16" else B.PA_BF16, "fp8_e4m3": B.PA_FP8_E4M3,
+                  "int8": B.PA_INT8}[wl.cache_kind]
     q0, k0, v0 = bits16(t.q), bits16(t.k_new), bits16(t.v_new)
     if whole_pool:
         kc0, vc0 = cache_bits(t.key_cache, fp8), cache_bits(t.value_cache, fp8)
     desc = B.make_desc(wl.num_q_heads, wl.num_kv_heads, wl.head_dim, wl.block_size,
                        B.PA_F16 if act == "f16" else B.PA_BF16,
-                       B.PA_FP8_E4M3 if fp8 else (B.PA_F16 if act == "f16" else B.PA_BF16),
-                       k_scale=t.k_scale, v_scale=t.v_scale)
+                       cache_code, k_scale=t.k_scale, v_scale=t.v_scale)
     print(f"[rope] {wl.name} rotary_dim={rotary_dim} neox={neox} tokens={Tp}", flush=True)
     B.pa_rope_cache_write(desc, torch.from_numpy(pos).to(DEV), torch.from_numpy(table).to(DEV),
                           rotary_dim, neox, t.q, t.k_new, t.v_new,
@@ -92,11 +93,11 @@ def test_walkthrough(rotary_dim, neox):
 
 
 @pytest.mark.parametrize("act", [torch.float16, torch.bfloat16])
-@pytest.mark.parametrize("fp8", [False, True])
+@pytest.mark.parametrize("kind", ["act", "fp8", "int8"])
 @pytest.mark.parametrize("neox", [True, False])
-def test_gqa_batches(act, fp8, neox):
+def test_gqa_batches(act, kind, neox):
     wl = S.random_batch(31, [3, 16, 200], [(0, 37), (16, 16), (5, 100)], hq=8, hkv=2, d=128,
-                        act=act, fp8=fp8, pad=5)
+                        act=act, fp8=kind == "fp8", int8=kind == "int8", pad=5)
     _check(wl, 128, neox, base=500000.0)
 
 

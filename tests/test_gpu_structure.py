@@ -38,7 +38,7 @@ def _slot(wl, r, j):
     return int(wl.block_tables[r, j // wl.block_size]) * wl.block_size + j % wl.block_size
 
 
-@pytest.mark.parametrize("case", ["gqa_bf16", "mqa_fp8", "mha_f16"])
+@pytest.mark.parametrize("case", ["gqa_bf16", "mqa_fp8", "mha_f16", "gqa_int8"])
 def test_spike_positions(case):
     _need_gpu()
     if case == "gqa_bf16":
@@ -47,6 +47,9 @@ def test_spike_positions(case):
     elif case == "mqa_fp8":
         cached = [32768, 32768, 4095, 1]
         wl = S.random_batch(6, cached, [], hq=32, hkv=1, d=128, act=torch.bfloat16, fp8=True)
+    elif case == "gqa_int8":
+        cached = [8191, 30000, 100, 0]
+        wl = S.random_batch(9, cached, [], hq=32, hkv=4, d=128, act=torch.float16, int8=True)
     else:
         cached = [2047, 3000, 64, 17]
         wl = S.random_batch(7, cached, [], hq=16, hkv=16, d=64, act=torch.float16)
@@ -65,6 +68,8 @@ def test_spike_positions(case):
     def enc(x, scale):
         if wl.cache_fp8:
             return torch.clamp(x / scale, -448, 448).to(torch.float8_e4m3fn).view(torch.uint8)
+        if wl.cache_int8:
+            return torch.clamp(torch.round(x / scale), -127, 127).to(torch.int8)
         return x.to(wl.act_dtype)
 
     positions = {}
@@ -92,6 +97,8 @@ def test_spike_positions(case):
         mk = marker[r]
         if wl.cache_fp8:   # the marker as stored: its e4m3 code times the scale
             mk = enc(mk, t.v_scale).view(torch.float8_e4m3fn).float() * t.v_scale
+        elif wl.cache_int8:
+            mk = enc(mk, t.v_scale).float() * t.v_scale
         want = mk.repeat_interleave(G, dim=0)                 # [Hq, D]
         got = out[qsl[r]]
         err = float((got - want).abs().max())
@@ -120,11 +127,11 @@ def _permuted(wl, t, seed):
     return wl2, t2
 
 
-@pytest.mark.parametrize("fp8", [False, True])
-def test_block_permutation_bit_identical(fp8):
+@pytest.mark.parametrize("kind", ["act", "fp8", "int8"])
+def test_block_permutation_bit_identical(kind):
     _need_gpu()
     wl = S.random_batch(8, [100, 3000, 5000, 17], [(0, 200), (300, 130)], hq=32, hkv=8, d=128,
-                        act=torch.bfloat16, fp8=fp8)
+                        act=torch.bfloat16, fp8=kind == "fp8", int8=kind == "int8")
     t = S.make_tensors(wl, DEV)
     wl2, t2 = _permuted(wl, t, 3)
     a = PagedAttentionStep(wl, t)
