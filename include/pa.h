@@ -97,9 +97,9 @@ typedef enum pa_dtype {
  * "vLLM 推理全流程深度解析" PagedAttention section names as a throughput lever.
  *
  * decode_workers: number of waves pa_decode divides its key stream among
- * (see pa_decode); 0 lets the library choose (four per compute unit of the
- * current device).  Otherwise 1 .. 2^20; the result does not depend on it
- * beyond float32 rounding.
+ * (see pa_decode); 0 lets the library choose (per compute unit of the
+ * current device: four for 16-bit caches, eight for 8-bit ones).  Otherwise
+ * 1 .. 2^20; the result does not depend on it beyond float32 rounding.
  *
  * Mask variants of pa_decode and pa_prefill_varlen (the alibi_slopes and
  * window_size arguments of the attention call in stop 10 of "Tour: One
@@ -283,6 +283,10 @@ pa_status pa_copy_blocks(const pa_attn_desc* desc,
  * PA_ERR_WORKSPACE_TOO_SMALL), required whenever the range is not empty.
  * Its contents need no initialisation and are scratch after the call; two
  * calls in flight at once need two workspaces.
+ * PA_ERR_UNSUPPORTED (besides the descriptor's own limits) when a block of
+ * one K/V cache spans 2^32 bytes or more (16 * num_kv_heads * head_dim *
+ * element size), or when (req_end - req_begin) * num_kv_heads *
+ * max_blocks_per_req exceeds the worker count times 2^31 - 1.
  */
 pa_status pa_decode(const pa_attn_desc* desc, int32_t req_begin, int32_t req_end,
                     const void* q, int64_t q_row_stride,

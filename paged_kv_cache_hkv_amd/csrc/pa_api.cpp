@@ -58,8 +58,7 @@ pa_status check_desc(const pa_attn_desc* d) {
 // resident for the whole launch) unless the descriptor fixes the count.
 int decode_workers(const pa_attn_desc* d) {
   if (d->decode_workers > 0) return d->decode_workers;
-  const int per_cu = pa::decode_waves_per_cu(d->num_q_heads / d->num_kv_heads,
-                                             d->cache_dtype == PA_FP8_E4M3 ? pa::kFP8
+  const int per_cu = pa::decode_waves_per_cu(d->cache_dtype == PA_FP8_E4M3 ? pa::kFP8
                                              : d->cache_dtype == PA_INT8   ? pa::kINT8
                                                                            : pa::kF16);
   int dev = 0, cus = 0;
@@ -396,6 +395,15 @@ pa_status pa_decode(const pa_attn_desc* desc, int32_t req_begin, int32_t req_end
   const int num_reqs = req_end - req_begin;
   if (num_reqs == 0) return PA_OK;
   const DecodePlan pl = plan_decode(desc, num_reqs);
+  // the kernel keeps a block's byte offset in 32 bits and each worker's share
+  // of the (request, K/V head, block) stream below 2^31 units
+  if ((int64_t)16 * desc->num_kv_heads * desc->head_dim * elem_bytes(desc->cache_dtype) > 0xFFFFFFFFll) {
+    return PA_ERR_UNSUPPORTED;
+  }
+  if ((double)num_reqs * desc->num_kv_heads * max_blocks_per_req >
+      (double)pl.workers * 2147483647.0) {
+    return PA_ERR_UNSUPPORTED;
+  }
   if (workspace == nullptr || workspace_bytes < pl.ws_bytes) return PA_ERR_WORKSPACE_TOO_SMALL;
   if (!aligned16(workspace)) return PA_ERR_INVALID_ARG;
   pa::AttnParams p = make_params(desc, req_begin, req_end, q, q_row_stride, query_start_loc,

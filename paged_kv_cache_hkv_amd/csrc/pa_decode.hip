@@ -76,6 +76,7 @@ constexpr int kLdsBudget = 160 * 1024;    // LDS of one compute unit
 #define PA_DECODE_STAGES 3
 #endif
 constexpr int kStages = PA_DECODE_STAGES; // LDS ring depth per wave (where it fits)
+constexpr int kStages8 = 4;               // the same for 8-bit caches (half-size blocks)
 
 // Token of MFMA row i (0..15) of a block.  Any permutation works as long as
 // scores and V use the same one; this one makes the four lane groups that
@@ -99,19 +100,20 @@ struct Ring {
   }
 };
 
-// Wait until at most n (wave-uniform, 0 .. 3) blocks' copies are in flight.
+// Wait until at most n (wave-uniform, clamped to N) blocks' copies are in
+// flight.
 // Copies of query rows are issued before the block they belong to, so they
 // only make the count conservative.
-template <int IPB>
+template <int IPB, int N>
 __device__ inline void wait_blocks(int n) {
-  if (n >= 3) {
-    wait_vmcnt<3 * IPB>();
-  } else if (n == 2) {
-    wait_vmcnt<2 * IPB>();
-  } else if (n == 1) {
-    wait_vmcnt<IPB>();
-  } else {
+  if constexpr (N == 0) {
     wait_vmcnt<0>();
+  } else {
+    if (n >= N) {
+      wait_vmcnt<N * IPB>();
+    } else {
+      wait_blocks<IPB, N - 1>(n);
+    }
   }
 }
 
@@ -183,6 +185,7 @@ struct Cursor {
   int rr, kvh, b, nb;
   int s_eff, q_row;
   int b0, lo;
+  const int32_t* row;   // the request's block-table entries from block b0 on
 };
 
 // Fill the request fields of c for request c.rr (wave-uniform loads).
@@ -196,6 +199,7 @@ __device__ inline void load_request(const AttnParams& p, Cursor& c) {
   c.lo = first_key(p, s);
   c.b0 = c.lo / kBlock;
   c.nb = (q1 - q0 == 1 && s > 0) ? (s + kBlock - 1) / kBlock - c.b0 : 0;
+  c.row = p.block_tables + (int64_t)r * p.max_blocks_per_req + c.b0;
 }
 
 // Advance by one unit (wave-uniform); skips requests that stream nothing.
@@ -224,7 +228,7 @@ __global__ __launch_bounds__(64 * WV) void decode_kernel(AttnParams p) {
   constexpr int kStage = 2 * R::kBlkBytes; // K | V of one block
   constexpr int kQCap = HT * 16 * D * 2;   // query rows of one segment (<= 16*HT heads)
   constexpr int kWaveBytes = S * kStage + kQCap;
-  static_assert(S >= 2 && S <= 4, "ring depth");
+  static_assert(S >= 2 && S <= 8, "ring depth");
   static_assert(WV * kWaveBytes <= kLdsBudget, "rings exceed LDS");
   __shared__ __attribute__((aligned(1024))) unsigned char lds[WV * kWaveBytes];
 
@@ -246,8 +250,9 @@ __global__ __launch_bounds__(64 * WV) void decode_kernel(AttnParams p) {
     T += readlane64(wave_scan(v), 63);
   }
   const int64_t g0 = range_begin(worker, T, W);
-  const int64_t n = range_begin(worker + 1, T, W) - g0;
-  Cursor cur{0, 0, 0, 0, 0, 0, 0, 0};
+  // units of this worker: the host keeps every share below 2^31
+  const int n = (int)(range_begin(worker + 1, T, W) - g0);
+  Cursor cur{0, 0, 0, 0, 0, 0, 0, 0, nullptr};
   {
     // worker 0 also publishes the exclusive prefix for the reduce kernel
     int64_t run = 0;
@@ -275,8 +280,10 @@ __global__ __launch_bounds__(64 * WV) void decode_kernel(AttnParams p) {
   }
 
   const int64_t tok_stride = (int64_t)Hkv * D * KVB;     // bytes between slots
-  const int64_t blk_stride = tok_stride * kBlock;        // bytes between blocks
-  const int64_t num_blocks = p.num_blocks;
+  // bytes between blocks (below 2^32, checked on the host)
+  const uint32_t blk_stride = (uint32_t)(tok_stride * kBlock);
+  // a table entry is a pool block when (unsigned) id < nblk
+  const uint32_t nblk = p.num_blocks > 0x7FFFFFFF ? 0x80000000u : (uint32_t)p.num_blocks;
 
   // per-lane source offsets of the copy instructions of one block
   int koff[R::kIPT], voff[R::kIPT];
@@ -299,12 +306,13 @@ __global__ __launch_bounds__(64 * WV) void decode_kernel(AttnParams p) {
   // area.  That area holds one segment's rows, so the issue side waits
   // (issues nothing) while rows it copied are not yet read. ----
   Cursor ic = cur;
-  int64_t jn = 0;            // units issued
+  int jn = 0;                // units issued
+  int ist = 0;               // stage of unit jn (jn mod S)
   bool q_pending = false;    // query rows copied but not yet read
   unsigned okbits = 0;       // bit st: the unit in stage st has its block
-  auto can_issue = [&](int64_t lim) { return jn < n && jn < lim && !(q_pending && ic.b == 0); };
-  auto issue_one = [&]() {
-    const int st = (int)(jn % S);
+  auto can_issue = [&](int lim) { return jn < n && jn < lim && !(q_pending && ic.b == 0); };
+  auto issue_one = [&]() __attribute__((always_inline)) {
+    const int st = ist;
     const unsigned dst = ring_m0 + st * kStage;
     if (ic.b == 0 || jn == 0) {
       const unsigned char* qb = static_cast<const unsigned char*>(p.q) +
@@ -313,20 +321,23 @@ __global__ __launch_bounds__(64 * WV) void decode_kernel(AttnParams p) {
         if (k + 16 * lane < qbytes) lds_dma16(qb, (unsigned)(k + 16 * lane), q_m0 + k);
       q_pending = true;
     }
-    int id = load_uniform(p.block_tables,
-                          (int64_t)(p.req_begin + ic.rr) * p.max_blocks_per_req + ic.b0 + ic.b);
-    id = (id >= 0 && (int64_t)id < num_blocks) ? id : -1;
-    okbits = (okbits & ~(1u << st)) | ((id >= 0 ? 1u : 0u) << st);
-    const int64_t boff = (int64_t)(id < 0 ? 0 : id) * blk_stride + (int64_t)ic.kvh * D * KVB;
+    const int32_t id = load_uniform(ic.row, ic.b);
+    const bool ok = (uint32_t)id < nblk;
+    okbits = (okbits & ~(1u << st)) | ((ok ? 1u : 0u) << st);
+    const uint64_t boff = (uint64_t)(ok ? (uint32_t)id : 0u) * blk_stride + (uint32_t)(ic.kvh * (D * KVB));
     const unsigned char* kb = static_cast<const unsigned char*>(p.key_cache) + boff;
     const unsigned char* vb = static_cast<const unsigned char*>(p.value_cache) + boff;
+    // one LDS wait for the block's copies (they overwrite the stage read
+    // S - 1 units ago)
+    asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
 #pragma unroll
     for (int i = 0; i < R::kIPT; ++i) {
-      lds_dma16<true>(kb, (unsigned)koff[i], dst + 1024 * i);
-      lds_dma16<true>(vb, (unsigned)voff[i], dst + R::kBlkBytes + 1024 * i);
+      lds_dma16<true, false>(kb, (unsigned)koff[i], dst + 1024 * i);
+      lds_dma16<true, false>(vb, (unsigned)voff[i], dst + R::kBlkBytes + 1024 * i);
     }
     advance(p, ic);
     ++jn;
+    ist = (ist == S - 1) ? 0 : ist + 1;
   };
 
   // ---- per-lane LDS read offsets within a stage ----
@@ -362,10 +373,10 @@ __global__ __launch_bounds__(64 * WV) void decode_kernel(AttnParams p) {
   int seg = 0;          // segments this worker has finished
   int seg_b0 = 0;       // first block of the current segment
 
-  for (int64_t i = 0; i < n; ++i) {
+  int st_i = 0;         // stage of unit i
+  for (int i = 0; i < n; ++i) {
     while (can_issue(i + S)) issue_one();
-    wait_blocks<R::kIPB>((int)(jn - 1 - i));    // unit i landed (jn > i always holds here)
-    const int st_i = (int)(i % S);
+    wait_blocks<R::kIPB, S - 1>(jn - 1 - i);    // unit i landed (jn > i always holds here)
     const unsigned char* st = ring + st_i * kStage;
 
     // ---- segment start: query operands, fresh softmax state ----
@@ -525,28 +536,42 @@ __global__ __launch_bounds__(64 * WV) void decode_kernel(AttnParams p) {
             unsigned short* orow = static_cast<unsigned short*>(p.out) +
                                    (int64_t)cur.q_row * p.out_row_stride +
                                    (int64_t)(cur.kvh * G + hig) * D;
+            if constexpr (KVB == 2) {
 #pragma unroll
-            for (int m = 0; m < NM; ++m) {
-              if constexpr (KVB == 2) {
+              for (int m = 0; m < NM; ++m) {
                 // rows 4*q4 .. 4*q4+3 of tile m: d = 16m + 4*q4 + k, contiguous
                 st8(orow + 16 * m + 4 * q4,
                     u32x2{pack2<CT>(acc[ht][m][0] * inv, acc[ht][m][1] * inv),
                           pack2<CT>(acc[ht][m][2] * inv, acc[ht][m][3] * inv)});
-              } else {
+              }
+            } else {
+              // 8-bit rows: d = VE*(4*q4 + k) + m, so m = 0..NM-1 is contiguous
 #pragma unroll
-                for (int k = 0; k < 4; ++k) orow[VE * (4 * q4 + k) + m] = M::from_float(acc[ht][m][k] * inv);
+              for (int k = 0; k < 4; ++k) {
+                unsigned w[NM / 2];
+#pragma unroll
+                for (int m = 0; m < NM; m += 2)
+                  w[m / 2] = pack2<CT>(acc[ht][m][k] * inv, acc[ht][m + 1][k] * inv);
+                unsigned short* dst = orow + VE * (4 * q4 + k);
+                if constexpr (NM == 8) {
+                  st16(dst, u32x4{w[0], w[1], w[2], w[3]});
+                } else {
+                  st8(dst, u32x2{w[0], w[1]});
+                }
               }
             }
           } else {
             float* wa = p.ws_acc + (slot * G + hig) * D;
+            if constexpr (KVB == 2) {
 #pragma unroll
-            for (int m = 0; m < NM; ++m) {
-              if constexpr (KVB == 2) {
-                *reinterpret_cast<f32x4*>(wa + 16 * m + 4 * q4) = acc[ht][m];
-              } else {
+              for (int m = 0; m < NM; ++m) *reinterpret_cast<f32x4*>(wa + 16 * m + 4 * q4) = acc[ht][m];
+            } else {
 #pragma unroll
-                for (int k = 0; k < 4; ++k) wa[VE * (4 * q4 + k) + m] = acc[ht][m][k];
-              }
+              for (int k = 0; k < 4; ++k)
+#pragma unroll
+                for (int m = 0; m < NM; m += 4)
+                  *reinterpret_cast<f32x4*>(wa + VE * (4 * q4 + k) + m) =
+                      f32x4{acc[ht][m][k], acc[ht][m + 1][k], acc[ht][m + 2][k], acc[ht][m + 3][k]};
             }
             if (q4 == 0) {
               float* ml = p.ws_ml + (slot * G + hig) * 2;
@@ -559,6 +584,7 @@ __global__ __launch_bounds__(64 * WV) void decode_kernel(AttnParams p) {
       ++seg;
     }
     advance(p, cur);
+    st_i = (st_i == S - 1) ? 0 : st_i + 1;
   }
 }
 
@@ -653,12 +679,13 @@ __global__ __launch_bounds__(64) void decode_reduce_kernel(AttnParams p) {
   for (int e = 0; e < DPL; ++e) orow[lane + 64 * e] = Mfma<CT>::from_float(o[e] * inv);
 }
 
-// Waves per workgroup and ring depth for one instantiation: two column tiles
-// of fp8 (G > 16) make the per-block math long for a 4 KB block, so eight
-// waves per compute unit share the work; otherwise four.  The ring is as deep
-// as the configured depth where it fits the LDS.
+// Waves per workgroup and ring depth for one instantiation: a block of an
+// 8-bit cache carries half the bytes of a 16-bit one for the same per-block
+// math, so eight waves per compute unit share the work (two waves per SIMD
+// keep its issue slots busy); 16-bit caches use four.  The ring is as deep as
+// the configured depth where it fits the LDS.
 template <int D, int KVB, int HT>
-constexpr int waves_per_wg() { return decode_waves_per_cu(HT == 2 ? 32 : 16, KVB == 1 ? kFP8 : kF16); }
+constexpr int waves_per_wg() { return decode_waves_per_cu(KVB == 1 ? kFP8 : kF16); }
 
 template <int D, int KVB, int HT>
 constexpr int ring_depth() {
@@ -666,7 +693,8 @@ constexpr int ring_depth() {
   constexpr int stage = 2 * Ring<D, KVB>::kBlkBytes;
   constexpr int qcap = HT * 16 * D * 2;
   constexpr int fit = (kLdsBudget / wv - qcap) / stage;
-  return kStages < fit ? kStages : fit;
+  constexpr int want = KVB == 1 ? kStages8 : kStages;
+  return want < fit ? want : fit;
 }
 
 template <int D, typename CT, int KVB, bool I8, int HT>

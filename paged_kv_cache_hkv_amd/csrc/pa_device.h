@@ -204,7 +204,15 @@ __device__ inline unsigned lds_offset(const void* p) {
 // contents (scalar loads in flight are then not waited for either).
 template <bool NT = false, bool WAIT_LDS = true>
 __device__ inline void lds_dma16(const void* base, unsigned voff, unsigned m0) {
-  if constexpr (!WAIT_LDS) {
+  if constexpr (!WAIT_LDS && NT) {
+    asm volatile(
+        "s_mov_b32 m0, %2\n\t"
+        "s_nop 0\n\t"
+        "global_load_lds_dwordx4 %0, %1 nt"
+        :
+        : "v"(voff), "s"(base), "s"(m0)
+        : "memory");
+  } else if constexpr (!WAIT_LDS) {
     asm volatile(
         "s_mov_b32 m0, %2\n\t"
         "s_nop 0\n\t"

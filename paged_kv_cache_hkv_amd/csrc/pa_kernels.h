@@ -105,11 +105,10 @@ struct AttnParams {
 };
 
 // Decode waves per workgroup (= per compute unit: one resident workgroup of
-// independent waves).  8-bit caches (fp8, int8) with G > 16 (two MFMA column
-// tiles, 4 KB blocks) have the longest math per block and use eight;
-// everything else four.
-constexpr int decode_waves_per_cu(int group, int cache_dtype) {
-  return (group > 16 && (cache_dtype == kFP8 || cache_dtype == kINT8)) ? 8 : 4;
+// independent waves).  8-bit caches (fp8, int8) stream half the bytes per
+// block for the same per-block math and use eight; 16-bit caches four.
+constexpr int decode_waves_per_cu(int cache_dtype) {
+  return (cache_dtype == kFP8 || cache_dtype == kINT8) ? 8 : 4;
 }
 
 hipError_t launch_metadata(const MetadataParams& p, hipStream_t stream);
