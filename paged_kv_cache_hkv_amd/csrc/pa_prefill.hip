@@ -16,15 +16,17 @@
 // in that order, so the tiles with the most keys start first (longest-first
 // scheduling over uneven chunks).  All waves of a workgroup share each 64-key
 // K/V tile in LDS.  Two kernels:
-//   * 16-bit caches (prefill_pp_kernel): 8 waves, 256/hpw queries, K/V tiles
-//     copied global -> LDS by DMA into 4-stage rings, and two groups of 4
-//     waves alternating between the MFMA phase and the softmax phase (see
-//     the kernel's own comment);
-//   * fp8 caches (prefill_kernel): 4 waves, 128/hpw queries, tiles staged
-//     through registers and widened to bf16/fp16 when written to LDS
-//     (double-buffered, one barrier per tile): K row-major with padded rows,
-//     V transposed (key bits 2 and 3 swapped so the 8 keys one lane feeds
-//     into one MFMA step are adjacent).
+//   * prefill_pp_kernel (16-bit caches, and 8-bit caches with head_dim 128):
+//     8 waves, 256/hpw queries, K/V tiles copied global -> LDS by DMA into
+//     4-stage rings, and two groups of 4 waves alternating between the MFMA
+//     phase and the softmax phase (see the kernel's own comment); 8-bit
+//     tiles land in a ring of their own and each wave widens the rows it
+//     copied into two bf16/fp16 operand stages;
+//   * prefill_kernel (8-bit caches with head_dim 64): 4 waves, 128/hpw
+//     queries, tiles staged through registers and widened to bf16/fp16 when
+//     written to LDS (double-buffered, one barrier per tile): K row-major
+//     with padded rows, V transposed (key bits 2 and 3 swapped so the 8 keys
+//     one lane feeds into one MFMA step are adjacent).
 // Per tile a wave computes S^T = K . Q^T (v_mfma_f32_32x32x16, keys x queries)
 // so each lane holds 32 scores of ONE query: the row max needs one exchange
 // with the lane 32 apart and every rescale is lane-local.  The probabilities,
@@ -450,9 +452,9 @@ __device__ inline u32x2 lds_read_tr16(const u32x4* base, int pos16, int byte_off
 }
 
 // ---------------------------------------------------------------------------
-// 16-bit caches: eight waves in two groups of four (one wave of each group on
-// every SIMD) that alternate between a matrix phase and a softmax phase, so
-// the MFMAs of one group run while the other group computes its softmax.
+// Eight waves in two groups of four (one wave of each group on every SIMD)
+// that alternate between a matrix phase and a softmax phase, so the MFMAs of
+// one group run while the other group computes its softmax.
 //
 // Per wave and 64-key tile j the work splits into
 //   M(j): S_j = K_j . Q^T and O^T += V_{j-1}^T . P_{j-1}^T (MFMA, LDS reads)
@@ -473,6 +475,15 @@ __device__ inline u32x2 lds_read_tr16(const u32x4* base, int pos16, int byte_off
 // compiler would wait for behind the copies in flight).  The workgroup checks
 // its table entries once up front; only rows holding ids outside the pool
 // test block presence per tile.
+// 8-bit caches: the copies fill rings of 8-bit tiles in plain [key][chunk]
+// order (one 1 KB instruction per wave per tile), and at the end of M(j)
+// each wave widens the rows it copied of K tile j+1 and V tile j into two
+// operand stages (tile t in stage t % 2, LdsTile layout, V rows of absent
+// keys zeroed); the barrier that ends M(j) publishes them.  Two operand
+// stages suffice: K(j+1) and V(j) replace K(j-1) and V(j-2), whose last
+// reads were in M(j-1), and the other group is in its softmax phase.  The
+// widening (one 16-byte LDS read, 8 converts, two 16-byte writes per lane
+// and tensor) runs in the MFMA phase, off the critical softmax path.
 constexpr int kPPWaves = 8;
 constexpr int kPPThreads = 64 * kPPWaves;
 constexpr int kPPStages = 4;
@@ -499,23 +510,34 @@ __device__ inline unsigned tile_okmask(const int32_t* bt_row, int nblk, int nb32
   return ok;
 }
 
-template <int D, typename CT, bool MASK>
+template <int D, typename CT, int KVB, bool I8, bool MASK>
 __global__ __launch_bounds__(kPPThreads) void prefill_pp_kernel(AttnParams p, int hpw) {
   using M = Mfma<CT>;
   using vec8 = typename M::vec8;
   using L = LdsTile<D>;
   constexpr int QS = D / 16;                 // QK MFMA steps (16 d each)
   constexpr int DT = D / 32;                 // 32-row d tiles of O^T
-  constexpr int NS = kPPStages;
-  constexpr int IPW = L::kInst / kPPWaves;   // copy instructions per wave per tile (K and V each)
-  constexpr int KPI = 64 / L::CPR;           // keys per copy instruction
+  constexpr int NS = kPPStages;              // copy ring depth
+  // operand stages (16-bit, LdsTile layout): the copy ring itself for 16-bit
+  // caches; for 8-bit caches two stages that each wave fills by widening the
+  // rows it copied into an 8-bit ring (tile t in 8-bit stage t % NS, operand
+  // stage t % 2)
+  constexpr int NO = KVB == 2 ? NS : 2;
+  constexpr int CPR8 = D / 16;               // 16-byte chunks of an 8-bit key row
+  constexpr int kPos8 = kTileK * CPR8;       // 16-byte positions of an 8-bit tile
+  constexpr int kCopyPos = KVB == 2 ? L::kPos : kPos8;
+  constexpr int IPW = kCopyPos / 64 / kPPWaves;   // copy instructions per wave per tile (K and V each)
+  constexpr int KPI = 64 / (KVB == 2 ? L::CPR : CPR8);   // keys per copy instruction
   constexpr int PPS = 4 * DT / QS;           // PV MFMAs per QK step
-  static_assert(IPW * kPPWaves == L::kInst && PPS * QS == 4 * DT, "tile shape");
+  static_assert(IPW * kPPWaves * 64 == kCopyPos && PPS * QS == 4 * DT, "tile shape");
   static_assert(2 * IPW * KPI == kBlock, "two waves copy each block of a tile");
-  constexpr unsigned kTileBytes = L::kPos * 16;
+  static_assert(KVB == 2 || IPW == 1, "8-bit tiles: one copy instruction per wave");
+  constexpr unsigned kTileBytes = kCopyPos * 16;
 
-  __shared__ u32x4 Kr[NS * L::kPos];
-  __shared__ u32x4 Vr[NS * L::kPos];
+  __shared__ u32x4 Kr[NO * L::kPos];
+  __shared__ u32x4 Vr[NO * L::kPos];
+  __shared__ u32x4 K8[KVB == 1 ? NS * kPos8 : 1];
+  __shared__ u32x4 V8[KVB == 1 ? NS * kPos8 : 1];
 
   // Request-major numbering: consecutive workgroups are the query tiles of
   // one request for consecutive head groups; workgroups are spread over the
@@ -573,10 +595,10 @@ __global__ __launch_bounds__(kPPThreads) void prefill_pp_kernel(AttnParams p, in
   const int32_t* bt_row = p.block_tables + (int64_t)r * p.max_blocks_per_req;
   const int nblk = (s_eff + kBlock - 1) / kBlock;
   const int nb32 = (int)min(p.num_blocks, (int64_t)0x7FFFFFFF);
-  const int64_t tok_stride = (int64_t)p.num_kv_heads * D * 2;
+  const int64_t tok_stride = (int64_t)p.num_kv_heads * D * KVB;
   const int64_t blk_stride = tok_stride * kBlock;
-  const unsigned char* kbase = static_cast<const unsigned char*>(p.key_cache) + (int64_t)kvh * D * 2;
-  const unsigned char* vbase = static_cast<const unsigned char*>(p.value_cache) + (int64_t)kvh * D * 2;
+  const unsigned char* kbase = static_cast<const unsigned char*>(p.key_cache) + (int64_t)kvh * D * KVB;
+  const unsigned char* vbase = static_cast<const unsigned char*>(p.value_cache) + (int64_t)kvh * D * KVB;
 
   // One pass over the table entries the workgroup's tiles use: when all of
   // them are pool ids (the normal case) every block of every tile is present,
@@ -599,12 +621,18 @@ __global__ __launch_bounds__(kPPThreads) void prefill_pp_kernel(AttnParams p, in
 #pragma unroll
   for (int i = 0; i < IPW; ++i) {
     const int pidx = (wave * IPW + i) * 64 + lane;
-    const int key = pidx / L::CPR, pos = pidx % L::CPR;
-    const unsigned row = (unsigned)((key % kBlock) * tok_stride);
-    koff[i] = row + (unsigned)((pos ^ L::swk(key)) * 16);
-    voff[i] = row + (unsigned)((pos ^ L::swv(key)) * 16);
+    if constexpr (KVB == 2) {
+      const int key = pidx / L::CPR, pos = pidx % L::CPR;
+      const unsigned row = (unsigned)((key % kBlock) * tok_stride);
+      koff[i] = row + (unsigned)((pos ^ L::swk(key)) * 16);
+      voff[i] = row + (unsigned)((pos ^ L::swv(key)) * 16);
+    } else {
+      // 8-bit ring: plain [key][chunk] order, each lane widens what it copied
+      const int key = pidx / CPR8, pos = pidx % CPR8;
+      koff[i] = voff[i] = (unsigned)((key % kBlock) * tok_stride) + (unsigned)(pos * 16);
+    }
   }
-  const unsigned kr0 = lds_offset(Kr), vr0 = lds_offset(Vr);
+  const unsigned kr0 = lds_offset(KVB == 2 ? Kr : K8), vr0 = lds_offset(KVB == 2 ? Vr : V8);
   // this wave's table entry for tile t (index clamped into the sequence), and
   // the id its copies use (absent -> block 0: masked keys, zeroed V rows)
   auto raw_id = [&](int t) __attribute__((always_inline)) {
@@ -632,6 +660,30 @@ __global__ __launch_bounds__(kPPThreads) void prefill_pp_kernel(AttnParams p, in
       const int key = pidx / L::CPR;
       if (kTileK * t + key >= s_eff || !((ok >> (key / kBlock)) & 1u)) Vs[pidx] = u32x4{0u, 0u, 0u, 0u};
     }
+  };
+
+  // 8-bit caches: after this wave's copies of tile t have landed, widen them
+  // (16 bytes per lane) into the operand stage in the LdsTile layout; V rows
+  // of keys the tile lacks become zeros (K rows need not: their scores are
+  // masked by selects)
+  auto widen = [&](const u32x4* src8, u32x4* dst, int t, bool is_v) __attribute__((always_inline)) {
+    const int pidx = wave * 64 + lane;
+    const int key = pidx / CPR8, c8 = pidx % CPR8;
+    const u32x4 w = src8[pidx];
+    u32x4 lo{widen8x2<CT, I8>(w[0], false), widen8x2<CT, I8>(w[0], true),
+             widen8x2<CT, I8>(w[1], false), widen8x2<CT, I8>(w[1], true)};
+    u32x4 hi{widen8x2<CT, I8>(w[2], false), widen8x2<CT, I8>(w[2], true),
+             widen8x2<CT, I8>(w[3], false), widen8x2<CT, I8>(w[3], true)};
+    int sw = L::swk(key);
+    if (is_v) {
+      sw = L::swv(key);
+      if (!(kTileK * t + kTileK <= s_eff && rowok)) {
+        const unsigned ok = okmask(t);
+        if (kTileK * t + key >= s_eff || !((ok >> (key / kBlock)) & 1u)) lo = hi = u32x4{0u, 0u, 0u, 0u};
+      }
+    }
+    dst[key * L::CPR + ((2 * c8) ^ sw)] = lo;
+    dst[key * L::CPR + ((2 * c8 + 1) ^ sw)] = hi;
   };
 
   // lane roles in the LDS reads (tile-invariant)
@@ -775,19 +827,23 @@ __global__ __launch_bounds__(kPPThreads) void prefill_pp_kernel(AttnParams p, in
       copy_tile(vbase, voff, id1, vr0 + kTileBytes);
     }
     if (kt0 + 2 < ntiles) copy_tile(kbase, koff, id2, kr0 + 2 * kTileBytes);
-    // the first M phase multiplies zero probabilities with V stage NS-1:
-    // clear it, so stale LDS contents cannot turn 0 * V into NaN
+    // the first M phase multiplies zero probabilities with V operand stage
+    // NO-1: clear it, so stale LDS contents cannot turn 0 * V into NaN
     for (int i = threadIdx.x; i < L::kPos; i += kPPThreads)
-      Vr[(NS - 1) * L::kPos + i] = u32x4{0u, 0u, 0u, 0u};
+      Vr[(NO - 1) * L::kPos + i] = u32x4{0u, 0u, 0u, 0u};
     wait_vmcnt<0>();
-    fix_v(kt0, Vr);
-    if (kt0 + 1 < ntiles) fix_v(kt0 + 1, Vr + L::kPos);
+    if constexpr (KVB == 2) {
+      fix_v(kt0, Vr);
+      if (kt0 + 1 < ntiles) fix_v(kt0 + 1, Vr + L::kPos);
+    } else {
+      widen(K8, Kr, kt0, false);   // K(kt0); K(kt0 + 1) and V(kt0) in M(kt0)
+    }
     barrier_nowait<true>();
 
     auto step = [&](auto st_c, int j) __attribute__((always_inline)) {
       constexpr int ST = decltype(st_c)::value;
-      const u32x4* Kt = Kr + ST * L::kPos;
-      const u32x4* Vt = Vr + ((ST + NS - 1) % NS) * L::kPos;
+      const u32x4* Kt = Kr + (ST % NO) * L::kPos;
+      const u32x4* Vt = Vr + ((ST + NO - 1) % NO) * L::kPos;
       // ---- M(j) ----
       // one straight MFMA path (branches around MFMAs cost accumulator
       // copies): a tile the wave does not need still runs, with zero
@@ -798,7 +854,14 @@ __global__ __launch_bounds__(kPPThreads) void prefill_pp_kernel(AttnParams p, in
       if (j - 1 >= kt0 && j + 2 < ntiles) wait_vmcnt<2 * IPW>();
       else if (j - 1 >= kt0 && j + 1 < ntiles) wait_vmcnt<IPW>();
       else wait_vmcnt<0>();
-      if (j >= kt0 + 2 && j < ntiles) fix_v(j, Vr + ST * L::kPos);
+      if constexpr (KVB == 2) {
+        if (j >= kt0 + 2 && j < ntiles) fix_v(j, Vr + ST * L::kPos);
+      } else {
+        // operand stages of K(j+1) and V(j): their previous tiles, K(j-1) and
+        // V(j-2), were last read in M(j-1), which every wave has finished
+        if (j + 1 < ntiles) widen(K8 + ((ST + 1) % NS) * kPos8, Kr + ((ST + 1) % NO) * L::kPos, j + 1, false);
+        if (j < ntiles) widen(V8 + ST * kPos8, Vr + (ST % NO) * L::kPos, j, true);
+      }
       barrier_nowait<true>();
       // ---- V(j) ----
       const int id_k = copy_id(raw_n, j + 3);
@@ -852,16 +915,16 @@ int heads_per_wg(int G) {
 template <int D, typename CT, int KVB, bool I8 = false>
 hipError_t launch_typed(const AttnParams& p, hipStream_t stream) {
   const int hpw = heads_per_wg(p.group);
-  const int QB = (KVB == 2 ? 32 * kPPWaves : 128) / hpw;
+  const int QB = (KVB == 2 || D == 128 ? 32 * kPPWaves : 128) / hpw;
   const int qtiles = (p.max_query_len + QB - 1) / QB;
   if (qtiles == 0) return hipSuccess;
   // x: query-head group, y: request, z: tile counted from the end of the request
   dim3 grid((unsigned)(p.num_q_heads / hpw), (unsigned)p.num_reqs, (unsigned)qtiles);
-  if constexpr (KVB == 2) {
+  if constexpr (KVB == 2 || D == 128) {
     if (p.masked) {
-      hipLaunchKernelGGL((prefill_pp_kernel<D, CT, true>), grid, dim3(kPPThreads), 0, stream, p, hpw);
+      hipLaunchKernelGGL((prefill_pp_kernel<D, CT, KVB, I8, true>), grid, dim3(kPPThreads), 0, stream, p, hpw);
     } else {
-      hipLaunchKernelGGL((prefill_pp_kernel<D, CT, false>), grid, dim3(kPPThreads), 0, stream, p, hpw);
+      hipLaunchKernelGGL((prefill_pp_kernel<D, CT, KVB, I8, false>), grid, dim3(kPPThreads), 0, stream, p, hpw);
     }
   } else {
     if (p.masked) {
