@@ -598,6 +598,7 @@ __global__ __launch_bounds__(64 * WV) void decode_kernel(AttnParams p) {
 template <int D, typename CT>
 __global__ __launch_bounds__(64) void decode_reduce_kernel(AttnParams p) {
   constexpr int DPL = D / 64;   // output columns per lane
+  constexpr int RB = 16;        // partials whose loads are in flight together
   const int rr = blockIdx.y;
   const int qh = blockIdx.x;
   const int lane = threadIdx.x;
@@ -651,13 +652,13 @@ __global__ __launch_bounds__(64) void decode_reduce_kernel(AttnParams p) {
     for (int off = 32; off >= 1; off >>= 1) t += shfl_xor(t, off);
     lsum += t;
     // a missing partial reads an existing one with weight 0 (its memory may
-    // hold anything, and 0 * NaN is NaN); batches of 8 keep loads in flight
+    // hold anything, and 0 * NaN is NaN); batches of RB keep loads in flight
     ix = ok ? ix : ix0;
     const int m = min(64, cnt - g);
-    for (int j0 = 0; j0 < m; j0 += 8) {
-      float wj[8], v[8][DPL];
+    for (int j0 = 0; j0 < m; j0 += RB) {
+      float wj[RB], v[RB][DPL];
 #pragma unroll
-      for (int u = 0; u < 8; ++u) {
+      for (int u = 0; u < RB; ++u) {
         const int j = min(j0 + u, m - 1);
         wj[u] = (j0 + u < m) ? __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, w), j))
                              : 0.f;
@@ -666,7 +667,7 @@ __global__ __launch_bounds__(64) void decode_reduce_kernel(AttnParams p) {
         for (int e = 0; e < DPL; ++e) v[u][e] = a[64 * e];
       }
 #pragma unroll
-      for (int u = 0; u < 8; ++u)
+      for (int u = 0; u < RB; ++u)
 #pragma unroll
         for (int e = 0; e < DPL; ++e) o[e] += wj[u] * v[u][e];
     }

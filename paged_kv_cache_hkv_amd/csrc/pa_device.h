@@ -158,6 +158,16 @@ __device__ inline float pair32_sum(float v) { return v + shfl_xor(v, 32); }
 // operands equal, the two results hold the low and the high half of the wave
 // broadcast over both halves, so combining them gives every lane the value of
 // its pair, bit-identical in both lanes.
+// max of three floats in one instruction.  Written out because the builtin
+// fmaxf first quiets each operand the compiler cannot prove canonical (one
+// extra v_max_f32 x, x per MFMA result); v_max3_f32 follows the same maxNum
+// rule for quiet NaNs and -inf.
+__device__ inline float max3f(float a, float b, float c) {
+  float r;
+  asm("v_max3_f32 %0, %1, %2, %3" : "=v"(r) : "v"(a), "v"(b), "v"(c));
+  return r;
+}
+
 __device__ inline float pair32_max_swap(float v) {
   const unsigned u = __builtin_bit_cast(unsigned, v);
   const auto r = __builtin_amdgcn_permlane32_swap(u, u, false, false);

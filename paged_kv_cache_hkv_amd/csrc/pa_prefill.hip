@@ -772,15 +772,17 @@ __global__ __launch_bounds__(kPPThreads) void prefill_pp_kernel(AttnParams p, in
         }
     }
     if constexpr (MASK) window_alibi(sc, k0, half, qpos, p.window_left, p.scale_log2, slope2);
-    // row max as a tree (short dependency chains)
-    float m4[4];
+    // row max of the lane's 32 scores as a tree of three-input maxima (16
+    // instructions, short dependency chains)
+    float m10[11];
 #pragma unroll
-    for (int k = 0; k < 4; ++k)
-      m4[k] = fmaxf(fmaxf(fmaxf(sc[k >> 1][8 * (k & 1) + 0], sc[k >> 1][8 * (k & 1) + 1]),
-                          fmaxf(sc[k >> 1][8 * (k & 1) + 2], sc[k >> 1][8 * (k & 1) + 3])),
-                    fmaxf(fmaxf(sc[k >> 1][8 * (k & 1) + 4], sc[k >> 1][8 * (k & 1) + 5]),
-                          fmaxf(sc[k >> 1][8 * (k & 1) + 6], sc[k >> 1][8 * (k & 1) + 7])));
-    float mx = fmaxf(fmaxf(m4[0], m4[1]), fmaxf(m4[2], m4[3]));
+    for (int k = 0; k < 10; ++k)
+      m10[k] = max3f(sc[(3 * k) >> 4][(3 * k) & 15], sc[(3 * k + 1) >> 4][(3 * k + 1) & 15],
+                     sc[(3 * k + 2) >> 4][(3 * k + 2) & 15]);
+    m10[10] = fmaxf(sc[1][14], sc[1][15]);
+    const float m3a = max3f(m10[0], m10[1], m10[2]), m3b = max3f(m10[3], m10[4], m10[5]);
+    const float m3c = max3f(m10[6], m10[7], m10[8]);
+    float mx = max3f(max3f(m3a, m3b, m3c), m10[9], m10[10]);
     mx = pair32_max_swap(mx);
     // lazy rescale: move the reference max only when it grew by more than 2^8
     const bool grow = (m_used == -INFINITY) ? (mx > -INFINITY) : ((mx - m_used) * c2 > kRescaleLog2);
