@@ -38,6 +38,11 @@ The pages define neither, so the plain readings are taken:
 * ALiBi: query head ``h`` adds ``slope[h] * (j - p)`` (zero for the key at the
   query's own position, more negative the older the key) to the scaled score
   ``q . k * scale`` before the softmax; the caller gives the slopes.
+
+Absent blocks (a defensive reading; the pages only ever hand out pool blocks):
+a block-table entry that is not a block of the pool (negative, or not below
+``num_blocks``) holds no keys -- its keys take no part in any softmax, and a
+query row left with no visible key is zero.
 """
 
 import math
@@ -60,13 +65,16 @@ def gather_request_kv(key_cache_f64, value_cache_f64, block_table_row, seq_len, 
     return k, v
 
 
-def causal_attention(q, k, v, num_computed, scale, sliding_window=0, alibi_slopes=None):
+def causal_attention(q, k, v, num_computed, scale, sliding_window=0, alibi_slopes=None,
+                     key_present=None):
     """Dense causal attention of one request in float64.
 
     q: [n, Hq, D]; k, v: [s, Hkv, D] with s = num_computed + n.
     Row i (position p = num_computed + i) attends keys 0 .. p, or only
     p - sliding_window + 1 .. p when sliding_window > 0; with alibi_slopes
     ([Hq]) head h adds slope[h] * (j - p) to the score of key j.
+    key_present: bool [s] or None; keys marked False are left out, and a row
+    with no key left is zero.
     Returns [n, Hq, D].
     """
     n, hq, d = q.shape
@@ -80,6 +88,9 @@ def causal_attention(q, k, v, num_computed, scale, sliding_window=0, alibi_slope
     allowed = key_idx <= last_key                         # [n, s]
     if sliding_window > 0:
         allowed &= key_idx > last_key - sliding_window
+    if key_present is not None:
+        allowed &= np.asarray(key_present, dtype=bool)[None, :]
+    empty = ~allowed.any(axis=1)                          # rows with no visible key
     for h in range(hq):
         kv = h // g
         scores = (q[:, h, :] @ k[:, kv, :].T) * scale     # [n, s]
@@ -87,9 +98,11 @@ def causal_attention(q, k, v, num_computed, scale, sliding_window=0, alibi_slope
             scores = scores + float(alibi_slopes[h]) * (key_idx - last_key)
         scores = np.where(allowed, scores, -np.inf)
         mx = scores.max(axis=1, keepdims=True)
+        mx = np.where(empty[:, None], 0.0, mx)
         p = np.exp(scores - mx)
         p = np.where(allowed, p, 0.0)
-        p /= p.sum(axis=1, keepdims=True)
+        den = p.sum(axis=1, keepdims=True)
+        p /= np.where(empty[:, None], 1.0, den)
         out[:, h, :] = p @ v[:, kv, :]
     return out
 
@@ -105,7 +118,8 @@ def decode_cache(cache_bits, cache_dtype, scale=1.0):
 
 def paged_attention(q, key_cache, value_cache, block_tables, query_start_loc, seq_lens,
                     block_size, scale=None, requests=None, cache_dtype=None,
-                    k_scale=1.0, v_scale=1.0, sliding_window=0, alibi_slopes=None):
+                    k_scale=1.0, v_scale=1.0, sliding_window=0, alibi_slopes=None,
+                    num_blocks=None):
     """Attention of a batch over the paged cache, one request at a time.
 
     q: float64 [T, Hq, D] (already decoded).
@@ -114,6 +128,8 @@ def paged_attention(q, key_cache, value_cache, block_tables, query_start_loc, se
       bits are decoded per request, so a large pool is never widened at once.
     requests: iterable of request indices to compute (default: all).
     sliding_window, alibi_slopes: the mask variants of ``causal_attention``.
+    num_blocks: pool size; when given, table entries outside [0, num_blocks)
+      are absent blocks (their keys are left out; K/V read as zeros).
     Returns {r: float64 [n_r, Hq, D]}.
     """
     d = q.shape[2]
@@ -128,15 +144,25 @@ def paged_attention(q, key_cache, value_cache, block_tables, query_start_loc, se
         n = end - start
         s = int(seq_lens[r])
         c = s - n
-        row = block_tables[r]
-        if cache_dtype is None:
-            k, v = gather_request_kv(key_cache, value_cache, row, s, block_size)
+        nb = -(-s // block_size)
+        ids = np.asarray(list(block_tables[r][:nb]), dtype=np.int64)
+        present_blk = np.ones(nb, dtype=bool)
+        if num_blocks is not None:
+            present_blk = (ids >= 0) & (ids < num_blocks)
+        safe = np.where(present_blk, ids, 0)
+        if not present_blk.any():
+            kb = vb = np.zeros((nb,) + tuple(key_cache.shape[1:]), dtype=np.float64)
+        elif cache_dtype is None:
+            kb, vb = key_cache[safe], value_cache[safe]
         else:
-            nb = -(-s // block_size)
-            ids = np.asarray(row[:nb], dtype=np.int64)
-            kb = decode_cache(key_cache[ids], cache_dtype, k_scale)
-            vb = decode_cache(value_cache[ids], cache_dtype, v_scale)
-            local = np.arange(nb)
-            k, v = gather_request_kv(kb, vb, local, s, block_size)
-        result[r] = causal_attention(q[start:end], k, v, c, scale, sliding_window, alibi_slopes)
+            kb = decode_cache(key_cache[safe], cache_dtype, k_scale)
+            vb = decode_cache(value_cache[safe], cache_dtype, v_scale)
+        kb = np.where(present_blk[:, None, None, None], kb, 0.0)
+        vb = np.where(present_blk[:, None, None, None], vb, 0.0)
+        k, v = gather_request_kv(kb, vb, np.arange(nb), s, block_size)
+        key_present = None
+        if num_blocks is not None:
+            key_present = np.repeat(present_blk, block_size)[:s]
+        result[r] = causal_attention(q[start:end], k, v, c, scale, sliding_window, alibi_slopes,
+                                     key_present)
     return result

@@ -57,7 +57,8 @@ class Snapshot:
         for r in requests:
             s = int(wl.seq_lens_host[r])
             nb = -(-s // wl.block_size)
-            ids.update(int(b) for b in wl.block_tables[r, :nb])
+            # entries outside the pool are absent blocks: nothing to copy
+            ids.update(int(b) for b in wl.block_tables[r, :nb] if 0 <= b < wl.pool_blocks)
         self.ids = np.array(sorted(ids), dtype=np.int64)
         self.local = {int(b): i for i, b in enumerate(self.ids)}
         idx = torch.from_numpy(self.ids).to(tensors.key_cache.device)
@@ -97,13 +98,13 @@ def oracle_outputs(wl, tensors, snapshot, requests, qsl_len=None, sliding_window
         s = seq_lens[r]
         nb = -(-s // bs)
         if r in requests:
-            rows.append([snapshot.local[int(b)] for b in wl.block_tables[r, :nb]])
+            rows.append([snapshot.local.get(int(b), -1) for b in wl.block_tables[r, :nb]])
         else:
             rows.append([])
     return OA.paged_attention(q, kc, vc, rows, qsl, seq_lens, bs, requests=requests,
                               cache_dtype=cache_dt, k_scale=tensors.k_scale,
                               v_scale=tensors.v_scale, sliding_window=sliding_window,
-                              alibi_slopes=alibi_slopes)
+                              alibi_slopes=alibi_slopes, num_blocks=len(snapshot.ids))
 
 
 def gpu_rows(out, qsl, r):

@@ -11,7 +11,9 @@ invariants directly:
   bit-identical outputs;
 * determinism: two runs give bit-identical outputs;
 * split invariance: different decode worker counts agree to float32 rounding;
-* aliasing: requests that share prefix blocks read them correctly.
+* aliasing: requests that share prefix blocks read them correctly;
+* absent blocks: table entries outside the pool hold no keys (rows with no
+  visible key are zero).
 """
 
 import numpy as np
@@ -196,3 +198,45 @@ def test_aliased_prefix_blocks():
     expect = oracle_outputs(wl, t, snap, list(range(wl.num_reqs)))
     err, _ = compare(wl, st.out, expect, qsl)
     assert err <= tol_of(wl), err
+
+
+@pytest.mark.parametrize("kind", ["act", "fp8", "int8"])
+@pytest.mark.parametrize("hq,hkv,d,act", [(8, 2, 128, torch.bfloat16), (32, 1, 128, torch.bfloat16),
+                                          (8, 8, 64, torch.float16)])
+def test_absent_blocks(kind, hq, hkv, d, act):
+    """Table entries outside the pool (negative or past it) hold no keys: decode
+    and prefill leave those keys out, a row with no visible key is zero, and
+    the cache write skips tokens whose block is absent."""
+    _need_gpu()
+    wl = S.random_batch(13 + d + hq, [40, 100, 31, 500], [(0, 70), (33, 64), (200, 90), (0, 20)],
+                        hq=hq, hkv=hkv, d=d, act=act, fp8=kind == "fp8", int8=kind == "int8", pad=3)
+    t = S.make_tensors(wl, DEV, poison=True)
+    bt = wl.block_tables.copy()
+    pool = wl.pool_blocks
+    bt[0, 1] = -1                 # decode: a middle block
+    bt[1, 6] = -1                 # decode: the block of this step's token
+    bt[2, :2] = -1                # decode: every block -> zero output
+    bt[3, 0] = pool + 5           # decode: past the pool
+    bt[3, 17] = 2 ** 30
+    bt[4, 2] = -1                 # prefill: a block of its new tokens
+    bt[5, 0] = -1                 # prefill: a block of its cached prefix
+    bt[6, 12] = pool + 1
+    bt[6, 13] = -3
+    bt[7, 0] = -1                 # prefill: its first 16 queries see no key
+    wl = S.Workload(**{**wl.__dict__, "block_tables": bt})
+    t = S.Tensors(q=t.q, k_new=t.k_new, v_new=t.v_new, key_cache=t.key_cache,
+                  value_cache=t.value_cache, num_computed=t.num_computed, query_lens=t.query_lens,
+                  block_tables=torch.from_numpy(bt).to(DEV), k_scale=t.k_scale, v_scale=t.v_scale)
+    requests = list(range(wl.num_reqs))
+    snap = Snapshot(wl, t, requests)
+    st = PagedAttentionStep(wl, t)
+    print(f"[absent] kind={kind} hq={hq} hkv={hkv} d={d}", flush=True)
+    st.run()
+    torch.cuda.synchronize()
+    qsl, _, _, _ = oracle_metadata(wl)
+    expect = oracle_outputs(wl, t, snap, requests)
+    assert not np.any(expect[2])                       # the oracle's own zero row
+    err, _ = compare(wl, st.out, expect, qsl)
+    assert err <= tol_of(wl), err
+    assert torch.all(st.out[qsl[2]:qsl[3]] == 0)       # every block absent
+    assert torch.all(st.out[qsl[7]:qsl[7] + 16] == 0)  # queries with no visible key

@@ -254,3 +254,59 @@ def test_int8_cache_attention_equals_sdpa_on_dequantized():
         v = vcode[ids].reshape(-1, hkv, d)[:seq[r]].astype(np.float64) * vs
         ref = _sdpa_reference(q[qsl[r]:qsl[r + 1]], k, v, comp[r], scale)
         assert np.allclose(got[r], ref, rtol=0, atol=1e-12), r
+
+
+def test_absent_blocks_equal_sdpa_without_their_keys():
+    """Table entries outside the pool hold no keys: the oracle equals SDPA over
+    the dense K/V with those keys masked out (their cache contents, even NaN,
+    never matter), and a row with no visible key is exactly zero."""
+    rng = np.random.default_rng(91)
+    hq, hkv, d, bs, nb_pool = 8, 2, 8, 4, 40
+    comp = [9, 0, 3, 11]
+    ql = [1, 6, 5, 1]
+    seq, rows, kc, vc, q = _paged_setup(rng, comp, ql, hq, hkv, d, bs, nb_pool)
+    rows = [list(r) for r in rows]
+    rows[0][1] = -1               # decode: a middle block absent
+    rows[1][0] = nb_pool + 3      # prefill: the first block outside the pool
+    rows[2][1] = -7               # prefill with a cached prefix: the block of its last keys
+    rows[3] = [-1] * len(rows[3])  # decode with every block absent
+    # what sits in block 0 (read in place of absent ones) never matters: make
+    # it NaN, after moving any present use of block 0 to an unused block
+    used = {b for row in rows for b in row}
+    spare = min(set(range(1, nb_pool)) - used)
+    rows = [[spare if b == 0 else b for b in row] for row in rows]
+    kc[spare], vc[spare] = kc[0], vc[0]
+    kc[0] = np.nan
+    vc[0] = np.nan
+    qsl = [0] + list(np.cumsum(ql))
+    res = A.paged_attention(q, kc, vc, rows, qsl, seq, bs, num_blocks=nb_pool)
+    for r in range(len(ql)):
+        s, c, n = seq[r], seq[r] - ql[r], ql[r]
+        present = np.array([0 <= rows[r][j // bs] < nb_pool for j in range(s)])
+        k = np.zeros((s, hkv, d))
+        v = np.zeros((s, hkv, d))
+        for j in range(s):
+            if present[j]:
+                k[j] = kc[rows[r][j // bs], j % bs]
+                v[j] = vc[rows[r][j // bs], j % bs]
+        g = hq // hkv
+        kk = torch.from_numpy(np.repeat(k, g, axis=1)).permute(1, 0, 2)
+        vv = torch.from_numpy(np.repeat(v, g, axis=1)).permute(1, 0, 2)
+        qq = torch.from_numpy(q[qsl[r]:qsl[r + 1]]).permute(1, 0, 2)
+        mask = (torch.arange(s)[None, :] <= (c + torch.arange(n))[:, None]) & \
+            torch.from_numpy(present)[None, :]
+        visible = mask.any(dim=1).numpy()
+        got = res[r]
+        assert np.all(np.isfinite(got))
+        assert np.array_equal(got[~visible], np.zeros_like(got[~visible]))
+        if visible.any():
+            ref = torch.nn.functional.scaled_dot_product_attention(
+                qq, kk, vv, attn_mask=mask, scale=1.0 / math.sqrt(d)).permute(1, 0, 2).numpy()
+            np.testing.assert_allclose(got[visible], ref[visible], rtol=1e-12, atol=1e-12)
+    assert not np.any(res[3])     # every block absent: zero output
+    # a table of pool ids only: num_blocks changes nothing
+    pool_rows = [list(range(1, 1 + len(r))) for r in rows]
+    full = A.paged_attention(q, kc, vc, pool_rows, qsl, seq, bs, num_blocks=nb_pool)
+    ref_full = A.paged_attention(q, kc, vc, pool_rows, qsl, seq, bs)
+    for r in full:
+        assert np.array_equal(full[r], ref_full[r])
