@@ -15,18 +15,11 @@
 // 32 queries.  Tiles are numbered from the END of each request and dispatched
 // in that order, so the tiles with the most keys start first (longest-first
 // scheduling over uneven chunks).  All waves of a workgroup share each 64-key
-// K/V tile in LDS.  Two kernels:
-//   * prefill_pp_kernel (16-bit caches, and 8-bit caches with head_dim 128):
-//     8 waves, 256/hpw queries, K/V tiles copied global -> LDS by DMA into
-//     4-stage rings, and two groups of 4 waves alternating between the MFMA
-//     phase and the softmax phase (see the kernel's own comment); 8-bit
-//     tiles land in a ring of their own and each wave widens the rows it
-//     copied into two bf16/fp16 operand stages;
-//   * prefill_kernel (8-bit caches with head_dim 64): 4 waves, 128/hpw
-//     queries, tiles staged through registers and widened to bf16/fp16 when
-//     written to LDS (double-buffered, one barrier per tile): K row-major
-//     with padded rows, V transposed (key bits 2 and 3 swapped so the 8 keys
-//     one lane feeds into one MFMA step are adjacent).
+// K/V tile in LDS.  One kernel, prefill_pp_kernel: 8 waves, 256/hpw queries,
+// K/V tiles copied global -> LDS by DMA into 4-stage rings, and two groups of
+// 4 waves alternating between the MFMA phase and the softmax phase (see the
+// kernel's own comment); 8-bit tiles (fp8, int8) land in a ring of their own
+// and each wave widens the rows it copied into two bf16/fp16 operand stages.
 // Per tile a wave computes S^T = K . Q^T (v_mfma_f32_32x32x16, keys x queries)
 // so each lane holds 32 scores of ONE query: the row max needs one exchange
 // with the lane 32 apart and every rescale is lane-local.  The probabilities,
@@ -50,8 +43,6 @@ namespace pa {
 
 namespace {
 
-constexpr int kWaves = 4;
-constexpr int kThreads = 64 * kWaves;
 constexpr int kBlock = 16;
 constexpr int kTileK = 64;          // keys per LDS tile
 constexpr float kRescaleLog2 = 8.f; // lazy rescale threshold (log2 units)
@@ -74,346 +65,10 @@ __device__ inline void window_alibi(f32x16 (&sc)[2], int k0, int half, int qpos,
     }
 }
 
-__device__ inline int swap_bits23(int k) {
-  return (k & ~0xC) | ((k & 0x4) << 1) | ((k & 0x8) >> 1);
-}
-
-template <int D, int KVB>
-struct TileShape {
-  static constexpr int kElems = 16 / KVB;                 // cache elements per 16-byte chunk
-  static constexpr int kChunksPerRow = D / kElems;
-  static constexpr int kKChunks = kTileK * kChunksPerRow;  // K chunks per tile
-  static constexpr int kKPerThread = (kKChunks + kThreads - 1) / kThreads;
-  static constexpr int kVUnits = (kTileK / 4) * kChunksPerRow;  // (4 keys x 1 chunk) units
-  static constexpr int kVPerThread = (kVUnits + kThreads - 1) / kThreads;
-  static constexpr int KROW = D + 8;        // Ks row stride (elements)
-  static constexpr int VROW = kTileK + 8;   // Vt row stride (elements)
-  static constexpr int kKsElems = kTileK * KROW;
-  static constexpr int kVtElems = D * VROW;
-};
-
-template <int D, int KVB>
-struct TileRegs {
-  using TS = TileShape<D, KVB>;
-  u32x4 k[TS::kKPerThread];
-  u32x4 v[TS::kVPerThread][4];
-};
-
-struct TileCtx {
-  const unsigned char* kc;
-  const unsigned char* vc;
-  const int32_t* bt_row;
-  int64_t tok_stride, blk_stride, head_off, num_blocks;
-  int nblk, s_eff;
-};
-
-// Physical block id of logical block bi, or -1 if absent (past the sequence
-// or outside the pool).  bi must be uniform across the wave: the table entry
-// is then a scalar load, which never waits on the vector-memory counter (and
-// so never on K/V transfers still in flight).
-__device__ inline int block_id(const TileCtx& c, int bi) {
-  bi = __builtin_amdgcn_readfirstlane(bi);
-  int id = -1;
-  if (bi < c.nblk) id = load_uniform(c.bt_row, bi);
-  return (id >= 0 && (int64_t)id < c.num_blocks) ? id : -1;
-}
-
-// Bit b set: block b of tile kt is present (uniform across the workgroup).
-__device__ inline unsigned tile_okmask(const TileCtx& c, int kt) {
-  unsigned mask = 0;
-#pragma unroll
-  for (int b = 0; b < kTileK / kBlock; ++b)
-    mask |= (block_id(c, kt * (kTileK / kBlock) + b) >= 0) ? (1u << b) : 0u;
-  return mask;
-}
-
-// Select one of the 4 block ids of a tile by a per-lane index (no arrays).
-__device__ inline int pick_id(int i, int b0, int b1, int b2, int b3) {
-  return i == 0 ? b0 : (i == 1 ? b1 : (i == 2 ? b2 : b3));
-}
-
-// Global -> registers for tile kt.  K: thread moves chunks (key, chunk) with
-// key = idx / chunks_per_row, so one wave instruction reads whole 256-byte
-// rows.  V: thread moves 4 consecutive keys of one chunk.  Keys past the
-// sequence or in absent blocks read a valid address and are replaced by
-// zeros, so a 0-probability key can never turn P.V into NaN; the loads are
-// unconditional (no divergent branches).
-template <int D, int KVB>
-__device__ inline void load_tile(TileRegs<D, KVB>& regs, const TileCtx& c, int kt) {
-  using TS = TileShape<D, KVB>;
-  const int key0 = kt * kTileK;
-  const u32x4 zero = {0u, 0u, 0u, 0u};
-  const int b0 = block_id(c, kt * 4 + 0), b1 = block_id(c, kt * 4 + 1);
-  const int b2 = block_id(c, kt * 4 + 2), b3 = block_id(c, kt * 4 + 3);
-#pragma unroll
-  for (int j = 0; j < TS::kKPerThread; ++j) {
-    const int idx = threadIdx.x + kThreads * j;
-    const int key = idx / TS::kChunksPerRow;
-    const int chunk = idx % TS::kChunksPerRow;
-    const int id = pick_id(key / kBlock, b0, b1, b2, b3);
-    const bool ok = (idx < TS::kKChunks) && id >= 0 && (key0 + key < c.s_eff);
-    const int64_t off = (int64_t)id * c.blk_stride + (int64_t)(key % kBlock) * c.tok_stride +
-                        c.head_off + chunk * 16;
-    const u32x4 v = ld16(c.kc + (ok ? off : 0));
-    regs.k[j] = ok ? v : zero;
-  }
-#pragma unroll
-  for (int j = 0; j < TS::kVPerThread; ++j) {
-    const int u = threadIdx.x + kThreads * j;
-    const int kg = u % 16, ch = u / 16;
-    const int id = pick_id(kg / 4, b0, b1, b2, b3);
-    const bool bok = (u < TS::kVUnits) && id >= 0;
-    const int64_t off0 = (int64_t)id * c.blk_stride + (int64_t)((4 * kg) % kBlock) * c.tok_stride +
-                         c.head_off + ch * 16;
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const bool ok = bok && (key0 + 4 * kg + i < c.s_eff);
-      const u32x4 v = ld16(c.vc + (ok ? off0 + i * c.tok_stride : 0));
-      regs.v[j][i] = ok ? v : zero;
-    }
-  }
-}
-
-template <int D, typename CT, int KVB, bool I8>
-__device__ inline void store_tile(const TileRegs<D, KVB>& regs, unsigned short* Ks,
-                                  unsigned short* Vt) {
-  using TS = TileShape<D, KVB>;
-  using M = Mfma<CT>;
-#pragma unroll
-  for (int j = 0; j < TS::kKPerThread; ++j) {
-    const int idx = threadIdx.x + kThreads * j;
-    if (idx < TS::kKChunks) {
-      const int key = idx / TS::kChunksPerRow;
-      const int d0 = (idx % TS::kChunksPerRow) * TS::kElems;
-      unsigned short* dst = Ks + key * TS::KROW + d0;
-      if constexpr (KVB == 2) {
-        *reinterpret_cast<u32x4*>(dst) = regs.k[j];
-      } else {
-        const u32x4& w = regs.k[j];
-        *reinterpret_cast<u32x4*>(dst) =
-            u32x4{widen8x2<CT, I8>(w[0], false), widen8x2<CT, I8>(w[0], true),
-                  widen8x2<CT, I8>(w[1], false), widen8x2<CT, I8>(w[1], true)};
-        *reinterpret_cast<u32x4*>(dst + 8) =
-            u32x4{widen8x2<CT, I8>(w[2], false), widen8x2<CT, I8>(w[2], true),
-                  widen8x2<CT, I8>(w[3], false), widen8x2<CT, I8>(w[3], true)};
-      }
-    }
-  }
-#pragma unroll
-  for (int j = 0; j < TS::kVPerThread; ++j) {
-    const int u = threadIdx.x + kThreads * j;
-    if (u < TS::kVUnits) {
-      const int kg = u % 16, ch = u / 16;
-      const int col = swap_bits23(4 * kg);   // 4 consecutive keys stay adjacent
-      const u32x4* v = regs.v[j];
-      if constexpr (KVB == 2) {
-#pragma unroll
-        for (int e = 0; e < 8; ++e) {
-          const unsigned sel = (e & 1) ? 0x07060302u : 0x05040100u;
-          const u32x2 w{perm(v[1][e >> 1], v[0][e >> 1], sel), perm(v[3][e >> 1], v[2][e >> 1], sel)};
-          *reinterpret_cast<u32x2*>(Vt + (ch * 8 + e) * TS::VROW + col) = w;
-        }
-      } else {
-#pragma unroll
-        for (int m = 0; m < 8; ++m) {   // d pair (2m, 2m+1) of the 16-element chunk
-          unsigned cv[4];
-#pragma unroll
-          for (int i = 0; i < 4; ++i) cv[i] = widen8x2<CT, I8>(v[i][m >> 1], (m & 1) != 0);
-          const u32x2 lo{perm(cv[1], cv[0], 0x05040100u), perm(cv[3], cv[2], 0x05040100u)};
-          const u32x2 hi{perm(cv[1], cv[0], 0x07060302u), perm(cv[3], cv[2], 0x07060302u)};
-          *reinterpret_cast<u32x2*>(Vt + (ch * 16 + 2 * m) * TS::VROW + col) = lo;
-          *reinterpret_cast<u32x2*>(Vt + (ch * 16 + 2 * m + 1) * TS::VROW + col) = hi;
-        }
-      }
-    }
-  }
-}
-
-template <int D, typename CT, int KVB, bool I8, bool MASK>
-__global__ __launch_bounds__(kThreads, 2) void prefill_kernel(AttnParams p, int hpw) {
-  using M = Mfma<CT>;
-  using vec8 = typename M::vec8;
-  using TS = TileShape<D, KVB>;
-  constexpr int QS = D / 16;      // QK MFMA steps (16 d each)
-  constexpr int DT = D / 32;      // 32-row d tiles of O^T
-
-  __shared__ __attribute__((aligned(16))) unsigned short Ks[2][TS::kKsElems];
-  __shared__ __attribute__((aligned(16))) unsigned short Vt[2][TS::kVtElems];
-
-  const int r = p.req_begin + blockIdx.y;
-  const int q_first = p.qsl[r];
-  const int n = p.qsl[r + 1] - q_first;
-  const int QB = 128 / hpw;
-  const int q_hi = n - (int)blockIdx.z * QB;      // tile j covers queries [q_hi - QB, q_hi)
-  if (q_hi <= 0) return;
-  const int G = p.group;
-  const int s_all = p.seq_lens[r];
-  const int c = s_all - n;
-  int s_eff = min(s_all, p.max_seq_len);
-  s_eff = min(s_eff, p.max_blocks_per_req * kBlock);
-  const int k_end = min(c + q_hi, s_eff);          // keys any query of the tile may see
-  const int ntiles = (k_end + kTileK - 1) / kTileK;
-  // first key tile any query of the tile may see (a sliding window skips the rest)
-  const int kt0 = MASK ? max(0, c + max(q_hi - QB, 0) - p.window_left) / kTileK : 0;
-
-  const int lane = threadIdx.x & 63;
-  const int wave = wave_uniform(threadIdx.x >> 6);
-  const int half = lane >> 5;
-  const int l32 = lane & 31;
-  const int qh = blockIdx.x * hpw + (wave % hpw);
-  const int kvh = qh / G;
-  const int wq0 = q_hi - QB + (wave / hpw) * 32;   // first query of the wave (may be < 0)
-  const int qi = wq0 + l32;                        // this lane's query
-  const bool q_ok = qi >= 0;
-  const int qpos = c + qi;
-
-  // Q as the B operand of S^T = K . Q^T: B[k = 8*half + e][col = l32] = Q[qi][16 s + 8 half + e]
-  vec8 qop[QS];
-  {
-    const CT* qrow = static_cast<const CT*>(p.q) + (int64_t)(q_first + (q_ok ? qi : 0)) * p.q_row_stride +
-                     (int64_t)qh * D;
-#pragma unroll
-    for (int s = 0; s < QS; ++s) {
-      qop[s] = q_ok ? __builtin_bit_cast(vec8, ld16(qrow + 16 * s + 8 * half))
-                    : __builtin_bit_cast(vec8, u32x4{0u, 0u, 0u, 0u});
-    }
-  }
-
-  TileCtx tc;
-  tc.kc = static_cast<const unsigned char*>(p.key_cache);
-  tc.vc = static_cast<const unsigned char*>(p.value_cache);
-  tc.bt_row = p.block_tables + (int64_t)r * p.max_blocks_per_req;
-  tc.tok_stride = (int64_t)p.num_kv_heads * D * KVB;
-  tc.blk_stride = tc.tok_stride * kBlock;
-  tc.head_off = (int64_t)kvh * D * KVB;
-  tc.num_blocks = p.num_blocks;
-  tc.s_eff = s_eff;
-  tc.nblk = (s_eff + kBlock - 1) / kBlock;
-
-  // masked variants move the scores to log2 units themselves (window_alibi)
-  const float c2 = MASK ? 1.f : p.scale_log2;
-  const float slope2 = (MASK && p.alibi != nullptr)
-                           ? __builtin_bit_cast(float, load_uniform(reinterpret_cast<const int32_t*>(p.alibi), qh)) * kLog2e
-                           : 0.f;
-  f32x16 acc[DT];
-#pragma unroll
-  for (int t = 0; t < DT; ++t) acc[t] = f32x16{};
-  float m_used = -INFINITY, l_run = 0.f;
-  const int wave_first_pos = c + wq0;
-  const int wave_last_pos = c + wq0 + 31;
-
-  TileRegs<D, KVB> regs;
-  if (ntiles > kt0) {
-    load_tile<D, KVB>(regs, tc, kt0);
-    store_tile<D, CT, KVB, I8>(regs, Ks[0], Vt[0]);
-  }
-  __syncthreads();
-  for (int kt = kt0; kt < ntiles; ++kt) {
-    const int buf = (kt - kt0) & 1;
-    if (kt + 1 < ntiles) load_tile<D, KVB>(regs, tc, kt + 1);
-    const int k0 = kt * kTileK;
-    if (k0 <= wave_last_pos && (!MASK || k0 + kTileK - 1 >= wave_first_pos - p.window_left)) {
-      // ---- S^T (keys x queries), two 32-key subtiles ----
-      f32x16 sc[2];
-#pragma unroll
-      for (int u = 0; u < 2; ++u) {
-        f32x16 a = f32x16{};
-        const unsigned short* krow = Ks[buf] + (32 * u + l32) * TS::KROW + 8 * half;
-#pragma unroll
-        for (int s = 0; s < QS; ++s) {
-          const vec8 kop = __builtin_bit_cast(vec8, *reinterpret_cast<const u32x4*>(krow + 16 * s));
-          a = M::mma32(kop, qop[s], a);
-        }
-        sc[u] = a;
-      }
-      // ---- causal / length / absent-block mask ----
-      const unsigned okmask = tile_okmask(tc, kt);
-      const bool all_ok = okmask == 0xFu;
-      if (k0 + kTileK - 1 > wave_first_pos || k0 + kTileK > s_eff || !all_ok) {
-#pragma unroll
-        for (int u = 0; u < 2; ++u)
-#pragma unroll
-          for (int g = 0; g < 16; ++g) {
-            const int key = k0 + 32 * u + 8 * (g / 4) + 4 * half + (g % 4);
-            const bool blk = (okmask >> (2 * u + (g >= 8 ? 1 : 0))) & 1u;   // the key's block
-            sc[u][g] = (key > qpos || key >= s_eff || !blk) ? -INFINITY : sc[u][g];
-          }
-      }
-      if constexpr (MASK) window_alibi(sc, k0, half, qpos, p.window_left, p.scale_log2, slope2);
-      float mx = -INFINITY;
-#pragma unroll
-      for (int u = 0; u < 2; ++u)
-#pragma unroll
-        for (int g = 0; g < 16; ++g) mx = fmaxf(mx, sc[u][g]);
-      mx = pair32_max(mx);
-      // ---- lazy rescale: move the reference max only when it grew by > 2^8 ----
-      const bool grow = (m_used == -INFINITY) ? (mx > -INFINITY) : ((mx - m_used) * c2 > kRescaleLog2);
-      if (__builtin_amdgcn_read_exec() & __ballot(grow)) {
-        const float m_new = grow ? mx : m_used;
-        const float alpha = (m_used == -INFINITY) ? 0.f : fast_exp2((m_used - m_new) * c2);
-        l_run *= alpha;
-#pragma unroll
-        for (int t = 0; t < DT; ++t) acc[t] *= alpha;
-        m_used = m_new;
-      }
-      const float mref = (m_used == -INFINITY) ? 0.f : m_used * c2;
-      float psum = 0.f;
-#pragma unroll
-      for (int u = 0; u < 2; ++u)
-#pragma unroll
-        for (int g = 0; g < 16; ++g) {
-          const float e = fast_exp2(__builtin_fmaf(sc[u][g], c2, -mref));
-          sc[u][g] = e;
-          psum += e;
-        }
-      l_run += psum;
-
-      // ---- O^T += V^T . P^T, four 16-key steps ----
-#pragma unroll
-      for (int u = 0; u < 2; ++u) {
-#pragma unroll
-        for (int v = 0; v < 2; ++v) {
-          const u32x4 pw{pack2<CT>(sc[u][8 * v + 0], sc[u][8 * v + 1]),
-                         pack2<CT>(sc[u][8 * v + 2], sc[u][8 * v + 3]),
-                         pack2<CT>(sc[u][8 * v + 4], sc[u][8 * v + 5]),
-                         pack2<CT>(sc[u][8 * v + 6], sc[u][8 * v + 7])};
-          const vec8 pop = __builtin_bit_cast(vec8, pw);
-          const int col = 32 * u + 16 * v + 8 * half;   // Vt column of this lane's 8 keys
-#pragma unroll
-          for (int t = 0; t < DT; ++t) {
-            const vec8 vop = __builtin_bit_cast(
-                vec8, *reinterpret_cast<const u32x4*>(Vt[buf] + (32 * t + l32) * TS::VROW + col));
-            acc[t] = M::mma32(vop, pop, acc[t]);
-          }
-        }
-      }
-    }
-    if (kt + 1 < ntiles) store_tile<D, CT, KVB, I8>(regs, Ks[buf ^ 1], Vt[buf ^ 1]);
-    __syncthreads();
-  }
-
-  // ---- normalise and store: lane holds O[qi][32 t + 8 j + 4 half + i] ----
-  const float lt = pair32_sum(l_run);
-  if (!q_ok) return;
-  const float inv = (lt > 0.f) ? p.v_scale / lt : 0.f;
-  unsigned short* orow = static_cast<unsigned short*>(p.out) +
-                         (int64_t)(q_first + qi) * p.out_row_stride + (int64_t)qh * D;
-#pragma unroll
-  for (int t = 0; t < DT; ++t) {
-#pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      const int d = 32 * t + 8 * j + 4 * half;
-      u32x2 w{pack2<CT>(acc[t][4 * j] * inv, acc[t][4 * j + 1] * inv),
-              pack2<CT>(acc[t][4 * j + 2] * inv, acc[t][4 * j + 3] * inv)};
-      st8(orow + d, w);
-    }
-  }
-}
-
 // ---------------------------------------------------------------------------
-// 16-bit caches: K/V tiles are moved global -> LDS by the DMA path
-// (global_load_lds, 16 bytes per lane, no registers) and V is read back
-// transposed with ds_read_b64_tr_b16.
+// K/V tiles are moved global -> LDS by the DMA path (global_load_lds, 16
+// bytes per lane, no registers) and V is read back transposed with
+// ds_read_b64_tr_b16.
 //
 // LDS layout: per tile, K and V are each [64 keys][D/8 16-byte chunks] with
 // the chunks of key k stored at position (chunk ^ sw(k)); one DMA wave
@@ -476,7 +131,8 @@ __device__ inline u32x2 lds_read_tr16(const u32x4* base, int pos16, int byte_off
 // its table entries once up front; only rows holding ids outside the pool
 // test block presence per tile.
 // 8-bit caches: the copies fill rings of 8-bit tiles in plain [key][chunk]
-// order (one 1 KB instruction per wave per tile), and at the end of M(j)
+// order (one instruction per wave per tile: 1 KB at head_dim 128, 512 bytes
+// from the lower 32 lanes at head_dim 64), and at the end of M(j)
 // each wave widens the rows it copied of K tile j+1 and V tile j into two
 // operand stages (tile t in stage t % 2, LdsTile layout, V rows of absent
 // keys zeroed); the barrier that ends M(j) publishes them.  Two operand
@@ -526,10 +182,14 @@ __global__ __launch_bounds__(kPPThreads) void prefill_pp_kernel(AttnParams p, in
   constexpr int CPR8 = D / 16;               // 16-byte chunks of an 8-bit key row
   constexpr int kPos8 = kTileK * CPR8;       // 16-byte positions of an 8-bit tile
   constexpr int kCopyPos = KVB == 2 ? L::kPos : kPos8;
-  constexpr int IPW = kCopyPos / 64 / kPPWaves;   // copy instructions per wave per tile (K and V each)
-  constexpr int KPI = 64 / (KVB == 2 ? L::CPR : CPR8);   // keys per copy instruction
+  // lanes of a copy instruction: an 8-bit tile at head_dim 64 (4 KB) is too
+  // small for eight full-wave instructions, so each wave copies 512 bytes
+  // with its lower 32 lanes
+  constexpr int LPI = kCopyPos >= 64 * kPPWaves ? 64 : kCopyPos / kPPWaves;
+  constexpr int IPW = kCopyPos / LPI / kPPWaves;   // copy instructions per wave per tile (K and V each)
+  constexpr int KPI = LPI / (KVB == 2 ? L::CPR : CPR8);   // keys per copy instruction
   constexpr int PPS = 4 * DT / QS;           // PV MFMAs per QK step
-  static_assert(IPW * kPPWaves * 64 == kCopyPos && PPS * QS == 4 * DT, "tile shape");
+  static_assert(IPW * kPPWaves * LPI == kCopyPos && PPS * QS == 4 * DT, "tile shape");
   static_assert(2 * IPW * KPI == kBlock, "two waves copy each block of a tile");
   static_assert(KVB == 2 || IPW == 1, "8-bit tiles: one copy instruction per wave");
   constexpr unsigned kTileBytes = kCopyPos * 16;
@@ -614,13 +274,14 @@ __global__ __launch_bounds__(kPPThreads) void prefill_pp_kernel(AttnParams p, in
   };
 
   // copy roles (tile-invariant): instruction i of this wave fills positions
-  // inst*64 .. inst*64+63 of a tile, inst = wave*IPW + i: keys of block
+  // inst*LPI .. inst*LPI+LPI-1 of a tile, inst = wave*IPW + i: keys of block
   // wave/2 of the tile only, so a wave needs one block id per tile
   const int cb = wave >> 1;
+  const bool copy_lane = LPI == 64 || lane < LPI;
   unsigned koff[IPW], voff[IPW];
 #pragma unroll
   for (int i = 0; i < IPW; ++i) {
-    const int pidx = (wave * IPW + i) * 64 + lane;
+    const int pidx = (wave * IPW + i) * LPI + (copy_lane ? lane : 0);
     if constexpr (KVB == 2) {
       const int key = pidx / L::CPR, pos = pidx % L::CPR;
       const unsigned row = (unsigned)((key % kBlock) * tok_stride);
@@ -644,9 +305,11 @@ __global__ __launch_bounds__(kPPThreads) void prefill_pp_kernel(AttnParams p, in
   auto copy_tile = [&](const unsigned char* base, const unsigned (&off)[IPW], int id,
                        unsigned lds0) __attribute__((always_inline)) {
     const unsigned char* src = base + (int64_t)id * blk_stride;
+    if (copy_lane) {
 #pragma unroll
-    for (int i = 0; i < IPW; ++i)
-      lds_dma16<false, false>(src, off[i], lds0 + (unsigned)(wave * IPW + i) * 1024u);
+      for (int i = 0; i < IPW; ++i)
+        lds_dma16<false, false>(src, off[i], lds0 + (unsigned)((wave * IPW + i) * LPI * 16));
+    }
   };
   // after the copy of V tile t has landed: zero the rows of keys the tile
   // lacks (past the sequence, absent blocks), each lane exactly the positions
@@ -656,7 +319,7 @@ __global__ __launch_bounds__(kPPThreads) void prefill_pp_kernel(AttnParams p, in
     const unsigned ok = okmask(t);
 #pragma unroll
     for (int i = 0; i < IPW; ++i) {
-      const int pidx = (wave * IPW + i) * 64 + lane;
+      const int pidx = (wave * IPW + i) * LPI + lane;
       const int key = pidx / L::CPR;
       if (kTileK * t + key >= s_eff || !((ok >> (key / kBlock)) & 1u)) Vs[pidx] = u32x4{0u, 0u, 0u, 0u};
     }
@@ -667,7 +330,8 @@ __global__ __launch_bounds__(kPPThreads) void prefill_pp_kernel(AttnParams p, in
   // of keys the tile lacks become zeros (K rows need not: their scores are
   // masked by selects)
   auto widen = [&](const u32x4* src8, u32x4* dst, int t, bool is_v) __attribute__((always_inline)) {
-    const int pidx = wave * 64 + lane;
+    if (!copy_lane) return;
+    const int pidx = wave * LPI + lane;
     const int key = pidx / CPR8, c8 = pidx % CPR8;
     const u32x4 w = src8[pidx];
     u32x4 lo{widen8x2<CT, I8>(w[0], false), widen8x2<CT, I8>(w[0], true),
@@ -917,23 +581,15 @@ int heads_per_wg(int G) {
 template <int D, typename CT, int KVB, bool I8 = false>
 hipError_t launch_typed(const AttnParams& p, hipStream_t stream) {
   const int hpw = heads_per_wg(p.group);
-  const int QB = (KVB == 2 || D == 128 ? 32 * kPPWaves : 128) / hpw;
+  const int QB = 32 * kPPWaves / hpw;
   const int qtiles = (p.max_query_len + QB - 1) / QB;
   if (qtiles == 0) return hipSuccess;
   // x: query-head group, y: request, z: tile counted from the end of the request
   dim3 grid((unsigned)(p.num_q_heads / hpw), (unsigned)p.num_reqs, (unsigned)qtiles);
-  if constexpr (KVB == 2 || D == 128) {
-    if (p.masked) {
-      hipLaunchKernelGGL((prefill_pp_kernel<D, CT, KVB, I8, true>), grid, dim3(kPPThreads), 0, stream, p, hpw);
-    } else {
-      hipLaunchKernelGGL((prefill_pp_kernel<D, CT, KVB, I8, false>), grid, dim3(kPPThreads), 0, stream, p, hpw);
-    }
+  if (p.masked) {
+    hipLaunchKernelGGL((prefill_pp_kernel<D, CT, KVB, I8, true>), grid, dim3(kPPThreads), 0, stream, p, hpw);
   } else {
-    if (p.masked) {
-      hipLaunchKernelGGL((prefill_kernel<D, CT, KVB, I8, true>), grid, dim3(kThreads), 0, stream, p, hpw);
-    } else {
-      hipLaunchKernelGGL((prefill_kernel<D, CT, KVB, I8, false>), grid, dim3(kThreads), 0, stream, p, hpw);
-    }
+    hipLaunchKernelGGL((prefill_pp_kernel<D, CT, KVB, I8, false>), grid, dim3(kPPThreads), 0, stream, p, hpw);
   }
   return hipGetLastError();
 }
