@@ -13,7 +13,9 @@ invariants directly:
 * split invariance: different decode worker counts agree to float32 rounding;
 * aliasing: requests that share prefix blocks read them correctly;
 * absent blocks: table entries outside the pool hold no keys (rows with no
-  visible key are zero).
+  visible key are zero);
+* rising scores: prefill rows whose maxima grow after their first key tile,
+  a little, a lot, and past exp2's range against the old reference.
 """
 
 import numpy as np
@@ -38,6 +40,15 @@ def _need_gpu():
 
 def _slot(wl, r, j):
     return int(wl.block_tables[r, j // wl.block_size]) * wl.block_size + j % wl.block_size
+
+
+def _enc(wl, x, scale):
+    """x (float) as stored in the cache format."""
+    if wl.cache_fp8:
+        return torch.clamp(x / scale, -448, 448).to(torch.float8_e4m3fn).view(torch.uint8)
+    if wl.cache_int8:
+        return torch.clamp(torch.round(x / scale), -127, 127).to(torch.int8)
+    return x.to(wl.act_dtype)
 
 
 @pytest.mark.parametrize("case", ["gqa_bf16", "mqa_fp8", "mha_f16", "gqa_int8"])
@@ -68,11 +79,7 @@ def test_spike_positions(case):
     marker = torch.from_numpy(rng.choice([-3.0, 3.0], size=(wl.num_reqs, hkv, d))).float()
 
     def enc(x, scale):
-        if wl.cache_fp8:
-            return torch.clamp(x / scale, -448, 448).to(torch.float8_e4m3fn).view(torch.uint8)
-        if wl.cache_int8:
-            return torch.clamp(torch.round(x / scale), -127, 127).to(torch.int8)
-        return x.to(wl.act_dtype)
+        return _enc(wl, x, scale)
 
     positions = {}
     for r in range(wl.num_reqs):
@@ -240,3 +247,49 @@ def test_absent_blocks(kind, hq, hkv, d, act):
     assert err <= tol_of(wl), err
     assert torch.all(st.out[qsl[2]:qsl[3]] == 0)       # every block absent
     assert torch.all(st.out[qsl[7]:qsl[7] + 16] == 0)  # queries with no visible key
+
+
+@pytest.mark.parametrize("kind", ["act", "fp8", "int8"])
+@pytest.mark.parametrize("hq,hkv,d,act", [(8, 2, 128, torch.bfloat16), (8, 8, 64, torch.float16)])
+def test_prefill_rising_scores(kind, hq, hkv, d, act):
+    """Prefill rows whose score maxima rise after their first 64-key tile (the
+    tile that sets each row's reference max): by about 10 in log2 units (just
+    past the lazy-rescale threshold of 8), by about 40, and by more than 128
+    (exp2 against the old reference would overflow).  Every query of a request
+    shares one sign pattern per K/V head (amplitude qa); spike keys are that
+    pattern times an amplitude, in the cached prefix and among the new tokens."""
+    _need_gpu()
+    wl = S.random_batch(31 + d, [30], [(0, 300), (100, 200), (150, 100)], hq=hq, hkv=hkv, d=d,
+                        act=act, fp8=kind == "fp8", int8=kind == "int8")
+    t = S.make_tensors(wl, DEV)
+    G = wl.group
+    qsl, _, _, _ = oracle_metadata(wl)
+    rng = np.random.default_rng(17)
+    # random keys score ~N(0, qa^2) (natural units); a spike of amplitude a
+    # scores a * qa * sqrt(d); 8-bit formats saturate near 4.4 (the scale's amax)
+    qa = 2.5 if d == 128 else 3.0
+    a1 = 0.45 if d == 128 else 0.6
+    spikes = {1: [(70, a1), (150, 1.5)],        # new tokens: a small, then a large rise
+              2: [(230, 4.5)],                  # new token: exp2 overflow
+              3: [(100, 1.5), (210, 4.5)]}      # cached prefix, then a new token
+    for r, keys in spikes.items():
+        n = int(qsl[r + 1] - qsl[r])
+        c = int(wl.seq_lens_host[r]) - n
+        sign = torch.from_numpy(rng.choice([-1.0, 1.0], size=(hkv, d))).float()
+        t.q[qsl[r]:qsl[r + 1]] = (qa * sign).repeat_interleave(G, dim=0).to(act).to(DEV)
+        for pos, amp in keys:
+            k = amp * sign
+            if pos >= c:
+                t.k_new[qsl[r] + pos - c] = k.to(act).to(DEV)
+            else:
+                slot = _slot(wl, r, pos)
+                t.key_cache[slot // wl.block_size, slot % wl.block_size] = _enc(wl, k, t.k_scale).to(DEV)
+    requests = list(range(wl.num_reqs))
+    snap = Snapshot(wl, t, requests)
+    st = PagedAttentionStep(wl, t)
+    print(f"[rising] kind={kind} hq={hq} hkv={hkv} d={d}", flush=True)
+    st.run()
+    torch.cuda.synchronize()
+    expect = oracle_outputs(wl, t, snap, requests)
+    err, _ = compare(wl, st.out, expect, qsl)
+    assert err <= tol_of(wl), err
