@@ -113,8 +113,10 @@ __device__ inline u32x2 lds_read_tr16(const u32x4* base, int pos16, int byte_off
 //
 // Per wave and 64-key tile j the work splits into
 //   M(j): S_j = K_j . Q^T and O^T += V_{j-1}^T . P_{j-1}^T (MFMA, LDS reads)
-//   V(j): P_j from S_j (mask, row max, lazy rescale, exp2, bf16/fp16 pack,
-//         row sum), then the copies of K tile j+3 and V tile j+2 are issued
+//   V(j): the copies of K tile j+3 and V tile j+2 are issued first (the
+//         address unit works through the group's copies while the softmax
+//         runs, instead of holding up the barrier), then P_j from S_j (mask,
+//         row max, lazy rescale, exp2, bf16/fp16 pack, row sum)
 // and every wave runs M(j), barrier, V(j), barrier.  Group B passes one extra
 // barrier before its loop (group A one after it), so between two consecutive
 // barriers one group is in M and the other in V.
@@ -532,14 +534,14 @@ __global__ __launch_bounds__(kPPThreads) void prefill_pp_kernel(AttnParams p, in
       // ---- V(j) ----
       const int id_k = copy_id(raw_n, j + 3);
       raw_n = raw_id(j + 4);
+      if (j + 3 < ntiles) copy_tile(kbase, koff, id_k, kr0 + (unsigned)((ST + 3) % NS) * kTileBytes);
+      if (j + 2 < ntiles) copy_tile(vbase, voff, id_v, vr0 + (unsigned)((ST + 2) % NS) * kTileBytes);
       if (j < ntiles && active(j)) {
         softmax(j);
       } else {
 #pragma unroll
         for (int i = 0; i < 4; ++i) pk[i] = u32x4{0u, 0u, 0u, 0u};
       }
-      if (j + 3 < ntiles) copy_tile(kbase, koff, id_k, kr0 + (unsigned)((ST + 3) % NS) * kTileBytes);
-      if (j + 2 < ntiles) copy_tile(vbase, voff, id_v, vr0 + (unsigned)((ST + 2) % NS) * kTileBytes);
       id_v = id_k;
       barrier_nowait<false>();
     };
