@@ -30,8 +30,9 @@
 // overflows).
 // Mask variants (MASK instantiations; the alibi_slopes and window_size
 // arguments of the same call): a sliding window starts the key loop at the
-// first tile any query of the workgroup may see and skips a wave's math on
-// tiles wholly before its queries' windows; ALiBi adds slope * (key - query
+// first tile any query of the workgroup may see and skips a wave's softmax
+// on tiles wholly before its queries' windows (their MFMAs run with zero
+// probabilities); ALiBi adds slope * (key - query
 // position) to each score, applied together with the window mask when the
 // scores are moved to log2 units (window_alibi).
 #include <type_traits>
