@@ -206,12 +206,27 @@ __global__ __launch_bounds__(kPPThreads) void prefill_pp_kernel(AttnParams p, in
   // one request for consecutive head groups; workgroups are spread over the
   // 8 XCDs by number, so with 8 (or a multiple of 8) head groups an XCD keeps
   // the same K/V head and its L2 serves every query tile of the request the
-  // K/V stream it is reading.  Within a request the tiles run longest first.
+  // K/V stream it is reading.  Within a request the tiles run longest first,
+  // and when the launch holds at most 64 requests they are taken in order of
+  // decreasing sequence length (ties by index), so the longest tiles of the
+  // whole batch start first.
   const unsigned lin = blockIdx.x + gridDim.x * (blockIdx.y + gridDim.y * blockIdx.z);
   const unsigned bx = lin % gridDim.x;
   const unsigned bz = (lin / gridDim.x) % gridDim.z;
   const unsigned by = lin / (gridDim.x * gridDim.z);
-  const int r = p.req_begin + (int)by;
+  int rk = (int)by;
+  if (gridDim.y <= 64) {
+    const int nr = (int)gridDim.y;
+    const int l0 = (int)(threadIdx.x & 63);
+    const int key = l0 < nr ? p.seq_lens[p.req_begin + l0] : -1;
+    int rank = 0;
+    for (int j = 0; j < nr; ++j) {
+      const int kj = __builtin_amdgcn_readlane(key, j);
+      rank += (kj > key) | ((kj == key) & (j < l0));
+    }
+    rk = (int)__builtin_ctzll(__ballot(l0 < nr && rank == (int)by));
+  }
+  const int r = p.req_begin + rk;
   const int q_first = p.qsl[r];
   const int n = p.qsl[r + 1] - q_first;
   const int QB = (32 * kPPWaves) / hpw;
