@@ -208,24 +208,37 @@ __global__ __launch_bounds__(kPPThreads) void prefill_pp_kernel(AttnParams p, in
   // the same K/V head and its L2 serves every query tile of the request the
   // K/V stream it is reading.  Within a request the tiles run longest first,
   // and when the launch holds at most 64 requests they are taken in order of
-  // decreasing sequence length (ties by index), so the longest tiles of the
-  // whole batch start first.
+  // decreasing sequence length, so the longest tiles of the whole batch start
+  // first; requests of equal length share their turn tile by tile.
   const unsigned lin = blockIdx.x + gridDim.x * (blockIdx.y + gridDim.y * blockIdx.z);
   const unsigned bx = lin % gridDim.x;
-  const unsigned bz = (lin / gridDim.x) % gridDim.z;
-  const unsigned by = lin / (gridDim.x * gridDim.z);
-  int rk = (int)by;
+  unsigned bz = (lin / gridDim.x) % gridDim.z;
+  int rk = (int)(lin / (gridDim.x * gridDim.z));
   if (gridDim.y <= 64) {
+    // lane l < nr holds request l: `first` requests are longer, `same` are
+    // as long (itself included), `before` of those have a lower index
     const int nr = (int)gridDim.y;
+    const int gz = (int)gridDim.z;
     const int l0 = (int)(threadIdx.x & 63);
     const int key = l0 < nr ? p.seq_lens[p.req_begin + l0] : -1;
-    int rank = 0;
+    int first = 0, same = 0, before = 0;
     for (int j = 0; j < nr; ++j) {
       const int kj = __builtin_amdgcn_readlane(key, j);
-      rank += (kj > key) | ((kj == key) & (j < l0));
+      first += kj > key;
+      same += kj == key;
+      before += (kj == key) & (j < l0);
     }
-    rk = (int)__builtin_ctzll(__ballot(l0 < nr && rank == (int)by));
+    // the (request, tile) slots of a group of equally long requests are taken
+    // tile-major: every request's first tile, then every second tile, ...
+    const int t = (int)(lin / gridDim.x);
+    const int in_grp = t - first * gz;
+    const int m = max(same, 1);
+    const bool mine = l0 < nr && in_grp >= 0 && in_grp < same * gz && in_grp % m == before;
+    const int sel = (int)__builtin_ctzll(__ballot(mine));
+    rk = sel;
+    bz = (unsigned)__builtin_amdgcn_readlane(in_grp / m, sel);
   }
+  const unsigned by = (unsigned)rk;
   const int r = p.req_begin + rk;
   const int q_first = p.qsl[r];
   const int n = p.qsl[r + 1] - q_first;
