@@ -49,21 +49,35 @@ constexpr int kTileK = 64;          // keys per LDS tile
 constexpr float kRescaleLog2 = 8.f; // lazy rescale threshold (log2 units)
 constexpr float kLog2e = 1.4426950408889634f;
 
-// Mask variants (sliding window, ALiBi) of one score tile, in place: keys
-// before a query's window get -inf, then every score is moved to log2 units
-// with its ALiBi bias, slope * (key - query position).  The caller's softmax
-// then runs with a unit scale.  Lane layout as in the kernels: element g of
-// subtile u is key k0 + 32u + 8(g/4) + 4*half + g%4 of the lane's query.
+// Mask variants (sliding window, ALiBi) of one score tile, in place: every
+// score is moved to log2 units with its ALiBi bias, slope * (key - query
+// position), and on tiles that reach before some row's window (`edge`) the
+// keys before a row's window get -inf.  The caller's softmax then runs with a
+// unit scale.  Lane layout as in the kernel: element g of subtile u is key
+// k0 + 4*half + (32u + 8(g/4) + g%4) of the lane's query, so the bias is
+// slope * (k0 + 4*half - qpos) plus slope times a compile-time offset.
 __device__ inline void window_alibi(f32x16 (&sc)[2], int k0, int half, int qpos, int window_left,
-                                    float scale_log2, float slope2) {
+                                    float scale_log2, float slope2, bool edge) {
+  const int base = k0 + 4 * half - qpos;
+  const float sb = slope2 * (float)base;
 #pragma unroll
   for (int u = 0; u < 2; ++u)
 #pragma unroll
     for (int g = 0; g < 16; ++g) {
-      const int key = k0 + 32 * u + 8 * (g / 4) + 4 * half + (g % 4);
-      const float x = __builtin_fmaf(sc[u][g], scale_log2, slope2 * (float)(key - qpos));
-      sc[u][g] = (key < qpos - window_left) ? -INFINITY : x;
+      const int off = 32 * u + 8 * (g / 4) + (g % 4);
+      sc[u][g] = __builtin_fmaf(sc[u][g], scale_log2, __builtin_fmaf(slope2, (float)off, sb));
     }
+  if (edge) {
+    // key < qpos - window_left  <=>  off < -window_left - base (clamped to
+    // the offsets' range 0..63, in 64 bits so no window width can overflow)
+    const int64_t lim64 = -(int64_t)window_left - base;
+    const int lim = (int)(lim64 < -1 ? -1 : (lim64 > 64 ? 64 : lim64));
+#pragma unroll
+    for (int u = 0; u < 2; ++u)
+#pragma unroll
+      for (int g = 0; g < 16; ++g)
+        sc[u][g] = (32 * u + 8 * (g / 4) + (g % 4) < lim) ? -INFINITY : sc[u][g];
+  }
 }
 
 // ---------------------------------------------------------------------------
@@ -466,7 +480,8 @@ __global__ __launch_bounds__(kPPThreads) void prefill_pp_kernel(AttnParams p, in
           for (int g = 0; g < 8; ++g) sc[b >> 1][8 * (b & 1) + g] = -INFINITY;
         }
     }
-    if constexpr (MASK) window_alibi(sc, k0, half, qpos, p.window_left, p.scale_log2, slope2);
+    if constexpr (MASK)
+      window_alibi(sc, k0, half, qpos, p.window_left, p.scale_log2, slope2, k0 < wave_last_pos - p.window_left);
     // row max of the lane's 32 scores as a tree of three-input maxima (16
     // instructions, short dependency chains)
     float m10[11];
