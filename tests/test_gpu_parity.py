@@ -180,6 +180,23 @@ def test_small_mixed_parity(hq, hkv, d, act, kind):
     _run_and_check(wl)
 
 
+@pytest.mark.parametrize("case", ["equal_lengths", "many_requests"])
+def test_prefill_dispatch_order_parity(case):
+    """The prefill takes up to 64 requests longest first, equal lengths tile by
+    tile: a group of six requests of one sequence length with 1 to 300 new
+    tokens (so their tile counts differ) and a pair of another length; past 64
+    requests the launch order is kept (70 small prefills)."""
+    if case == "equal_lengths":
+        prefills = [(0, 300), (100, 200), (50, 120), (200, 100), (0, 300), (250, 50), (50, 120),
+                    (299, 1)]
+        wl = S.random_batch(91, [40, 7], prefills, hq=16, hkv=4, d=128, act=torch.bfloat16)
+    else:
+        rng = np.random.default_rng(92)
+        prefills = [(int(c), int(n)) for c, n in zip(rng.integers(0, 80, 70), rng.integers(1, 90, 70))]
+        wl = S.random_batch(92, [33], prefills, hq=8, hkv=2, d=64, act=torch.float16)
+    _run_and_check(wl)
+
+
 @pytest.mark.parametrize("workers", [1, 7, 64, 1000, 5000])
 def test_long_decode_split_parity(workers):
     """Long contexts cut between decode workers in every way: one worker (no
