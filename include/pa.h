@@ -87,7 +87,9 @@ typedef enum pa_dtype {
  * act_dtype F16 or BF16; cache_dtype equal to act_dtype, FP8_E4M3 or INT8;
  * G <= 32 for decode.
  *
- * softmax_scale multiplies q.k (1/sqrt(head_dim) is the usual value).
+ * softmax_scale multiplies q.k (1/sqrt(head_dim) is the usual value); it must
+ * be finite and > 0 (PA_ERR_INVALID_ARG otherwise: masked scores are -inf
+ * before the scale, and a zero or negative scale would make them NaN / +inf).
  * k_scale / v_scale apply to a quantized (fp8 or int8) cache only: a stored
  * code c means the value c * scale, one scale per tensor.  The write path
  * encodes y = float32(x) * (1.0f / scale) (one float32 multiply, the
@@ -108,6 +110,8 @@ typedef enum pa_dtype {
  * - sliding_window W > 0: the query at position p attends only keys j with
  *   p - W < j <= p (its W most recent positions, itself included); blocks
  *   wholly before the window are not read.  0 = plain causal attention.
+ *   A window of 2^30 keys or more sees every key (positions are below 2^30:
+ *   the attention calls reject max_seq_len > 2^30) and runs as such.
  * - alibi_slopes: when not NULL, query head h adds slope[h] * (j - p) to the
  *   scaled score softmax_scale * q.k of key j (fp8 / int8: the
  *   scale-corrected score) before the softmax.  The array stays owned by the caller and must
@@ -186,9 +190,9 @@ pa_status pa_cache_write(const pa_attn_desc* desc, int64_t num_tokens,
 
 /*
  * pa_rope_cache_write -- rotary position embedding of Q and K fused with the
- * cache write ("Tour: One forward pass", stop 9: the rotary embedding rotates q
- * and k by the positions of stop 3, a lookup in cos_sin_cache by position and
- * then the rotation of each head; followed by stop 10's cache write).  One
+ * cache write ("Tour: One forward pass", stop 9: RoPE turns q and k by each
+ * token's position from stop 3, using that position's cosines and sines from
+ * cos_sin_cache on every head's pairs; then stop 10's cache write).  One
  * kernel launch.
  *
  * positions: int64 [num_tokens] (as built by pa_metadata_build).
@@ -271,7 +275,7 @@ pa_status pa_copy_blocks(const pa_attn_desc* desc,
  *   out[qsl[r], h] = softmax_j(softmax_scale * q.k_j) v_j, k_j/v_j of K/V head
  *   h / G.
  * max_seq_len (host scalar) must be >= every seq_len of the range; keys past
- * it are ignored.  Accumulation is float32; out is act_dtype, rounded to
+ * it are ignored; above 2^30 the call returns PA_ERR_UNSUPPORTED.  Accumulation is float32; out is act_dtype, rounded to
  * nearest even.  The (request, K/V head, 16-token block) stream of the range
  * is cut into desc->decode_workers equal contiguous shares, one per wave;
  * a K/V head cut between waves leaves float32 partial results (running max,
@@ -321,7 +325,8 @@ pa_status pa_decode_workspace_size(const pa_attn_desc* desc, int32_t num_reqs,
  * new token sees the whole cached prefix and itself, never a later token).
  * max_query_len and max_seq_len (host scalars, as the tour's metadata keeps
  * them on the CPU) must bound every n and seq_len of the range; rows past
- * max_query_len are not computed.  Output rows of other requests and padding
+ * max_query_len are not computed; max_seq_len above 2^30 returns
+ * PA_ERR_UNSUPPORTED.  Output rows of other requests and padding
  * rows are never written.  Accumulation float32; out act_dtype.
  */
 pa_status pa_prefill_varlen(const pa_attn_desc* desc, int32_t req_begin, int32_t req_end,

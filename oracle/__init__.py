@@ -21,8 +21,8 @@ Sources (web pages; every function cites the part it follows):
   ``reshape_and_cache`` kernel description, the PagedAttention decode kernel
   signature, the KV-cache quantization remark and the ``LlamaAttention``
   listing (RoPE on Q and K before the cache write).
-* "Tour: One forward pass", stop 9 (the rotary embedding: a lookup in
-  ``cos_sin_cache`` by position, then the rotation of each head).
+* "Tour: One forward pass", stop 9 (RoPE on q and k: per-position cosines
+  and sines from ``cos_sin_cache`` turn every head's pairs).
 * "vLLM 推理全流程深度解析": the scheduler output's ``blocks_to_swap_in``,
   ``blocks_to_swap_out`` and ``blocks_to_copy`` lists, swapping to host memory
   and block sharing between sequences.

@@ -2,10 +2,10 @@
 (test infrastructure only).
 
 "Tour: One forward pass", stop 9 ("QKVParallelLinear and the rotary
-embedding"): after the fused QKV projection and split, the rotary embedding
-rotates q and k by the token positions of stop 3 -- a lookup in
-``cos_sin_cache`` by position, then the rotation of each head -- and the model
-uses the plain ``RotaryEmbedding`` (no scaling).  "vLLM MHA Code Path"
+embedding"): once the fused QKV output is split, q and k are turned by
+RoPE using each token's position from stop 3; the per-position cosines and
+sines come from the ``cos_sin_cache`` table and every head's pairs are rotated
+by them.  The model takes the unscaled ``RotaryEmbedding``.  "vLLM MHA Code Path"
 (worked decode trace, step 4) and the ``LlamaAttention`` listing of
 "vLLM 推理全流程深度解析" give the same order: RoPE on Q and K, then
 ``reshape_and_cache`` of K and V, then attention.

@@ -16,6 +16,11 @@ namespace {
 constexpr int kBlockSize = 16;
 constexpr int kMaxDecodeWorkers = 1 << 20;
 constexpr int kMaxGridYZ = 65535;
+// longest sequence the attention calls take: positions stay below 2^30, so a
+// sliding window of 2^30 keys or more leaves every key visible and is
+// clamped to that length (the kernels then never form position - window
+// below -2^31)
+constexpr int32_t kMaxSeqLen = 1 << 30;
 constexpr float kLog2e = 1.4426950408889634f;
 
 bool aligned16(const void* ptr) { return (reinterpret_cast<uintptr_t>(ptr) & 15u) == 0; }
@@ -39,7 +44,9 @@ pa_status check_desc(const pa_attn_desc* d) {
   }
   if (d->head_dim != 64 && d->head_dim != 128) return PA_ERR_UNSUPPORTED;
   if (d->block_size != kBlockSize) return PA_ERR_UNSUPPORTED;
-  if (!std::isfinite(d->softmax_scale)) return PA_ERR_INVALID_ARG;
+  // masked scores are -inf before the scale multiplies them: a zero or
+  // negative scale would turn them into NaN or +inf
+  if (!std::isfinite(d->softmax_scale) || !(d->softmax_scale > 0.f)) return PA_ERR_INVALID_ARG;
   if (quantized(d->cache_dtype)) {
     if (!(d->k_scale > 0.f) || !(d->v_scale > 0.f) || !std::isfinite(d->k_scale) ||
         !std::isfinite(d->v_scale)) {
@@ -361,7 +368,9 @@ static pa::AttnParams make_params(const pa_attn_desc* desc, int32_t req_begin, i
   p.out_row_stride = out_row_stride;
   p.scale_log2 = scale_log2(desc);
   p.v_scale = quantized(desc->cache_dtype) ? desc->v_scale : 1.0f;
-  p.window_left = desc->sliding_window > 0 ? desc->sliding_window - 1 : pa::kNoWindow;
+  p.window_left = (desc->sliding_window > 0 && desc->sliding_window - 1 < pa::kNoWindow)
+                      ? desc->sliding_window - 1
+                      : pa::kNoWindow;
   p.alibi = desc->alibi_slopes;
   p.masked = desc->sliding_window > 0 || desc->alibi_slopes != nullptr;
   return p;
@@ -391,6 +400,7 @@ pa_status pa_decode(const pa_attn_desc* desc, int32_t req_begin, int32_t req_end
                                    value_cache, num_blocks, out, out_row_stride);
   if (st != PA_OK) return st;
   if (max_seq_len < 0) return PA_ERR_INVALID_ARG;
+  if (max_seq_len > kMaxSeqLen) return PA_ERR_UNSUPPORTED;
   if (desc->num_q_heads / desc->num_kv_heads > 32) return PA_ERR_UNSUPPORTED;
   const int num_reqs = req_end - req_begin;
   if (num_reqs == 0) return PA_OK;
@@ -431,6 +441,7 @@ pa_status pa_prefill_varlen(const pa_attn_desc* desc, int32_t req_begin, int32_t
                                    value_cache, num_blocks, out, out_row_stride);
   if (st != PA_OK) return st;
   if (max_query_len < 0 || max_seq_len < 0) return PA_ERR_INVALID_ARG;
+  if (max_seq_len > kMaxSeqLen) return PA_ERR_UNSUPPORTED;
   if (req_end == req_begin || max_query_len == 0) return PA_OK;
   pa::AttnParams p = make_params(desc, req_begin, req_end, q, q_row_stride, query_start_loc,
                                  seq_lens, block_tables, max_blocks_per_req, key_cache,

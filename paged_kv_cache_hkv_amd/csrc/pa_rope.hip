@@ -1,10 +1,10 @@
 // pa_rope_cache_write kernel: rotary position embedding of Q and K fused with
 // the slot_mapping scatter of K and V.
 //
-// What is computed ("Tour: One forward pass", stop 9: the rotary embedding
-// rotates q and k by the positions of stop 3, a lookup in cos_sin_cache by
-// position and then the rotation of each head; stop 10: the cache write of K
-// and V; the same order in the LlamaAttention listing of "vLLM 推理全流程深度解析"):
+// What is computed ("Tour: One forward pass", stop 9: RoPE turns q and k by
+// each token's position from stop 3, with the per-position cosines and sines
+// of cos_sin_cache applied to every head's pairs; stop 10: the cache write of
+// K and V; the same order in the LlamaAttention listing of "vLLM 推理全流程深度解析"):
 // for token t at position p with cos_sin_cache[p] = (c_0..c_{R/2-1},
 // s_0..s_{R/2-1}), R = rotary_dim, every head of q and k has its pairs
 // (j, j + R/2) (half-split layout) or (2j, 2j+1) (interleaved) rotated:

@@ -75,6 +75,10 @@ def _write(desc, num_tokens=4, key=FAKE, stride=1024, kc=FAKE):
     (dict(cache_dtype=4), B.PA_ERR_INVALID_ARG),
     (dict(decode_workers=-1), B.PA_ERR_INVALID_ARG),
     (dict(softmax_scale=float("inf")), B.PA_ERR_INVALID_ARG),
+    # masked scores are -inf before the scale: 0 * -inf is NaN, a negative scale gives +inf
+    (dict(softmax_scale=0.0), B.PA_ERR_INVALID_ARG),
+    (dict(softmax_scale=-0.125), B.PA_ERR_INVALID_ARG),
+    (dict(softmax_scale=-0.0), B.PA_ERR_INVALID_ARG),
 ])
 def test_desc_rejections(kw, status):
     assert _write(_desc(**kw)) == status
@@ -136,6 +140,14 @@ def test_prefill_checks():
     assert f(out_stride=4092) == B.PA_ERR_INVALID_ARG
     assert f(mq=-1) == B.PA_ERR_INVALID_ARG
     assert f(mq=0) == B.PA_OK                                 # no query rows: nothing launched
+    # positions must stay below 2^30 (a window of 2^30 or more keys is then no window)
+    long = lambda ms: lib.pa_prefill_varlen(
+        ctypes.byref(d), 0, 3, FAKE, 4096, FAKE, FAKE, FAKE, 8, FAKE, FAKE, 100, 10, ms,
+        FAKE, 4096, None)
+    assert long((1 << 30) + 1) == B.PA_ERR_UNSUPPORTED
+    dlong = lib.pa_decode(ctypes.byref(d), 0, 3, FAKE, 4096, FAKE, FAKE, FAKE, 8, FAKE, FAKE,
+                          100, (1 << 30) + 1, FAKE, 1 << 40, FAKE, 4096, None)
+    assert dlong == B.PA_ERR_UNSUPPORTED
 
 
 def test_rope_cache_write_checks():

@@ -102,3 +102,11 @@ def test_decode_gqa_full_size_sampled():
 @pytest.mark.parametrize("hq,hkv,act", [(8, 2, torch.bfloat16), (32, 1, torch.float16)])
 def test_int8_cache(window, alibi, hq, hkv, act):
     _check(_mixed(60 + hq, hq, hkv, act, False, int8=True), window, alibi)
+
+
+@pytest.mark.parametrize("alibi", [False, True])
+def test_unbounded_window_walkthrough(alibi):
+    """A window of 2^31 - 1 keys (a caller's way to say "unbounded") on the tour's
+    batch: R3's first query tile holds rows before the sequence start, whose
+    window edge would fall below -2^31 in 32 bits; every key stays visible."""
+    _check(S.CONFIGS["walkthrough"](), 2 ** 31 - 1, alibi)
