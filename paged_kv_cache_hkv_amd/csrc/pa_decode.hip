@@ -483,8 +483,9 @@ __global__ __launch_bounds__(64 * WV) void decode_kernel(AttnParams p) {
       float pr[4];
 #pragma unroll
       for (int k = 0; k < 4; ++k) pr[k] = fast_exp2(x[k] - msub);
-      l_run[ht] += (pr[0] + pr[1]) + (pr[2] + pr[3]);
       pop[ht] = u32x2{pack2<CT>(pr[0], pr[1]), pack2<CT>(pr[2], pr[3])};
+      // the row sum adds the rounded probabilities the PV product multiplies
+      l_run[ht] = M::sum2(pop[ht][1], M::sum2(pop[ht][0], l_run[ht]));
     }
 
     // ---- O^T += V^T . P^T ----
