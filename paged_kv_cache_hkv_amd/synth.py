@@ -29,9 +29,12 @@ order; unused table entries are -1.  Tensor values are N(0, 1) draws in
 float32 from a seeded torch generator on the target device, rounded to the
 activation dtype.  Every block a table lists is filled with such draws; all
 other pool blocks are filled with NaN (0x7F for fp8), so a kernel that reads
-outside the table shows up.  For fp8 caches the per-tensor scale is
-float32(amax / 448) of the drawn values and the stored codes come from
-torch's own float8_e4m3fn cast.  For int8 caches the scale is
+outside the table shows up.  With ``poison`` the slots of each request's last
+listed block that lie at or past its sequence length are poisoned the same
+way (NaN / 0x7F / -128), so a read of a key past the sequence shows up too
+(for int8, -128 is finite: such a read only shows up through the error it
+adds).  For fp8 caches the per-tensor scale is float32(amax / 448) of the
+drawn values and the stored codes come from torch's own float8_e4m3fn cast.  For int8 caches the scale is
 float32(amax / 127) and the stored codes are the drawn values divided by the
 scale, rounded by torch.round and clamped to -127..127: the generator's own
 quantisation (the codes and the scale are simply inputs); unused blocks hold
@@ -243,6 +246,39 @@ def _randn(gen, shape, device):
     return torch.randn(shape, generator=gen, device=device, dtype=torch.float32)
 
 
+def _poison_value(cache):
+    if cache.dtype == torch.uint8:
+        return 0x7F           # fp8 e4m3fn NaN
+    if cache.dtype == torch.int8:
+        return -128           # a code the write path never produces
+    return float("nan")
+
+
+def tail_slots(wl):
+    """(block, slot) pairs past each request's sequence in its last listed block."""
+    bs = wl.block_size
+    blocks, slots = [], []
+    for r, s in enumerate(wl.seq_lens_host.tolist()):
+        if s <= 0 or s % bs == 0:
+            continue
+        b = int(wl.block_tables[r, (s - 1) // bs])
+        if 0 <= b < wl.pool_blocks:
+            for o in range(s % bs, bs):
+                blocks.append(b)
+                slots.append(o)
+    return np.asarray(blocks, np.int64), np.asarray(slots, np.int64)
+
+
+def _poison_tails(wl, kc, vc, device):
+    blocks, slots = tail_slots(wl)
+    if blocks.size == 0:
+        return
+    bi = torch.from_numpy(blocks).to(device)
+    si = torch.from_numpy(slots).to(device)
+    for cache in (kc, vc):
+        cache[bi, si] = _poison_value(cache)
+
+
 def make_tensors(wl, device, poison=True, chunk_blocks=8192):
     """Draw every tensor of the workload on ``device`` (deterministic per seed)."""
     device = torch.device(device)
@@ -303,6 +339,8 @@ def make_tensors(wl, device, poison=True, chunk_blocks=8192):
                 ids = used_t[lo:lo + chunk_blocks]
                 cache[ids] = _randn(gen, (ids.numel(), bs, hkv, d), device).to(act)
         k_scale = v_scale = 1.0
+    if poison:
+        _poison_tails(wl, kc, vc, device)
     return Tensors(
         q=q, k_new=k_new, v_new=v_new, key_cache=kc, value_cache=vc,
         num_computed=torch.from_numpy(wl.num_computed.astype(np.int32)).to(device),

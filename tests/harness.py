@@ -67,6 +67,55 @@ class Snapshot:
         self.vbits = cache_bits(tensors.value_cache.index_select(0, idx), one)
 
 
+class OraclePrep:
+    """The oracle's view of one step: its own metadata, its scatter of the
+    step's new K/V into the generator's snapshot (taken before the library
+    wrote to the pool), and the decoded queries.  Built once; rows for any set
+    of requests come from ``rows``."""
+
+    def __init__(self, wl, tensors, snapshot, qsl_len=None):
+        qsl, seq_lens, positions, slots = oracle_metadata(wl, qsl_len)
+        bs = wl.block_size
+        act = act_name(wl.act_dtype)
+        # remap the scatter to the snapshot's local block numbering
+        local_slots = []
+        for s in slots:
+            if s < 0 or (s // bs) not in snapshot.local:
+                local_slots.append(-1)
+            else:
+                local_slots.append(snapshot.local[s // bs] * bs + s % bs)
+        T = max(wl.num_tokens_padded, wl.num_tokens)
+        kb, vb = bits16(tensors.k_new[:T]), bits16(tensors.v_new[:T])
+        self.cache_dt = oracle_cache_dtype(wl)
+        k_inv = np.float32(1.0) / np.float32(tensors.k_scale)
+        v_inv = np.float32(1.0) / np.float32(tensors.v_scale)
+        self.kc, self.vc = OC.scatter(snapshot.kbits, snapshot.vbits, kb, vb, local_slots, bs,
+                                      act_dtype=act, cache_dtype=self.cache_dt, k_inv_scale=k_inv,
+                                      v_inv_scale=v_inv, num_tokens=T)
+        self.q = OD.decode(bits16(tensors.q), act)
+        self.qsl, self.seq_lens = qsl, seq_lens
+        self.wl, self.snapshot = wl, snapshot
+        self.k_scale, self.v_scale = tensors.k_scale, tensors.v_scale
+
+    def rows(self, requests, sliding_window=0, alibi_slopes=None):
+        """Oracle rows {r: float64 [n_r, Hq, D]} for the given requests."""
+        wl, snap, bs = self.wl, self.snapshot, self.wl.block_size
+        requests = list(requests)
+        wanted = set(requests)
+        table = []
+        for r in range(wl.num_reqs):
+            nb = -(-self.seq_lens[r] // bs)
+            if r in wanted:
+                table.append([snap.local.get(int(b), -1) for b in wl.block_tables[r, :nb]])
+            else:
+                table.append([])
+        return OA.paged_attention(self.q, self.kc, self.vc, table, self.qsl, self.seq_lens, bs,
+                                  requests=requests, cache_dtype=self.cache_dt,
+                                  k_scale=self.k_scale, v_scale=self.v_scale,
+                                  sliding_window=sliding_window, alibi_slopes=alibi_slopes,
+                                  num_blocks=len(snap.ids))
+
+
 def oracle_outputs(wl, tensors, snapshot, requests, qsl_len=None, sliding_window=0,
                    alibi_slopes=None):
     """Oracle rows {r: float64 [n_r, Hq, D]} for the given requests.
@@ -74,37 +123,8 @@ def oracle_outputs(wl, tensors, snapshot, requests, qsl_len=None, sliding_window
     Metadata and the scatter of the step's new K/V are the oracle's own; the
     pool is the generator's snapshot taken before the library wrote to it.
     """
-    qsl, seq_lens, positions, slots = oracle_metadata(wl, qsl_len)
-    bs = wl.block_size
-    act = act_name(wl.act_dtype)
-    # remap the scatter to the snapshot's local block numbering
-    local_slots = []
-    for s in slots:
-        if s < 0 or (s // bs) not in snapshot.local:
-            local_slots.append(-1)
-        else:
-            local_slots.append(snapshot.local[s // bs] * bs + s % bs)
-    T = max(wl.num_tokens_padded, wl.num_tokens)
-    kb, vb = bits16(tensors.k_new[:T]), bits16(tensors.v_new[:T])
-    cache_dt = oracle_cache_dtype(wl)
-    k_inv = np.float32(1.0) / np.float32(tensors.k_scale)
-    v_inv = np.float32(1.0) / np.float32(tensors.v_scale)
-    kc, vc = OC.scatter(snapshot.kbits, snapshot.vbits, kb, vb, local_slots, bs,
-                        act_dtype=act, cache_dtype=cache_dt, k_inv_scale=k_inv,
-                        v_inv_scale=v_inv, num_tokens=T)
-    q = OD.decode(bits16(tensors.q), act)
-    rows = []
-    for r in range(wl.num_reqs):
-        s = seq_lens[r]
-        nb = -(-s // bs)
-        if r in requests:
-            rows.append([snapshot.local.get(int(b), -1) for b in wl.block_tables[r, :nb]])
-        else:
-            rows.append([])
-    return OA.paged_attention(q, kc, vc, rows, qsl, seq_lens, bs, requests=requests,
-                              cache_dtype=cache_dt, k_scale=tensors.k_scale,
-                              v_scale=tensors.v_scale, sliding_window=sliding_window,
-                              alibi_slopes=alibi_slopes, num_blocks=len(snapshot.ids))
+    prep = OraclePrep(wl, tensors, snapshot, qsl_len)
+    return prep.rows(requests, sliding_window, alibi_slopes)
 
 
 def gpu_rows(out, qsl, r):

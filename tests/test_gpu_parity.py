@@ -3,9 +3,9 @@
 Bars: metadata and cache bytes bit-exact; attention max-abs within 5e-3
 (fp16), 2e-2 (bf16), 6e-2 (fp8 K/V, the oracle dequantising the identical
 codes); int8 K/V keep the activation dtype's bar (every code is exact in
-bf16 and fp16, so the cache format adds no rounding of its own).  Small shapes compare every output row; the five measured workloads
-run at full size in the launch configuration the benchmark times, and compare
-sampled requests (the oracle computes them one by one).
+bf16 and fp16, so the cache format adds no rounding of its own).  Small shapes
+compare every output row; the five measured workloads at full size are in
+test_gpu_full.py.
 """
 
 import numpy as np
@@ -205,27 +205,3 @@ def test_long_decode_split_parity(workers):
     wl = S.random_batch(77, [2047, 2048, 2049, 4000, 5000], [(3000, 5)], hq=32, hkv=4, d=128,
                         act=torch.bfloat16)
     _run_and_check(wl, workers=workers)
-
-
-@pytest.mark.parametrize("name,nsample,kind", [
-    ("decode_mha", 8, None), ("decode_gqa", 8, None), ("chunked_prefill_mix", 10, None),
-    ("mqa_fp8_long", 4, None),
-    # the same shapes over an int8 cache
-    ("decode_gqa", 6, "int8"), ("chunked_prefill_mix", 6, "int8"), ("mqa_fp8_long", 3, "int8"),
-])
-def test_full_config_sampled(name, nsample, kind):
-    """Full-size workload, as benchmarked; the oracle checks sampled requests."""
-    wl = S.CONFIGS[name]()
-    if kind is not None:
-        wl = S.with_cache(wl, kind)
-    rng = np.random.default_rng(1234)
-    nd = wl.num_decodes
-    req = set(rng.choice(nd, size=min(nsample, nd), replace=False).tolist()) if nd else set()
-    # always include the longest request and, for mixed batches, every prefill chunk
-    req.add(int(np.argmax(wl.seq_lens_host)))
-    if wl.num_decodes < wl.num_reqs:
-        # the longest prefill chunk and the one with the longest cached prefix
-        pre = np.arange(wl.num_decodes, wl.num_reqs)
-        req.add(int(pre[np.argmax(wl.query_lens[pre])]))
-        req.add(int(pre[np.argmax(wl.num_computed[pre])]))
-    _run_and_check(wl, requests=sorted(req))
