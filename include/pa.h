@@ -302,6 +302,33 @@ pa_status pa_decode(const pa_attn_desc* desc, int32_t req_begin, int32_t req_end
                     void* out, int64_t out_row_stride, void* stream);
 
 /*
+ * pa_decode_noalloc -- pa_decode without a caller's workspace, for callers
+ * that cannot allocate device memory (code under HIP graph capture, tight
+ * serving loops, harnesses that forbid allocation).  Same arguments, result
+ * and checks as pa_decode, minus the workspace pair.
+ *
+ * It uses a device array that the library holds, one per GPU, of
+ * PA_DECODE_NOALLOC_SCRATCH_BYTES bytes, which lives until the process ends;
+ * its address is looked up on the first call on each device.  The call
+ * allocates and frees nothing.  A call that would need more workspace than
+ * the array holds (pa_decode_workspace_size larger than
+ * PA_DECODE_NOALLOC_SCRATCH_BYTES) returns PA_ERR_WORKSPACE_TOO_SMALL and
+ * enqueues nothing.  Every call on one GPU shares that GPU's array: calls
+ * whose work may overlap on one GPU (other streams, other host threads)
+ * race and give undefined results; serialise them.  PA_ERR_HIP if the
+ * array's address cannot be obtained on the current device.
+ */
+#define PA_DECODE_NOALLOC_SCRATCH_BYTES ((size_t)32 << 20)
+
+pa_status pa_decode_noalloc(const pa_attn_desc* desc, int32_t req_begin, int32_t req_end,
+                            const void* q, int64_t q_row_stride,
+                            const int32_t* query_start_loc, const int32_t* seq_lens,
+                            const int32_t* block_tables, int32_t max_blocks_per_req,
+                            const void* key_cache, const void* value_cache, int64_t num_blocks,
+                            int32_t max_seq_len, void* out, int64_t out_row_stride,
+                            void* stream);
+
+/*
  * pa_decode_workspace_size -- bytes of workspace pa_decode needs for
  * num_reqs = req_end - req_begin requests of this desc (a prefix sum over the
  * requests, and two partial slots per worker of G float32 running maxima,

@@ -77,6 +77,8 @@ _SIGS = {
     "pa_copy_blocks": [ctypes.POINTER(AttnDesc), _P, _P, _I64, _P, _P, _I64, _P, _I64, _P],
     "pa_decode": [ctypes.POINTER(AttnDesc), _I32, _I32, _P, _I64, _P, _P, _P, _I32, _P, _P, _I64,
                   _I32, _P, _SZ, _P, _I64, _P],
+    "pa_decode_noalloc": [ctypes.POINTER(AttnDesc), _I32, _I32, _P, _I64, _P, _P, _P, _I32, _P, _P,
+                          _I64, _I32, _P, _I64, _P],
     "pa_decode_workspace_size": [ctypes.POINTER(AttnDesc), _I32, _I32, _I32, ctypes.POINTER(_SZ)],
     "pa_prefill_varlen": [ctypes.POINTER(AttnDesc), _I32, _I32, _P, _I64, _P, _P, _P, _I32, _P, _P,
                           _I64, _I32, _I32, _P, _I64, _P],
@@ -188,6 +190,16 @@ def pa_decode(desc, req_begin, req_end, q, query_start_loc, seq_lens, block_tabl
         _ptr(seq_lens), _ptr(block_tables), block_tables.shape[1], _ptr(key_cache),
         _ptr(value_cache), key_cache.shape[0], max_seq_len, _ptr(workspace), ws_bytes,
         _ptr(out), _row_stride(out), _stream(stream)), "pa_decode")
+
+
+def pa_decode_noalloc(desc, req_begin, req_end, q, query_start_loc, seq_lens, block_tables,
+                      key_cache, value_cache, max_seq_len, out, stream=None):
+    """pa_decode on the library's own per-GPU scratch array (no workspace argument)."""
+    _check(load().pa_decode_noalloc(
+        ctypes.byref(desc), req_begin, req_end, _ptr(q), _row_stride(q), _ptr(query_start_loc),
+        _ptr(seq_lens), _ptr(block_tables), block_tables.shape[1], _ptr(key_cache),
+        _ptr(value_cache), key_cache.shape[0], max_seq_len, _ptr(out), _row_stride(out),
+        _stream(stream)), "pa_decode_noalloc")
 
 
 def pa_prefill_varlen(desc, req_begin, req_end, q, query_start_loc, seq_lens, block_tables,

@@ -25,6 +25,7 @@ SOURCES = [
     "pa_rope.hip",
     "pa_decode.hip",
     "pa_prefill.hip",
+    "pa_noalloc.hip",
 ]
 
 ARCH = "gfx950"

@@ -9,6 +9,7 @@
 #include <cmath>
 #include <cstdint>
 
+#include "pa_decode_call.h"
 #include "pa_kernels.h"
 
 namespace {
@@ -395,38 +396,15 @@ pa_status pa_decode(const pa_attn_desc* desc, int32_t req_begin, int32_t req_end
                     const void* key_cache, const void* value_cache, int64_t num_blocks,
                     int32_t max_seq_len, void* workspace, size_t workspace_bytes, void* out,
                     int64_t out_row_stride, void* stream) {
-  pa_status st = check_attn_common(desc, req_begin, req_end, q, q_row_stride, query_start_loc,
-                                   seq_lens, block_tables, max_blocks_per_req, key_cache,
-                                   value_cache, num_blocks, out, out_row_stride);
-  if (st != PA_OK) return st;
-  if (max_seq_len < 0) return PA_ERR_INVALID_ARG;
-  if (max_seq_len > kMaxSeqLen) return PA_ERR_UNSUPPORTED;
-  if (desc->num_q_heads / desc->num_kv_heads > 32) return PA_ERR_UNSUPPORTED;
-  const int num_reqs = req_end - req_begin;
-  if (num_reqs == 0) return PA_OK;
-  const DecodePlan pl = plan_decode(desc, num_reqs);
-  // the kernel keeps a block's byte offset in 32 bits and each worker's share
-  // of the (request, K/V head, block) stream below 2^31 units
-  if ((int64_t)16 * desc->num_kv_heads * desc->head_dim * elem_bytes(desc->cache_dtype) > 0xFFFFFFFFll) {
-    return PA_ERR_UNSUPPORTED;
-  }
-  if ((double)num_reqs * desc->num_kv_heads * max_blocks_per_req >
-      (double)pl.workers * 2147483647.0) {
-    return PA_ERR_UNSUPPORTED;
-  }
-  if (workspace == nullptr || workspace_bytes < pl.ws_bytes) return PA_ERR_WORKSPACE_TOO_SMALL;
+  pa::DecodeCall call{};
+  pa_status st = pa::decode_prepare(desc, req_begin, req_end, q, q_row_stride, query_start_loc,
+                                    seq_lens, block_tables, max_blocks_per_req, key_cache,
+                                    value_cache, num_blocks, max_seq_len, out, out_row_stride,
+                                    &call);
+  if (st != PA_OK || call.empty) return st;
+  if (workspace == nullptr || workspace_bytes < call.ws_bytes) return PA_ERR_WORKSPACE_TOO_SMALL;
   if (!aligned16(workspace)) return PA_ERR_INVALID_ARG;
-  pa::AttnParams p = make_params(desc, req_begin, req_end, q, q_row_stride, query_start_loc,
-                                 seq_lens, block_tables, max_blocks_per_req, key_cache,
-                                 value_cache, num_blocks, out, out_row_stride);
-  p.max_seq_len = max_seq_len;
-  p.num_workers = pl.workers;
-  unsigned char* ws = static_cast<unsigned char*>(workspace);
-  p.ws_cum = reinterpret_cast<int64_t*>(ws + pl.cum_off);
-  p.ws_acc = reinterpret_cast<float*>(ws + pl.acc_off);
-  p.ws_ml = reinterpret_cast<float*>(ws + pl.ml_off);
-  return from_hip(pa::launch_decode(p, desc->act_dtype, desc->cache_dtype,
-                                    static_cast<hipStream_t>(stream)));
+  return pa::decode_launch(call, workspace, stream);
 }
 
 pa_status pa_prefill_varlen(const pa_attn_desc* desc, int32_t req_begin, int32_t req_end,
@@ -453,3 +431,57 @@ pa_status pa_prefill_varlen(const pa_attn_desc* desc, int32_t req_begin, int32_t
 }
 
 }  // extern "C"
+
+namespace pa {
+
+pa_status decode_prepare(const pa_attn_desc* desc, int32_t req_begin, int32_t req_end,
+                         const void* q, int64_t q_row_stride, const int32_t* query_start_loc,
+                         const int32_t* seq_lens, const int32_t* block_tables,
+                         int32_t max_blocks_per_req, const void* key_cache,
+                         const void* value_cache, int64_t num_blocks, int32_t max_seq_len,
+                         void* out, int64_t out_row_stride, DecodeCall* call) {
+  pa_status st = check_attn_common(desc, req_begin, req_end, q, q_row_stride, query_start_loc,
+                                   seq_lens, block_tables, max_blocks_per_req, key_cache,
+                                   value_cache, num_blocks, out, out_row_stride);
+  if (st != PA_OK) return st;
+  if (max_seq_len < 0) return PA_ERR_INVALID_ARG;
+  if (max_seq_len > kMaxSeqLen) return PA_ERR_UNSUPPORTED;
+  if (desc->num_q_heads / desc->num_kv_heads > 32) return PA_ERR_UNSUPPORTED;
+  const int num_reqs = req_end - req_begin;
+  call->empty = num_reqs == 0;
+  if (call->empty) return PA_OK;
+  const DecodePlan pl = plan_decode(desc, num_reqs);
+  // the kernel keeps a block's byte offset in 32 bits and each worker's share
+  // of the (request, K/V head, block) stream below 2^31 units
+  if ((int64_t)16 * desc->num_kv_heads * desc->head_dim * elem_bytes(desc->cache_dtype) > 0xFFFFFFFFll) {
+    return PA_ERR_UNSUPPORTED;
+  }
+  if ((double)num_reqs * desc->num_kv_heads * max_blocks_per_req >
+      (double)pl.workers * 2147483647.0) {
+    return PA_ERR_UNSUPPORTED;
+  }
+  call->p = make_params(desc, req_begin, req_end, q, q_row_stride, query_start_loc, seq_lens,
+                        block_tables, max_blocks_per_req, key_cache, value_cache, num_blocks, out,
+                        out_row_stride);
+  call->p.max_seq_len = max_seq_len;
+  call->p.num_workers = pl.workers;
+  call->cum_off = pl.cum_off;
+  call->acc_off = pl.acc_off;
+  call->ml_off = pl.ml_off;
+  call->ws_bytes = pl.ws_bytes;
+  call->act_dtype = desc->act_dtype;
+  call->cache_dtype = desc->cache_dtype;
+  return PA_OK;
+}
+
+pa_status decode_launch(const DecodeCall& call, void* workspace, void* stream) {
+  AttnParams p = call.p;
+  unsigned char* ws = static_cast<unsigned char*>(workspace);
+  p.ws_cum = reinterpret_cast<int64_t*>(ws + call.cum_off);
+  p.ws_acc = reinterpret_cast<float*>(ws + call.acc_off);
+  p.ws_ml = reinterpret_cast<float*>(ws + call.ml_off);
+  return from_hip(launch_decode(p, call.act_dtype, call.cache_dtype,
+                                static_cast<hipStream_t>(stream)));
+}
+
+}  // namespace pa

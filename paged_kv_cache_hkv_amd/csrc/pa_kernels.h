@@ -123,4 +123,13 @@ hipError_t launch_copy_blocks(const CopyBlocksParams& p, hipStream_t stream);
 hipError_t launch_decode(const AttnParams& p, int act_dtype, int cache_dtype, hipStream_t stream);
 hipError_t launch_prefill(const AttnParams& p, int act_dtype, int cache_dtype, hipStream_t stream);
 
+// A validated pa_decode call: its kernel parameters (workspace pointers not
+// yet set), where each workspace part sits, and the bytes the call needs.
+struct DecodeCall {
+  AttnParams p;
+  size_t cum_off, acc_off, ml_off, ws_bytes;
+  int act_dtype, cache_dtype;
+  bool empty;   // no requests: nothing to launch
+};
+
 }  // namespace pa

@@ -130,6 +130,24 @@ def test_decode_checks_and_workspace_query():
     assert bad_range == B.PA_ERR_INVALID_ARG
 
 
+def test_decode_noalloc_checks():
+    """The no-allocation decode validates like pa_decode and refuses, before any
+    device work, a call whose workspace would not fit the library's array."""
+    lib = B.load()
+    d = _desc()
+    call = lambda desc, q=FAKE, begin=0, end=256, stride=8192: lib.pa_decode_noalloc(
+        ctypes.byref(desc), begin, end, q, stride, FAKE, FAKE, FAKE, 513, FAKE, FAKE, 1000, 8193,
+        FAKE, stride, None)
+    assert call(d, q=None) == B.PA_ERR_INVALID_ARG
+    assert call(d, begin=5, end=2) == B.PA_ERR_INVALID_ARG
+    assert call(d, begin=7, end=7) == B.PA_OK                      # empty range: nothing to do
+    # 2^20 workers x 2 slots x G = 4 x (128 + 2) floats: far beyond the 32 MiB array
+    huge = _desc(decode_workers=1 << 20)
+    assert B.pa_decode_workspace_size(huge, 256, 8193, 513) > (32 << 20)
+    assert call(huge) == B.PA_ERR_WORKSPACE_TOO_SMALL
+    assert call(_desc(num_q_heads=64, num_kv_heads=1)) == B.PA_ERR_UNSUPPORTED   # G > 32
+
+
 def test_prefill_checks():
     lib = B.load()
     d = _desc()
