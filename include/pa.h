@@ -277,10 +277,12 @@ pa_status pa_copy_blocks(const pa_attn_desc* desc,
  * max_seq_len (host scalar) must be >= every seq_len of the range; keys past
  * it are ignored; above 2^30 the call returns PA_ERR_UNSUPPORTED.  Accumulation is float32; out is act_dtype, rounded to
  * nearest even.  The (request, K/V head, 16-token block) stream of the range
- * is cut into desc->decode_workers equal contiguous shares, one per wave;
- * a K/V head cut between waves leaves float32 partial results (running max,
- * sum, weighted sum) in `workspace` that a second kernel merges in a fixed
- * order (deterministic output for a given worker count).
+ * is cut into desc->decode_workers equal contiguous shares, one per wave,
+ * and consecutive waves form workgroups; a K/V head cut between waves leaves
+ * float32 partial results (running max, sum, weighted sum) that the
+ * workgroup merges, and a head cut between workgroups leaves one partial
+ * per workgroup in `workspace` that a second kernel merges (fixed orders:
+ * the output is deterministic for a given worker count).
  *
  * Workspace: 16-byte aligned device memory of at least
  * pa_decode_workspace_size() bytes for the same desc and request count (else
@@ -308,9 +310,10 @@ pa_status pa_decode(const pa_attn_desc* desc, int32_t req_begin, int32_t req_end
  * and checks as pa_decode, minus the workspace pair.
  *
  * It uses a device array that the library holds, one per GPU, of
- * PA_DECODE_NOALLOC_SCRATCH_BYTES bytes, which lives until the process ends;
- * its address is looked up on the first call on each device.  The call
- * allocates and frees nothing.  A call that would need more workspace than
+ * PA_DECODE_NOALLOC_SCRATCH_BYTES bytes (64 MiB: enough for head_dim <= 128
+ * and G <= 32 at the default worker count of a 256-compute-unit device),
+ * which lives until the process ends; its address is looked up on the first
+ * call on each device.  The call allocates and frees nothing.  A call that would need more workspace than
  * the array holds (pa_decode_workspace_size larger than
  * PA_DECODE_NOALLOC_SCRATCH_BYTES) returns PA_ERR_WORKSPACE_TOO_SMALL and
  * enqueues nothing.  Every call on one GPU shares that GPU's array: calls
@@ -318,7 +321,7 @@ pa_status pa_decode(const pa_attn_desc* desc, int32_t req_begin, int32_t req_end
  * race and give undefined results; serialise them.  PA_ERR_HIP if the
  * array's address cannot be obtained on the current device.
  */
-#define PA_DECODE_NOALLOC_SCRATCH_BYTES ((size_t)32 << 20)
+#define PA_DECODE_NOALLOC_SCRATCH_BYTES ((size_t)64 << 20)
 
 pa_status pa_decode_noalloc(const pa_attn_desc* desc, int32_t req_begin, int32_t req_end,
                             const void* q, int64_t q_row_stride,
@@ -331,10 +334,12 @@ pa_status pa_decode_noalloc(const pa_attn_desc* desc, int32_t req_begin, int32_t
 /*
  * pa_decode_workspace_size -- bytes of workspace pa_decode needs for
  * num_reqs = req_end - req_begin requests of this desc (a prefix sum over the
- * requests, and two partial slots per worker of G float32 running maxima,
- * sums and head_dim weighted sums).  max_seq_len and max_blocks_per_req are
- * validated but do not change the size.  0 when num_reqs is 0.  Host only;
- * launches nothing (it may query the current device's compute-unit count).
+ * requests, two partial slots per workgroup of G float32 running maxima, sums
+ * and head_dim weighted sums, and one slot per worker of G * head_dim
+ * weighted sums).  max_seq_len and
+ * max_blocks_per_req are validated but do not change the size.  0 when
+ * num_reqs is 0.  Host only; launches nothing (it may query the current
+ * device's compute-unit count).
  */
 pa_status pa_decode_workspace_size(const pa_attn_desc* desc, int32_t num_reqs,
                                    int32_t max_seq_len, int32_t max_blocks_per_req,

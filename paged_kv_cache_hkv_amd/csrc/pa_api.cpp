@@ -15,7 +15,6 @@
 namespace {
 
 constexpr int kBlockSize = 16;
-constexpr int kMaxDecodeWorkers = 1 << 20;
 constexpr int kMaxGridYZ = 65535;
 // longest sequence the attention calls take: positions stay below 2^30, so a
 // sliding window of 2^30 keys or more leaves every key visible and is
@@ -54,10 +53,15 @@ pa_status check_desc(const pa_attn_desc* d) {
       return PA_ERR_INVALID_ARG;
     }
   }
-  if (d->decode_workers < 0 || d->decode_workers > kMaxDecodeWorkers) return PA_ERR_INVALID_ARG;
+  if (d->decode_workers < 0 || d->decode_workers > pa::kMaxDecodeWorkers) return PA_ERR_INVALID_ARG;
   if (d->sliding_window < 0) return PA_ERR_INVALID_ARG;
   if ((reinterpret_cast<uintptr_t>(d->alibi_slopes) & 3u) != 0) return PA_ERR_INVALID_ARG;
   return PA_OK;
+}
+
+// the kernels' cache-format code of a pa_dtype
+int cache_kind(int cache_dtype) {
+  return cache_dtype == PA_FP8_E4M3 ? pa::kFP8 : cache_dtype == PA_INT8 ? pa::kINT8 : pa::kF16;
 }
 
 // Decode workers: waves that each stream one contiguous share of the
@@ -66,9 +70,7 @@ pa_status check_desc(const pa_attn_desc* d) {
 // resident for the whole launch) unless the descriptor fixes the count.
 int decode_workers(const pa_attn_desc* d) {
   if (d->decode_workers > 0) return d->decode_workers;
-  const int per_cu = pa::decode_waves_per_cu(d->cache_dtype == PA_FP8_E4M3 ? pa::kFP8
-                                             : d->cache_dtype == PA_INT8   ? pa::kINT8
-                                                                           : pa::kF16);
+  const int per_cu = pa::decode_waves_per_cu(cache_kind(d->cache_dtype));
   int dev = 0, cus = 0;
   if (hipGetDevice(&dev) != hipSuccess ||
       hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
@@ -79,23 +81,27 @@ int decode_workers(const pa_attn_desc* d) {
 }
 
 struct DecodePlan {
-  int workers;
-  size_t cum_off, acc_off, ml_off, ws_bytes;
+  int workers, wg_waves;
+  size_t cum_off, acc_off, ml_off, facc_off, ws_bytes;
 };
 
 size_t round_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
 
-// Workspace: the stream prefix (int64, num_reqs + 1) and two float32 partial
-// slots per worker of G * (head_dim + 2) values.
+// Workspace: the stream prefix (int64, num_reqs + 1); two float32 partial
+// slots per workgroup of G * (head_dim + 2) values (weighted sums, then
+// running maxima and sums) and one per worker of G * head_dim weighted sums.
 DecodePlan plan_decode(const pa_attn_desc* d, int num_reqs) {
   DecodePlan pl{};
   pl.workers = decode_workers(d);
+  pl.wg_waves = pa::decode_waves_per_cu(cache_kind(d->cache_dtype));
   const size_t G = (size_t)(d->num_q_heads / d->num_kv_heads);
-  const size_t slots = (size_t)pl.workers * 2;
+  const size_t wg_slots = (size_t)((pl.workers + pl.wg_waves - 1) / pl.wg_waves) * 2;
+  const size_t w_slots = (size_t)pl.workers;
   pl.cum_off = 0;
   pl.acc_off = round_up((size_t)(num_reqs + 1) * sizeof(int64_t), 256);
-  pl.ml_off = pl.acc_off + round_up(slots * G * d->head_dim * sizeof(float), 256);
-  pl.ws_bytes = pl.ml_off + round_up(slots * G * 2 * sizeof(float), 256);
+  pl.ml_off = pl.acc_off + round_up(wg_slots * G * d->head_dim * sizeof(float), 256);
+  pl.facc_off = pl.ml_off + round_up(wg_slots * G * 2 * sizeof(float), 256);
+  pl.ws_bytes = pl.facc_off + round_up(w_slots * G * d->head_dim * sizeof(float), 256);
   return pl;
 }
 
@@ -465,9 +471,11 @@ pa_status decode_prepare(const pa_attn_desc* desc, int32_t req_begin, int32_t re
                         out_row_stride);
   call->p.max_seq_len = max_seq_len;
   call->p.num_workers = pl.workers;
+  call->p.wg_waves = pl.wg_waves;
   call->cum_off = pl.cum_off;
   call->acc_off = pl.acc_off;
   call->ml_off = pl.ml_off;
+  call->facc_off = pl.facc_off;
   call->ws_bytes = pl.ws_bytes;
   call->act_dtype = desc->act_dtype;
   call->cache_dtype = desc->cache_dtype;
@@ -480,6 +488,7 @@ pa_status decode_launch(const DecodeCall& call, void* workspace, void* stream) {
   p.ws_cum = reinterpret_cast<int64_t*>(ws + call.cum_off);
   p.ws_acc = reinterpret_cast<float*>(ws + call.acc_off);
   p.ws_ml = reinterpret_cast<float*>(ws + call.ml_off);
+  p.ws_facc = reinterpret_cast<float*>(ws + call.facc_off);
   return from_hip(launch_decode(p, call.act_dtype, call.cache_dtype,
                                 static_cast<hipStream_t>(stream)));
 }

@@ -22,9 +22,11 @@
 // covers a few (request, K/V head) segments.  A segment that is a whole
 // (request, K/V head) is finished in place and its output rows written
 // directly; a segment cut by a range boundary leaves a float32 partial
-// (running max, sum, weighted sum) in the worker's slot 0 (its first segment)
-// or slot 1 (its last), and the reduce kernel merges the partials of each cut
-// head in worker order (deterministic, no atomics).
+// (running max, sum, weighted sum).  Consecutive workers form a workgroup
+// (one per compute unit), which merges in LDS, in worker order, every head
+// cut only between its own workers; a head cut between workgroups leaves one
+// partial per workgroup, merged in workgroup order by the reduce kernel
+// (deterministic, no atomics).
 //
 // Streaming.  Each wave owns a ring of S LDS stages, one block (K and V rows
 // of one head) each, and a query area for one segment's G query rows, copied
@@ -238,7 +240,10 @@ __global__ __launch_bounds__(64 * WV) void decode_kernel(AttnParams p) {
   const int c16 = lane & 15;
   const int W = p.num_workers;
   const int worker = blockIdx.x * WV + wave;
-  if (worker >= W) return;
+  // waves past the worker count (a last workgroup of fewer workers) and
+  // workers with empty ranges stream nothing but still take part in the
+  // workgroup's merge of partials below, so no wave leaves early
+  const bool in_range = worker < W;
   const int Rn = p.num_reqs;
   const int G = p.group;
   const int Hkv = p.num_kv_heads;
@@ -249,14 +254,14 @@ __global__ __launch_bounds__(64 * WV) void decode_kernel(AttnParams p) {
     const int64_t v = (c + lane < Rn) ? (int64_t)Hkv * stream_blocks(p, c + lane, false) : 0;
     T += readlane64(wave_scan(v), 63);
   }
-  const int64_t g0 = range_begin(worker, T, W);
+  const int64_t g0 = in_range ? range_begin(worker, T, W) : T;
   // units of this worker: the host keeps every share below 2^31
-  const int n = (int)(range_begin(worker + 1, T, W) - g0);
+  const int n = in_range ? (int)(range_begin(worker + 1, T, W) - g0) : 0;
   Cursor cur{0, 0, 0, 0, 0, 0, 0, 0, nullptr};
-  {
+  bool found = false;
+  if (in_range) {
     // worker 0 also publishes the exclusive prefix for the reduce kernel
     int64_t run = 0;
-    bool found = false;
     for (int c = 0; c < Rn; c += 64) {
       const int64_t v = (c + lane < Rn) ? (int64_t)Hkv * stream_blocks(p, c + lane, false) : 0;
       const int64_t incl = wave_scan(v);
@@ -276,8 +281,48 @@ __global__ __launch_bounds__(64 * WV) void decode_kernel(AttnParams p) {
       run += readlane64(incl, 63);
     }
     if (worker == 0 && lane == 0) p.ws_cum[Rn] = T;
-    if (!found || n <= 0) return;
   }
+  const bool active = found && n > 0;
+
+  // partial state of the worker's last head when a range boundary cuts it
+  // (kept for the workgroup merge), and whether its first head left one
+  bool has_l = false, has_f = false;
+  int64_t l_first = 0, l_end = 0, f_first = 0, f_end = 0;   // stream units of those heads
+  int l_kvh = 0, l_qrow = 0, f_kvh = 0, f_qrow = 0;
+  float m_used[HT], l_run[HT];
+  f32x4 acc[HT][NM];
+  float f_m[HT], f_l[HT];   // the first head's running max and sum, when it left a partial
+  // a partial -- weighted sums [G][D], then running max and sum [G][2] --
+  // from the lanes' accumulator layout
+  auto store_partial = [&](float* pacc, float* pml, const f32x4 (&a)[HT][NM], const float (&mu)[HT],
+                           const float (&lr)[HT]) __attribute__((always_inline)) {
+#pragma unroll
+    for (int ht = 0; ht < HT; ++ht) {
+      float lt = lr[ht];
+      lt += shfl_xor(lt, 16);
+      lt += shfl_xor(lt, 32);
+      const int hig = ht * 16 + c16;
+      if (hig < G) {
+        float* wa = pacc + hig * D;
+        if constexpr (KVB == 2) {
+#pragma unroll
+          for (int m = 0; m < NM; ++m) *reinterpret_cast<f32x4*>(wa + 16 * m + 4 * q4) = a[ht][m];
+        } else {
+#pragma unroll
+          for (int k = 0; k < 4; ++k)
+#pragma unroll
+            for (int m = 0; m < NM; m += 4)
+              *reinterpret_cast<f32x4*>(wa + VE * (4 * q4 + k) + m) =
+                  f32x4{a[ht][m][k], a[ht][m + 1][k], a[ht][m + 2][k], a[ht][m + 3][k]};
+        }
+        if (q4 == 0 && pml != nullptr) {
+          pml[2 * hig] = mu[ht];
+          pml[2 * hig + 1] = lt;
+        }
+      }
+    }
+  };
+  if (active) {
 
   const int64_t tok_stride = (int64_t)Hkv * D * KVB;     // bytes between slots
   // bytes between blocks (below 2^32, checked on the host)
@@ -367,9 +412,7 @@ __global__ __launch_bounds__(64 * WV) void decode_kernel(AttnParams p) {
 
   const float c2 = p.scale_log2;
   vec8 qop[HT][KS];
-  float m_used[HT], l_run[HT];
   float slope2[HT];     // ALiBi slope of this lane's head, in log2 units
-  f32x4 acc[HT][NM];
   int seg = 0;          // segments this worker has finished
   int seg_b0 = 0;       // first block of the current segment
 
@@ -521,18 +564,20 @@ __global__ __launch_bounds__(64 * WV) void decode_kernel(AttnParams p) {
       }
     }
 
-    // ---- segment end: output rows, or a partial for the reduce kernel ----
+    // ---- segment end: output rows of a whole head; a head cut at the
+    // range's start that ends inside it leaves its partial in the worker's
+    // slot; a head cut at the range's end keeps its state in registers for
+    // the workgroup merge ----
     if (cur.b == cur.nb - 1 || i == n - 1) {
       const bool whole = seg_b0 == 0 && cur.b == cur.nb - 1;
-      const int64_t slot = (int64_t)worker * 2 + (seg == 0 ? 0 : 1);
+      if (whole) {
 #pragma unroll
-      for (int ht = 0; ht < HT; ++ht) {
-        float lt = l_run[ht];
-        lt += shfl_xor(lt, 16);
-        lt += shfl_xor(lt, 32);
-        const int hig = ht * 16 + c16;
-        if (hig < G) {
-          if (whole) {
+        for (int ht = 0; ht < HT; ++ht) {
+          float lt = l_run[ht];
+          lt += shfl_xor(lt, 16);
+          lt += shfl_xor(lt, 32);
+          const int hig = ht * 16 + c16;
+          if (hig < G) {
             const float inv = (lt > 0.f) ? p.v_scale / lt : 0.f;
             unsigned short* orow = static_cast<unsigned short*>(p.out) +
                                    (int64_t)cur.q_row * p.out_row_stride +
@@ -561,41 +606,215 @@ __global__ __launch_bounds__(64 * WV) void decode_kernel(AttnParams p) {
                 }
               }
             }
-          } else {
-            float* wa = p.ws_acc + (slot * G + hig) * D;
-            if constexpr (KVB == 2) {
-#pragma unroll
-              for (int m = 0; m < NM; ++m) *reinterpret_cast<f32x4*>(wa + 16 * m + 4 * q4) = acc[ht][m];
-            } else {
-#pragma unroll
-              for (int k = 0; k < 4; ++k)
-#pragma unroll
-                for (int m = 0; m < NM; m += 4)
-                  *reinterpret_cast<f32x4*>(wa + VE * (4 * q4 + k) + m) =
-                      f32x4{acc[ht][m][k], acc[ht][m + 1][k], acc[ht][m + 2][k], acc[ht][m + 3][k]};
-            }
-            if (q4 == 0) {
-              float* ml = p.ws_ml + (slot * G + hig) * 2;
-              ml[0] = m_used[ht];
-              ml[1] = lt;
-            }
           }
         }
+      } else if (i < n - 1) {
+        // the worker's first head, begun before its range: its weighted
+        // sums wait in the worker's slot for the workgroup merge, its
+        // running max and sum in registers
+        store_partial(p.ws_facc + (int64_t)worker * G * D, nullptr, acc, m_used, l_run);
+#pragma unroll
+        for (int ht = 0; ht < HT; ++ht) {
+          float lt = l_run[ht];
+          lt += shfl_xor(lt, 16);
+          lt += shfl_xor(lt, 32);
+          f_m[ht] = m_used[ht];
+          f_l[ht] = lt;
+        }
+        has_f = true;
+        f_first = g0 + i - cur.b;
+        f_end = g0 + i + 1;
+        f_kvh = cur.kvh;
+        f_qrow = cur.q_row;
+      } else {
+        has_l = true;
+        l_first = g0 + i - cur.b;
+        l_end = l_first + cur.nb;
+        l_kvh = cur.kvh;
+        l_qrow = cur.q_row;
       }
       ++seg;
     }
     advance(p, cur);
     st_i = (st_i == S - 1) ? 0 : st_i + 1;
   }
+  }   // active
+
+  // ---- workgroup merge.  The workgroup's range is the union of its
+  // workers' ranges.  Each worker with a cut last head stages that partial in
+  // its own LDS region (its ring has drained), and the running max and sum of
+  // a first head it left in its slot.  After a barrier the whole workgroup
+  // merges every head cut between its workers, in worker order: a head that
+  // begins and ends inside the workgroup's range is finished here, and the at
+  // most two heads it shares with neighbouring workgroups (the one holding
+  // its first unit -> slot 0, the one holding its last -> slot 1) leave one
+  // partial each for the reduce kernel.  All global loads of the merge (the
+  // first-head weighted sums) are issued before any of its stores, so no wait
+  // for them covers a store. ----
+  // a wave's region: the last-head partial ([G][D] sums, [G][2] max and
+  // sum), the first head's [G][2] max and sum, and a record of its heads
+  struct MergeInfo {
+    int64_t l_first, l_end, f_first, f_end;
+    int flags, l_kvh, l_qrow, f_kvh, f_qrow;
+  };
+  constexpr int kFmlOff = 16 * HT * (D + 2) * 4;
+  constexpr int kInfoOff = kWaveBytes - 64;
+  static_assert(sizeof(MergeInfo) <= 64, "merge record");
+  static_assert(kFmlOff + 16 * HT * 2 * 4 <= kInfoOff, "partials must fit a wave's LDS region");
+  constexpr int kL = 1, kF = 2, kBusy = 4;
+  auto info = [&](int w) __attribute__((always_inline)) {
+    return reinterpret_cast<MergeInfo*>(lds + w * kWaveBytes + kInfoOff);
+  };
+  auto lacc = [&](int w) __attribute__((always_inline)) {
+    return reinterpret_cast<float*>(lds + w * kWaveBytes);
+  };
+  auto lml = [&](int w) __attribute__((always_inline)) { return lacc(w) + G * D; };
+  auto fml = [&](int w) __attribute__((always_inline)) {
+    return reinterpret_cast<float*>(lds + w * kWaveBytes + kFmlOff);
+  };
+  if (has_l) store_partial(lacc(wave), lml(wave), acc, m_used, l_run);
+  if (has_f) {
+#pragma unroll
+    for (int ht = 0; ht < HT; ++ht) {
+      const int hig = ht * 16 + c16;
+      if (hig < G && q4 == 0) {
+        fml(wave)[2 * hig] = f_m[ht];
+        fml(wave)[2 * hig + 1] = f_l[ht];
+      }
+    }
+  }
+  if (lane == 0) {
+    MergeInfo* mi = info(wave);
+    mi->flags = (active ? kBusy : 0) | (has_l ? kL : 0) | (has_f ? kF : 0);
+    mi->l_first = l_first;
+    mi->l_end = l_end;
+    mi->f_first = f_first;
+    mi->f_end = f_end;
+    mi->l_kvh = l_kvh;
+    mi->l_qrow = l_qrow;
+    mi->f_kvh = f_kvh;
+    mi->f_qrow = f_qrow;
+  }
+  wait_vmcnt<0>();   // the first-head sums (and this worker's output rows) are stored
+  __syncthreads();
+  const int64_t wg0 = (int64_t)blockIdx.x * WV;
+  const int64_t wg_begin = range_begin(wg0, T, W);
+  const int64_t wg_end = range_begin(min(wg0 + WV, (int64_t)W), T, W);
+  const int tid = threadIdx.x;
+  constexpr int NT = 64 * WV;
+  // each thread takes groups of 4 consecutive elements (one head each)
+  constexpr int kGPT = (16 * HT * D / 4 + NT - 1) / NT;   // element groups per thread, at most
+  // every first-head partial's sums of this thread's groups, loaded first
+  f32x4 fa[WV][kGPT];
+#pragma unroll
+  for (int v = 0; v < WV; ++v) {
+    const bool fv = (info(v)->flags & kF) != 0;   // LDS broadcast reads, issued together
+    const float* src = p.ws_facc + (wg0 + v) * G * D;
+#pragma unroll
+    for (int q = 0; q < kGPT; ++q) {
+      const int e = 4 * (tid + q * NT);
+      fa[v][q] = (fv && e < G * D) ? *reinterpret_cast<const f32x4*>(src + e) : f32x4{0.f, 0.f, 0.f, 0.f};
+    }
+  }
+  float* const slot_acc = p.ws_acc + (int64_t)blockIdx.x * 2 * G * D;
+  float* const slot_ml = p.ws_ml + (int64_t)blockIdx.x * 2 * G * 2;
+  // one run: the last-head partials of `lmask` and the first-head partial
+  // of worker fw (or none), merged in worker order
+  auto merge_run = [&](unsigned lmask, int fw, bool complete, int slot, int kvh, int q_row)
+      __attribute__((always_inline)) {
+#pragma unroll
+    for (int q = 0; q < kGPT; ++q) {
+      const int e = 4 * (tid + q * NT);
+      if (e >= G * D) break;
+      const int h = e / D;
+      float mx = -INFINITY;
+#pragma unroll
+      for (int v = 0; v < WV; ++v)
+        if ((lmask >> v) & 1u) mx = fmaxf(mx, lml(v)[2 * h]);
+      if (fw >= 0) mx = fmaxf(mx, fml(fw)[2 * h]);
+      const float Ms = (mx == -INFINITY) ? 0.f : mx;
+      float L = 0.f;
+      f32x4 A{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int v = 0; v < WV; ++v) {
+        if ((lmask >> v) & 1u) {
+          const float wgt = fast_exp2(lml(v)[2 * h] - Ms);
+          L += wgt * lml(v)[2 * h + 1];
+          A += wgt * *reinterpret_cast<const f32x4*>(lacc(v) + e);
+        }
+      }
+      if (fw >= 0) {
+        const float wgt = fast_exp2(fml(fw)[2 * h] - Ms);
+        L += wgt * fml(fw)[2 * h + 1];
+        f32x4 fv{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int v = 0; v < WV; ++v) fv = (v == fw) ? fa[v][q] : fv;
+        A += wgt * fv;
+      }
+      if (complete) {
+        const float inv = (L > 0.f) ? p.v_scale / L : 0.f;
+        unsigned short* orow = static_cast<unsigned short*>(p.out) + (int64_t)q_row * p.out_row_stride +
+                               (int64_t)kvh * G * D + e;
+        st8(orow, u32x2{pack2<CT>(A[0] * inv, A[1] * inv), pack2<CT>(A[2] * inv, A[3] * inv)});
+      } else {
+        *reinterpret_cast<f32x4*>(slot_acc + slot * G * D + e) = A;
+        if (e % D == 0) {
+          slot_ml[slot * G * 2 + 2 * h] = mx;
+          slot_ml[slot * G * 2 + 2 * h + 1] = L;
+        }
+      }
+    }
+  };
+  // the workers' records, lane v of every wave holding worker v's, read
+  // back uniformly with lane reads (no LDS round trip per step of the walk)
+  const MergeInfo* mi_l = info(lane < WV ? lane : 0);
+  const int r_flags = lane < WV ? mi_l->flags : 0;
+  const int64_t r_lfirst = mi_l->l_first, r_lend = mi_l->l_end, r_ffirst = mi_l->f_first;
+  const int r_lkvh = mi_l->l_kvh, r_lqrow = mi_l->l_qrow, r_fkvh = mi_l->f_kvh, r_fqrow = mi_l->f_qrow;
+  auto flags_of = [&](int v) { return __builtin_amdgcn_readlane(r_flags, v); };
+  auto lfirst_of = [&](int v) { return readlane64(r_lfirst, v); };
+  auto ffirst_of = [&](int v) { return readlane64(r_ffirst, v); };
+  for (int w = 0; w < WV; ++w) {   // uniform
+    const int fl = flags_of(w);
+    if (!(fl & (kL | kF))) continue;
+    int u = w - 1;                          // previous worker that streamed anything
+    while (u >= 0 && !(flags_of(u) & kBusy)) --u;
+    if ((fl & kF) && !(u >= 0 && (flags_of(u) & kL) && lfirst_of(u) == ffirst_of(w))) {
+      // a first head begun before the workgroup's range: its only piece
+      // here, and it holds the range's first unit (slot 0)
+      merge_run(0u, w, false, 0, __builtin_amdgcn_readlane(r_fkvh, w),
+                __builtin_amdgcn_readlane(r_fqrow, w));
+    }
+    if (!(fl & kL)) continue;
+    const int64_t X = lfirst_of(w);
+    if (u >= 0 && (flags_of(u) & kL) && lfirst_of(u) == X) continue;   // merged with an earlier run
+    // the run of workers holding head X: this one, workers whose whole range
+    // lies inside it, and possibly the one where it ends (its first head)
+    unsigned lmask = 1u << w;
+    int fw = -1;
+    for (int v = w + 1; v < WV; ++v) {
+      const int fv = flags_of(v);
+      if (!(fv & kBusy)) continue;
+      if ((fv & kL) && lfirst_of(v) == X) {
+        lmask |= 1u << v;
+        continue;
+      }
+      if ((fv & kF) && ffirst_of(v) == X) fw = v;
+      break;
+    }
+    const int64_t Xend = readlane64(r_lend, w);
+    merge_run(lmask, fw, X >= wg_begin && Xend <= wg_end, X <= wg_begin ? 0 : 1,
+              __builtin_amdgcn_readlane(r_lkvh, w), __builtin_amdgcn_readlane(r_lqrow, w));
+  }
 }
 
 // Merge of the partials of one (request, query head) whose K/V head was cut
-// between workers w_a .. w_b: one wave.  Lanes take partials (64 at a time)
-// for the global max and the weighted sum of the row sums; then each lane
-// accumulates its D/64 output columns over the partials in worker order with
-// the weights broadcast from the lane that owns them.  Fixed order, no
-// atomics: deterministic.  A head finished by one worker was written by the
-// main kernel and is skipped here.
+// between workgroups g_a .. g_b (a head cut only between workers of one
+// workgroup was finished by that workgroup): one wave.  Lanes take partials
+// (64 at a time) for the global max and the weighted sum of the row sums;
+// then each lane accumulates its D/64 output columns over the partials in
+// workgroup order with the weights broadcast from the lane that owns them.
+// Fixed order, no atomics: deterministic.
 template <int D, typename CT>
 __global__ __launch_bounds__(64) void decode_reduce_kernel(AttnParams p) {
   constexpr int DPL = D / 64;   // output columns per lane
@@ -609,22 +828,23 @@ __global__ __launch_bounds__(64) void decode_reduce_kernel(AttnParams p) {
   const int kvh = qh / G;
   const int hig = qh % G;
   const int64_t W = p.num_workers;
+  const int64_t WV = p.wg_waves;
   const int64_t T = p.ws_cum[p.num_reqs];
   const int64_t a = p.ws_cum[rr] + (int64_t)kvh * nb;
   const int64_t b = a + nb;
-  const int64_t wa = ((a + 1) * W - 1) / T;   // worker holding unit a
-  const int64_t wb = (b * W - 1) / T;         // worker holding unit b-1
-  if (wa == wb) return;
-  const int cnt = (int)(wb - wa + 1);
-  // partial of the i-th worker of the cut: slot 1 if that worker's range
-  // began before this head (the head is its last segment), else slot 0;
-  // a worker whose range is empty holds none
+  const int64_t ga = (((a + 1) * W - 1) / T) / WV;   // workgroup holding unit a
+  const int64_t gb = ((b * W - 1) / T) / WV;         // workgroup holding unit b-1
+  if (ga == gb) return;
+  const int cnt = (int)(gb - ga + 1);
+  // partial of the i-th workgroup of the cut: slot 1 for g_a if its range
+  // began before this head (the head holds its last unit), else slot 0;
+  // when T >= W every workgroup range holds units, otherwise a workgroup
+  // whose range is empty holds none
+  const int sl_a = range_begin(ga * WV, T, W) < a ? 1 : 0;
   auto part_index = [&](int i, bool& valid) -> int64_t {
-    const int64_t w = wa + i;
-    const int64_t beg = range_begin(w, T, W);
-    valid = beg < range_begin(w + 1, T, W);
-    const int slot = (i == 0 && beg < a) ? 1 : 0;
-    return (w * 2 + slot) * G + hig;
+    const int64_t g = ga + i;
+    valid = T >= W || range_begin(g * WV, T, W) < range_begin(min(g * WV + WV, W), T, W);
+    return (g * 2 + (i == 0 ? sl_a : 0)) * G + hig;
   };
 
   float mloc = -INFINITY;
@@ -642,7 +862,7 @@ __global__ __launch_bounds__(64) void decode_reduce_kernel(AttnParams p) {
 #pragma unroll
   for (int e = 0; e < DPL; ++e) o[e] = 0.f;
   bool ok0;
-  const int64_t ix0 = part_index(0, ok0);   // worker w_a always holds a partial
+  const int64_t ix0 = part_index(0, ok0);   // workgroup g_a always holds a partial
   for (int g = 0; g < cnt; g += 64) {
     const int i = g + lane;
     bool ok = false;
@@ -663,9 +883,9 @@ __global__ __launch_bounds__(64) void decode_reduce_kernel(AttnParams p) {
         const int j = min(j0 + u, m - 1);
         wj[u] = (j0 + u < m) ? __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, w), j))
                              : 0.f;
-        const float* a = p.ws_acc + readlane64(ix, j) * D + lane;
+        const float* ap = p.ws_acc + readlane64(ix, j) * D + lane;
 #pragma unroll
-        for (int e = 0; e < DPL; ++e) v[u][e] = a[64 * e];
+        for (int e = 0; e < DPL; ++e) v[u][e] = ap[64 * e];
       }
 #pragma unroll
       for (int u = 0; u < RB; ++u)

@@ -97,11 +97,20 @@ struct AttnParams {
   int32_t max_seq_len;
   int32_t max_query_len;
   // decode: the flattened (request, K/V head, block) key stream is cut into
-  // num_workers equal contiguous ranges, one per wave
+  // num_workers equal contiguous ranges, one per wave; wg_waves consecutive
+  // workers form one workgroup, whose range is the union of theirs
   int32_t num_workers;
-  int64_t* ws_cum;    // [num_reqs + 1] first stream block of each request; [num_reqs] = total
-  float* ws_acc;      // [num_workers, 2, G, D] partial weighted sums of split K/V heads
-  float* ws_ml;       // [num_workers, 2, G, 2] their running max (log2 units) and sum
+  int32_t wg_waves;
+  int64_t* ws_cum;    // [num_reqs + 1] first stream unit of each request; [num_reqs] = total
+  // per workgroup, two partials of K/V heads the workgroup shares with its
+  // neighbours (slot 0: the head holding the workgroup's first unit, slot 1:
+  // its last head): weighted sums [num_wg, 2, G, D], running max (log2
+  // units) and sum [num_wg, 2, G, 2]
+  float* ws_acc;
+  float* ws_ml;
+  // per worker, the weighted sums of its first head when that head began
+  // before its range and ended inside it (merged inside the workgroup)
+  float* ws_facc;     // [num_workers, G, D]
 };
 
 // Decode waves per workgroup (= per compute unit: one resident workgroup of
@@ -110,6 +119,9 @@ struct AttnParams {
 constexpr int decode_waves_per_cu(int cache_dtype) {
   return (cache_dtype == kFP8 || cache_dtype == kINT8) ? 8 : 4;
 }
+
+// Most decode workers a call may use.
+constexpr int kMaxDecodeWorkers = 1 << 20;
 
 hipError_t launch_metadata(const MetadataParams& p, hipStream_t stream);
 hipError_t launch_cache_write(const CacheWriteParams& p, int act_dtype, int cache_dtype,
@@ -127,7 +139,7 @@ hipError_t launch_prefill(const AttnParams& p, int act_dtype, int cache_dtype, h
 // yet set), where each workspace part sits, and the bytes the call needs.
 struct DecodeCall {
   AttnParams p;
-  size_t cum_off, acc_off, ml_off, ws_bytes;
+  size_t cum_off, acc_off, ml_off, facc_off, ws_bytes;
   int act_dtype, cache_dtype;
   bool empty;   // no requests: nothing to launch
 };

@@ -109,11 +109,14 @@ def test_decode_checks_and_workspace_query():
     d = _desc()
     # size query is host-only
     assert B.pa_decode_workspace_size(d, 256, 8193, 513) > 0
-    # fixed worker count: prefix (int64, R+1) + 2 slots/worker of G*(D+2) floats, 256-aligned parts
+    # fixed worker count: prefix (int64, R+1), 2 slots per workgroup (4 workers each for a
+    # 16-bit cache) of G*(D+2) floats, 1 per worker of G*D floats, in 256-aligned parts
     d8 = _desc(decode_workers=8)
     rup = lambda x: (x + 255) // 256 * 256
     G, D = 4, 128
-    assert B.pa_decode_workspace_size(d8, 4, 100, 8) == rup(5 * 8) + rup(16 * G * D * 4) + rup(16 * G * 2 * 4)
+    wg_slots, w_slots = 2 * 2, 8
+    assert B.pa_decode_workspace_size(d8, 4, 100, 8) == (
+        rup(5 * 8) + rup(wg_slots * G * D * 4) + rup(wg_slots * G * 2 * 4) + rup(w_slots * G * D * 4))
     assert B.pa_decode_workspace_size(d8, 0, 100, 8) == 0
     big = _desc(num_q_heads=64, num_kv_heads=1)
     with pytest.raises(B.PaError) as e:
@@ -141,9 +144,9 @@ def test_decode_noalloc_checks():
     assert call(d, q=None) == B.PA_ERR_INVALID_ARG
     assert call(d, begin=5, end=2) == B.PA_ERR_INVALID_ARG
     assert call(d, begin=7, end=7) == B.PA_OK                      # empty range: nothing to do
-    # 2^20 workers x 2 slots x G = 4 x (128 + 2) floats: far beyond the 32 MiB array
+    # 2^20 workers' slots of G = 4 x (128 + 2) floats: far beyond the 64 MiB array
     huge = _desc(decode_workers=1 << 20)
-    assert B.pa_decode_workspace_size(huge, 256, 8193, 513) > (32 << 20)
+    assert B.pa_decode_workspace_size(huge, 256, 8193, 513) > (64 << 20)
     assert call(huge) == B.PA_ERR_WORKSPACE_TOO_SMALL
     assert call(_desc(num_q_heads=64, num_kv_heads=1)) == B.PA_ERR_UNSUPPORTED   # G > 32
 

@@ -48,15 +48,16 @@ def _decode_both(wl):
     assert err <= tol_of(wl), err
 
 
-@pytest.mark.parametrize("kind", ["act", "fp8"])
+@pytest.mark.parametrize("kind", ["act", "fp8", "mqa_fp8"])
 def test_noalloc_two_calls(kind):
     if not torch.cuda.is_available():
         pytest.skip("no GPU")
     B.load()
-    fp8 = kind == "fp8"
-    big = S.random_batch(41, [6000, 17, 3000, 9000, 1, 2048, 700, 4095] * 4, [], hq=32, hkv=8,
+    fp8 = kind != "act"
+    hkv = 1 if kind == "mqa_fp8" else 8     # 32 query heads per K/V head: the largest partials
+    big = S.random_batch(41, [6000, 17, 3000, 9000, 1, 2048, 700, 4095] * 4, [], hq=32, hkv=hkv,
                          d=128, act=torch.bfloat16, fp8=fp8)
-    small = S.random_batch(42, [100, 2500, 33], [], hq=32, hkv=8, d=128, act=torch.bfloat16,
+    small = S.random_batch(42, [100, 2500, 33], [], hq=32, hkv=hkv, d=128, act=torch.bfloat16,
                            fp8=fp8)
     _decode_both(big)
     _decode_both(small)
