@@ -96,6 +96,8 @@ struct AttnParams {
   bool masked;        // window or ALiBi present: the kernels' masked variants run
   int32_t max_seq_len;
   int32_t max_query_len;
+  // prefill: query heads (of one K/V head) per workgroup
+  int32_t heads_per_wg;
   // decode: the flattened (request, K/V head, block) key stream is cut into
   // num_workers equal contiguous ranges, one per wave; wg_waves consecutive
   // workers form one workgroup, whose range is the union of theirs

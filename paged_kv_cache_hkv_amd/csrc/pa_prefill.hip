@@ -10,12 +10,14 @@
 // tile in registers and LDS ("vLLM 推理全流程深度解析", FlashAttention keeps
 // softmax and matmul in on-chip memory and never writes the score matrix out).
 //
-// Work decomposition.  A workgroup owns (request, group of `hpw` query heads
-// sharing one K/V head, tile of queries); each wave takes one query head and
-// 32 queries.  Tiles are numbered from the END of each request and dispatched
-// in that order, so the tiles with the most keys start first (longest-first
-// scheduling over uneven chunks).  All waves of a workgroup share each 64-key
-// K/V tile in LDS.  One kernel, prefill_pp_kernel: 8 waves, 256/hpw queries,
+// Work decomposition.  An item is (request, group of `hpw` query heads
+// sharing one K/V head, tile of queries); each wave of the workgroup working
+// on it takes one query head and 32 queries, and all waves share each 64-key
+// K/V tile in LDS.  The grid is one resident workgroup per compute unit, each
+// working through its own list of items (see the kernel's schedule comment):
+// no unit waits for the dispatcher between items.  Within a request, items
+// run from the END of the request (the most keys) to its start.
+// One kernel, prefill_pp_kernel: 8 waves, 256/hpw queries per item,
 // K/V tiles copied global -> LDS by DMA into 4-stage rings, and two groups of
 // 4 waves alternating between the MFMA phase and the softmax phase (see the
 // kernel's own comment); 8-bit tiles (fp8, int8) land in a ring of their own
@@ -71,7 +73,10 @@ __device__ inline void window_alibi(f32x16 (&sc)[2], int k0, int half, int qpos,
     // key < qpos - window_left  <=>  off < -window_left - base (clamped to
     // the offsets' range 0..63, in 64 bits so no window width can overflow)
     const int64_t lim64 = -(int64_t)window_left - base;
-    const int lim = (int)(lim64 < -1 ? -1 : (lim64 > 64 ? 64 : lim64));
+    int lim = (int)(lim64 < -1 ? -1 : (lim64 > 64 ? 64 : lim64));
+    // compare in 32 bits below (left to itself the compiler folds the clamp
+    // into 64-bit compares against constants held in scalar registers)
+    asm volatile("" : "+v"(lim));
 #pragma unroll
     for (int u = 0; u < 2; ++u)
 #pragma unroll
@@ -112,6 +117,8 @@ struct LdsTile {
 };
 
 typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+// the kernel's parameter block in the kernarg segment (read-only, scalar loads)
+typedef __attribute__((address_space(4))) const AttnParams CParams;
 typedef __attribute__((address_space(3))) bf16x4 lds_bf16x4;
 typedef __attribute__((address_space(3))) void lds_void;
 
@@ -184,7 +191,7 @@ __device__ inline unsigned tile_okmask(const int32_t* bt_row, int nblk, int nb32
 }
 
 template <int D, typename CT, int KVB, bool I8, bool MASK>
-__global__ __launch_bounds__(kPPThreads) void prefill_pp_kernel(AttnParams p, int hpw) {
+__global__ __launch_bounds__(kPPThreads) void prefill_pp_kernel(AttnParams p) {
   using M = Mfma<CT>;
   using vec8 = typename M::vec8;
   using L = LdsTile<D>;
@@ -216,111 +223,27 @@ __global__ __launch_bounds__(kPPThreads) void prefill_pp_kernel(AttnParams p, in
   __shared__ u32x4 K8[KVB == 1 ? NS * kPos8 : 1];
   __shared__ u32x4 V8[KVB == 1 ? NS * kPos8 : 1];
 
-  // Request-major numbering: consecutive workgroups are the query tiles of
-  // one request for consecutive head groups; workgroups are spread over the
-  // 8 XCDs by number, so with 8 (or a multiple of 8) head groups an XCD keeps
-  // the same K/V head and its L2 serves every query tile of the request the
-  // K/V stream it is reading.  Within a request the tiles run longest first,
-  // and when the launch holds at most 64 requests they are taken in order of
-  // decreasing sequence length, so the longest tiles of the whole batch start
-  // first; requests of equal length share their turn tile by tile.
-  const unsigned lin = blockIdx.x + gridDim.x * (blockIdx.y + gridDim.y * blockIdx.z);
-  const unsigned bx = lin % gridDim.x;
-  unsigned bz = (lin / gridDim.x) % gridDim.z;
-  int rk = (int)(lin / (gridDim.x * gridDim.z));
-  if (gridDim.y <= 64) {
-    // lane l < nr holds request l: `first` requests are longer, `same` are
-    // as long (itself included), `before` of those have a lower index
-    const int nr = (int)gridDim.y;
-    const int gz = (int)gridDim.z;
-    const int l0 = (int)(threadIdx.x & 63);
-    const int key = l0 < nr ? p.seq_lens[p.req_begin + l0] : -1;
-    int first = 0, same = 0, before = 0;
-    for (int j = 0; j < nr; ++j) {
-      const int kj = __builtin_amdgcn_readlane(key, j);
-      first += kj > key;
-      same += kj == key;
-      before += (kj == key) & (j < l0);
-    }
-    // the (request, tile) slots of a group of equally long requests are taken
-    // tile-major: every request's first tile, then every second tile, ...
-    const int t = (int)(lin / gridDim.x);
-    const int in_grp = t - first * gz;
-    const int m = max(same, 1);
-    const bool mine = l0 < nr && in_grp >= 0 && in_grp < same * gz && in_grp % m == before;
-    const int sel = (int)__builtin_ctzll(__ballot(mine));
-    rk = sel;
-    bz = (unsigned)__builtin_amdgcn_readlane(in_grp / m, sel);
-  }
-  const unsigned by = (unsigned)rk;
-  const int r = p.req_begin + rk;
-  const int q_first = p.qsl[r];
-  const int n = p.qsl[r + 1] - q_first;
-  const int QB = (32 * kPPWaves) / hpw;
-  const int q_hi = n - (int)bz * QB;      // tile z covers queries [q_hi - QB, q_hi)
-  if (q_hi <= 0) return;
-  const int G = p.group;
-  const int s_all = p.seq_lens[r];
-  const int c = s_all - n;
-  int s_eff = min(s_all, p.max_seq_len);
-  s_eff = min(s_eff, p.max_blocks_per_req * kBlock);
-  const int k_end = min(c + q_hi, s_eff);
-  const int ntiles = (k_end + kTileK - 1) / kTileK;
-  const int kt0 = MASK ? max(0, c + max(q_hi - QB, 0) - p.window_left) / kTileK : 0;
-
+  // ---- roles that hold for every item ----
   const int lane = threadIdx.x & 63;
   const int wave = wave_uniform(threadIdx.x >> 6);
   const int grp = wave >> 2;
   const int half = lane >> 5;
   const int l32 = lane & 31;
-  const int qh = (int)bx * hpw + (wave % hpw);
-  const int kvh = qh / G;
-  const int wq0 = q_hi - QB + (wave / hpw) * 32;   // first query of the wave (may be < 0)
-  const int qi = wq0 + l32;                        // this lane's query
-  const bool q_ok = qi >= 0;
-  const int qpos = c + qi;
-  const int wave_first_pos = c + wq0;
-  const int wave_last_pos = c + wq0 + 31;
-
-  // Q as the B operand of S^T = K . Q^T: B[k = 8*half + e][col = l32] = Q[qi][16 s + 8 half + e]
-  vec8 qop[QS];
-  {
-    const CT* qrow = static_cast<const CT*>(p.q) + (int64_t)(q_first + (q_ok ? qi : 0)) * p.q_row_stride +
-                     (int64_t)qh * D;
-#pragma unroll
-    for (int s = 0; s < QS; ++s)
-      qop[s] = q_ok ? __builtin_bit_cast(vec8, ld16(qrow + 16 * s + 8 * half))
-                    : __builtin_bit_cast(vec8, u32x4{0u, 0u, 0u, 0u});
-    // consume Q here, so the compiler retires these loads before the loop: a
-    // wait it placed inside the loop would also wait for every copy in flight
-#pragma unroll
-    for (int s = 0; s < QS; ++s) asm volatile("" : : "v"(__builtin_bit_cast(u32x4, qop[s])));
-  }
-
-  const int32_t* bt_row = p.block_tables + (int64_t)r * p.max_blocks_per_req;
-  const int nblk = (s_eff + kBlock - 1) / kBlock;
-  const int nb32 = (int)min(p.num_blocks, (int64_t)0x7FFFFFFF);
-  const int64_t tok_stride = (int64_t)p.num_kv_heads * D * KVB;
-  const int64_t blk_stride = tok_stride * kBlock;
-  const unsigned char* kbase = static_cast<const unsigned char*>(p.key_cache) + (int64_t)kvh * D * KVB;
-  const unsigned char* vbase = static_cast<const unsigned char*>(p.value_cache) + (int64_t)kvh * D * KVB;
-
-  // One pass over the table entries the workgroup's tiles use: when all of
-  // them are pool ids (the normal case) every block of every tile is present,
-  // and keys past the sequence are handled by the length tests alone.
-  bool my_ok = true;
-  for (int b = 4 * kt0 + (int)threadIdx.x; b < nblk; b += kPPThreads) {
-    const int id = bt_row[b];
-    my_ok &= (id >= 0) & (id < nb32);
-  }
-  const bool rowok = __syncthreads_and(my_ok);
-  auto okmask = [&](int t) __attribute__((always_inline)) {
-    return rowok ? 0xFu : tile_okmask(bt_row, nblk, nb32, t);
+  // The parameters are read afresh where an item starts and where it ends
+  // (scalar loads through a pointer the compiler cannot see through), so the
+  // values used only there are not held in scalar registers through the tile
+  // loop: the loop needs nearly all of them, and over budget the compiler
+  // stops running LDS reads ahead of the MFMAs.
+  auto params = []() __attribute__((always_inline)) {
+    const CParams* q = (const CParams*)__builtin_amdgcn_kernarg_segment_ptr();
+    asm volatile("" : "+s"(q));
+    return q;
   };
+  const int64_t tok_stride = (int64_t)p.num_kv_heads * D * KVB;
 
-  // copy roles (tile-invariant): instruction i of this wave fills positions
-  // inst*LPI .. inst*LPI+LPI-1 of a tile, inst = wave*IPW + i: keys of block
-  // wave/2 of the tile only, so a wave needs one block id per tile
+  // copy roles: instruction i of this wave fills positions inst*LPI ..
+  // inst*LPI+LPI-1 of a tile, inst = wave*IPW + i: keys of block wave/2 of
+  // the tile only, so a wave needs one block id per tile
   const int cb = wave >> 1;
   const bool copy_lane = LPI == 64 || lane < LPI;
   unsigned koff[IPW], voff[IPW];
@@ -339,283 +262,456 @@ __global__ __launch_bounds__(kPPThreads) void prefill_pp_kernel(AttnParams p, in
     }
   }
   const unsigned kr0 = lds_offset(KVB == 2 ? Kr : K8), vr0 = lds_offset(KVB == 2 ? Vr : V8);
-  // this wave's table entry for tile t (index clamped into the sequence), and
-  // the id its copies use (absent -> block 0: masked keys, zeroed V rows)
-  auto raw_id = [&](int t) __attribute__((always_inline)) {
-    return load_uniform(bt_row, min(4 * t + cb, nblk - 1));
-  };
-  auto copy_id = [&](int raw, int t) __attribute__((always_inline)) {
-    return ((4 * t + cb < nblk) & (raw >= 0) & (raw < nb32)) ? raw : 0;
-  };
-  auto copy_tile = [&](const unsigned char* base, const unsigned (&off)[IPW], int id,
-                       unsigned lds0) __attribute__((always_inline)) {
-    const unsigned char* src = base + (int64_t)id * blk_stride;
-    if (copy_lane) {
-#pragma unroll
-      for (int i = 0; i < IPW; ++i)
-        lds_dma16<false, false>(src, off[i], lds0 + (unsigned)((wave * IPW + i) * LPI * 16));
-    }
-  };
-  // after the copy of V tile t has landed: zero the rows of keys the tile
-  // lacks (past the sequence, absent blocks), each lane exactly the positions
-  // its own copies wrote
-  auto fix_v = [&](int t, u32x4* Vs) __attribute__((always_inline)) {
-    if (kTileK * t + kTileK <= s_eff && rowok) return;
-    const unsigned ok = okmask(t);
-#pragma unroll
-    for (int i = 0; i < IPW; ++i) {
-      const int pidx = (wave * IPW + i) * LPI + lane;
-      const int key = pidx / L::CPR;
-      if (kTileK * t + key >= s_eff || !((ok >> (key / kBlock)) & 1u)) Vs[pidx] = u32x4{0u, 0u, 0u, 0u};
-    }
-  };
 
-  // 8-bit caches: after this wave's copies of tile t have landed, widen them
-  // (16 bytes per lane) into the operand stage in the LdsTile layout; V rows
-  // of keys the tile lacks become zeros (K rows need not: their scores are
-  // masked by selects)
-  auto widen = [&](const u32x4* src8, u32x4* dst, int t, bool is_v) __attribute__((always_inline)) {
-    if (!copy_lane) return;
-    const int pidx = wave * LPI + lane;
-    const int key = pidx / CPR8, c8 = pidx % CPR8;
-    const u32x4 w = src8[pidx];
-    u32x4 lo{widen8x2<CT, I8>(w[0], false), widen8x2<CT, I8>(w[0], true),
-             widen8x2<CT, I8>(w[1], false), widen8x2<CT, I8>(w[1], true)};
-    u32x4 hi{widen8x2<CT, I8>(w[2], false), widen8x2<CT, I8>(w[2], true),
-             widen8x2<CT, I8>(w[3], false), widen8x2<CT, I8>(w[3], true)};
-    int sw = L::swk(key);
-    if (is_v) {
-      sw = L::swv(key);
-      if (!(kTileK * t + kTileK <= s_eff && rowok)) {
-        const unsigned ok = okmask(t);
-        if (kTileK * t + key >= s_eff || !((ok >> (key / kBlock)) & 1u)) lo = hi = u32x4{0u, 0u, 0u, 0u};
-      }
-    }
-    dst[key * L::CPR + ((2 * c8) ^ sw)] = lo;
-    dst[key * L::CPR + ((2 * c8 + 1) ^ sw)] = hi;
-  };
-
-  // lane roles in the LDS reads (tile-invariant)
+  // lane roles in the LDS reads
   const int kswz = L::swk(l32);                   // key 32u + l32 has the swizzle of l32
   const int g16 = lane >> 4;                      // 16-lane group
   const int ta = (lane & 15) >> 2, tb = lane & 3; // transposed-read row supplier (key a, d 4b)
   const int vswz = L::swv(ta);                    // keys ... + 4h + a share a's swizzle
 
-  const float c2 = MASK ? 1.f : p.scale_log2;
-  const float slope2 = (MASK && p.alibi != nullptr)
-                           ? __builtin_bit_cast(float, load_uniform(reinterpret_cast<const int32_t*>(p.alibi), qh)) * kLog2e
-                           : 0.f;
-  f32x16 acc[DT];
-#pragma unroll
-  for (int t = 0; t < DT; ++t) acc[t] = f32x16{};
-  float m_used = -INFINITY, l_run = 0.f;
-  f32x16 sc[2];
-  u32x4 pk[4];    // P of the previous tile, two 16-bit values per dword: pk[2u + v] feeds PV step (u, v)
-#pragma unroll
-  for (int i = 0; i < 4; ++i) pk[i] = u32x4{0u, 0u, 0u, 0u};
+  // ---- schedule ----
+  // One resident workgroup per compute unit works through a list of items
+  // (request, head group, QB-query tile); no workgroup waits for another, so
+  // a unit goes from one item straight to its next.  With the grid a
+  // multiple of the head-group count, workgroup w keeps head group w % nhg
+  // (workgroups are spread over the 8 XCDs by number, so with 8 head groups
+  // an XCD's L2 serves one K/V head) and takes that head group's items in
+  // rounds of C = grid / nhg, in snake order (round k: position cw in even
+  // rounds, C-1-cw in odd ones), so the longest and shortest items of
+  // consecutive rounds pair up.  Items are ordered by request -- requests by
+  // decreasing sequence length within each run of 64, ties by index -- and
+  // within a request from its last tile (the most keys) to its first.
+  // Request cursor over runs of 64 requests, lane l holding request 64*ch + l:
+  // its first batch row, new tokens, sequence length, items, and the items
+  // of the run ahead of it.  Each wave keeps its own copy in LDS (every wave
+  // computes the same values), so none of it stays in registers while an
+  // item runs.
+  __shared__ int cur_lane[kPPWaves][5][64];
+  __shared__ int cur_sc[kPPWaves][4];   // run, items before it, items in it, next item number
+  cur_sc[wave][0] = -1;
+  cur_sc[wave][1] = 0;
+  cur_sc[wave][2] = 0;
+  cur_sc[wave][3] = 0;
 
-  auto active = [&](int t) __attribute__((always_inline)) {
-    const int k0 = t * kTileK;
-    return k0 <= wave_last_pos && (!MASK || k0 + kTileK - 1 >= wave_first_pos - p.window_left);
-  };
-
-  // M phase: S_j (QK) and O += V_{j-1} P_{j-1} (PV), the two MFMA chains interleaved
-  auto mphase = [&](const u32x4* Kt, const u32x4* Vt) __attribute__((always_inline)) {
-    sc[0] = f32x16{};
-    sc[1] = f32x16{};
-#pragma unroll
-    for (int s = 0; s < QS; ++s) {
-#pragma unroll
-      for (int u = 0; u < 2; ++u) {
-        const vec8 kop = __builtin_bit_cast(vec8, Kt[(32 * u + l32) * L::CPR + ((2 * s + half) ^ kswz)]);
-        sc[u] = M::mma32(kop, qop[s], sc[u]);
+  for (;;) {
+    const CParams* pp = params();
+    const int hpw = pp->heads_per_wg;
+    const int QB = (32 * kPPWaves) / hpw;   // queries per item
+    const int nhg = pp->num_q_heads / hpw;  // head groups
+    const int P = (int)gridDim.x;
+    const bool pinned = P % nhg == 0;
+    const int C = pinned ? P / nhg : P;
+    const int cw = pinned ? (int)blockIdx.x / nhg : (int)blockIdx.x;
+    const int hg_pin = pinned ? (int)blockIdx.x % nhg : 0;
+    const int k = wave_uniform(cur_sc[wave][3]);
+    int ch = wave_uniform(cur_sc[wave][0]);
+    int ch_base = wave_uniform(cur_sc[wave][1]);
+    int ch_total = wave_uniform(cur_sc[wave][2]);
+    const int pos = k * C + ((k & 1) ? C - 1 - cw : cw);
+    const int hg = pinned ? hg_pin : pos % nhg;
+    const int tt = pinned ? pos : pos / nhg;
+    bool found = true;
+    while (ch < 0 || tt >= ch_base + ch_total) {
+      if (ch >= 0) ch_base += ch_total;
+      ++ch;
+      if (ch * 64 >= pp->num_reqs) {
+        found = false;
+        break;
       }
-#pragma unroll
-      for (int e = 0; e < PPS; ++e) {
-        const int pv = s * PPS + e;
-        const int uv = pv / DT, t = pv % DT;
-        // keys of this step: 32u + 16v + 8r + 4h + a (h = lane/32), element e = 4r + a
-        const int key_r0 = 32 * (uv >> 1) + 16 * (uv & 1) + 4 * half + ta;
-        const int chunk = 4 * t + 2 * (g16 & 1) + (tb >> 1);
-        const int byte_off = 8 * (tb & 1);
-        const u32x2 lo = lds_read_tr16(Vt, key_r0 * L::CPR + (chunk ^ vswz), byte_off);
-        const u32x2 hi = lds_read_tr16(Vt, (key_r0 + 8) * L::CPR + (chunk ^ vswz), byte_off);
-        const vec8 vop = __builtin_bit_cast(vec8, u32x4{lo[0], lo[1], hi[0], hi[1]});
-        acc[t] = M::mma32(vop, __builtin_bit_cast(vec8, pk[uv]), acc[t]);
+      const int rr = ch * 64 + lane;
+      const bool v = rr < pp->num_reqs;
+      const int ra = pp->req_begin + (v ? rr : 0);
+      const int q0 = pp->qsl[ra];
+      const int nn = v ? max(pp->qsl[ra + 1] - q0, 0) : 0;
+      const int sl = pp->seq_lens[ra];
+      const int cnt = (nn + QB - 1) / QB;
+      const int key = v ? sl : -1;
+      int rank = 0;
+      for (int j = 0; j < 64; ++j) {
+        const int kj = __builtin_amdgcn_readlane(key, j);
+        rank += (kj > key) | ((kj == key) & (j < lane));
       }
+      int pre = 0, tot = 0;
+      for (int j = 0; j < 64; ++j) {
+        const int rj = __builtin_amdgcn_readlane(rank, j), cj = __builtin_amdgcn_readlane(cnt, j);
+        pre += rj < rank ? cj : 0;
+        tot += cj;
+      }
+      cur_lane[wave][0][lane] = q0;
+      cur_lane[wave][1][lane] = nn;
+      cur_lane[wave][2][lane] = sl;
+      cur_lane[wave][3][lane] = cnt;
+      cur_lane[wave][4][lane] = pre;
+      ch_total = tot;
     }
-    // issue order: LDS reads run ahead of the MFMAs that consume them
-    constexpr int kReads = 2 * QS + 8 * DT;
-    constexpr int kMfma = 2 * QS + 4 * DT;
-    constexpr int kLead = 6;
-    constexpr int kPer = (kReads - kLead + kMfma - 1) / kMfma;
-    __builtin_amdgcn_sched_group_barrier(0x100, kLead, 0);
-#pragma unroll
-    for (int i = 0; i < kMfma; ++i) {
-      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-      __builtin_amdgcn_sched_group_barrier(0x100, kPer, 0);
-    }
-  };
+    if (!found) break;
+    cur_sc[wave][0] = ch;
+    cur_sc[wave][1] = ch_base;
+    cur_sc[wave][2] = ch_total;
+    cur_sc[wave][3] = k + 1;
+    const int rel = tt - ch_base;
+    const int c_cnt = cur_lane[wave][3][lane], c_pre = cur_lane[wave][4][lane];
+    const bool mine = c_cnt > 0 && rel >= c_pre && rel < c_pre + c_cnt;
+    const int sel = (int)__builtin_ctzll(__ballot(mine));
+    const int r = pp->req_begin + ch * 64 + sel;
+    const int bz = rel - wave_uniform(cur_lane[wave][4][sel]);   // tile, counted from the request's end
+    const int q_first = wave_uniform(cur_lane[wave][0][sel]);
+    const int n = wave_uniform(cur_lane[wave][1][sel]);
+    const int s_all = wave_uniform(cur_lane[wave][2][sel]);
 
-  // V phase softmax of tile j: scores in sc -> probabilities in pk, row sums in l_run
-  auto softmax = [&](int j) __attribute__((always_inline)) {
-    const int k0 = j * kTileK;
-    if (k0 + kTileK - 1 > wave_first_pos || k0 + kTileK > s_eff) {
-      // element g of subtile u is key k0 + 4 half + (32u + 8(g/4) + g%4):
-      // masked past the query's position and past the sequence
-      const int lim = min(qpos, s_eff - 1) - (k0 + 4 * half);
+    const int q_hi = n - bz * QB;      // the item covers queries [q_hi - QB, q_hi)
+    const int c = s_all - n;
+    int s_eff = min(s_all, pp->max_seq_len);
+    s_eff = min(s_eff, pp->max_blocks_per_req * kBlock);
+    const int k_end = min(c + q_hi, s_eff);
+    const int ntiles = (k_end + kTileK - 1) / kTileK;
+    const int window_left = pp->window_left;
+    const int kt0 = MASK ? max(0, c + max(q_hi - QB, 0) - window_left) / kTileK : 0;
+    const int G = pp->group;
+    const int nb32 = (int)min(pp->num_blocks, (int64_t)0x7FFFFFFF);
+    const int64_t blk_stride = (int64_t)pp->num_kv_heads * D * KVB * kBlock;
+
+    const int qh = hg * hpw + (wave % hpw);
+    const int kvh = qh / G;
+    const int wq0 = q_hi - QB + (wave / hpw) * 32;   // first query of the wave (may be < 0)
+    const int qi = wq0 + l32;                        // this lane's query
+    const bool q_ok = qi >= 0;
+    const int qpos = c + qi;
+    const int wave_first_pos = c + wq0;
+    const int wave_last_pos = c + wq0 + 31;
+
+    const int32_t* bt_row = pp->block_tables + (int64_t)r * pp->max_blocks_per_req;
+    const int nblk = (s_eff + kBlock - 1) / kBlock;
+    const unsigned char* kbase = static_cast<const unsigned char*>(pp->key_cache) + (int64_t)kvh * D * KVB;
+    const unsigned char* vbase = static_cast<const unsigned char*>(pp->value_cache) + (int64_t)kvh * D * KVB;
+
+    // this wave's table entry for tile t (index clamped into the sequence), and
+    // the id its copies use (absent -> block 0: masked keys, zeroed V rows)
+    auto raw_id = [&](int t) __attribute__((always_inline)) {
+      return load_uniform(bt_row, min(4 * t + cb, nblk - 1));
+    };
+    auto copy_id = [&](int raw, int t) __attribute__((always_inline)) {
+      return ((4 * t + cb < nblk) & (raw >= 0) & (raw < nb32)) ? raw : 0;
+    };
+    // The LDS destination is formed where the copy is issued: the add is
+    // hidden from loop-invariant hoisting, which would otherwise hold one
+    // scalar register per (stage, instruction) through the tile loop and push
+    // the loop over the scalar register budget (the compiler then stops
+    // running LDS reads ahead of the MFMAs).
+    auto copy_tile = [&](const unsigned char* base, const unsigned (&off)[IPW], int id,
+                         unsigned lds0) __attribute__((always_inline)) {
+      const unsigned char* src = base + (int64_t)id * blk_stride;
+      unsigned wdst = (unsigned)(wave * IPW * LPI * 16);
+      asm volatile("" : "+s"(wdst));
+      if (copy_lane) {
+#pragma unroll
+        for (int i = 0; i < IPW; ++i)
+          lds_dma16<false, false>(src, off[i], lds0 + wdst + (unsigned)(i * LPI * 16));
+      }
+    };
+
+    // The item's first copies (K tiles t0 .. t0+2, V tiles t0 .. t0+1) go out
+    // before its Q rows and table check are loaded, so the three transfers
+    // overlap; the loads' wait below covers the copies as well.
+    int raw_n = 0, id_v = 0;
+    if (ntiles > kt0) {
+      const int id0 = copy_id(raw_id(kt0), kt0);
+      const int id1 = copy_id(raw_id(kt0 + 1), kt0 + 1);
+      const int id2 = copy_id(raw_id(kt0 + 2), kt0 + 2);
+      raw_n = raw_id(kt0 + 3);      // tile j+3's entry, checked in V(j)
+      id_v = id2;                   // tile j+2's id (its V copy in V(j))
+      copy_tile(kbase, koff, id0, kr0);
+      copy_tile(vbase, voff, id0, vr0);
+      if (kt0 + 1 < ntiles) {
+        copy_tile(kbase, koff, id1, kr0 + kTileBytes);
+        copy_tile(vbase, voff, id1, vr0 + kTileBytes);
+      }
+      if (kt0 + 2 < ntiles) copy_tile(kbase, koff, id2, kr0 + 2 * kTileBytes);
+    }
+
+    // Q as the B operand of S^T = K . Q^T: B[k = 8*half + e][col = l32] = Q[qi][16 s + 8 half + e]
+    vec8 qop[QS];
+    {
+      const CT* qrow = static_cast<const CT*>(pp->q) + (int64_t)(q_first + (q_ok ? qi : 0)) * pp->q_row_stride +
+                       (int64_t)qh * D;
+#pragma unroll
+      for (int s = 0; s < QS; ++s)
+        qop[s] = q_ok ? __builtin_bit_cast(vec8, ld16(qrow + 16 * s + 8 * half))
+                      : __builtin_bit_cast(vec8, u32x4{0u, 0u, 0u, 0u});
+    }
+    // One pass over the table entries the item's tiles use: when all of them
+    // are pool ids (the normal case) every block of every tile is present,
+    // and keys past the sequence are handled by the length tests alone.
+    bool my_ok = true;
+    for (int b = 4 * kt0 + (int)threadIdx.x; b < nblk; b += kPPThreads) {
+      const int id = bt_row[b];
+      my_ok &= (id >= 0) & (id < nb32);
+    }
+    // consume Q here, so the compiler retires these loads (and with them the
+    // copies above) before the loop: a wait it placed inside the loop would
+    // also wait for every copy in flight
+#pragma unroll
+    for (int s = 0; s < QS; ++s) asm volatile("" : : "v"(__builtin_bit_cast(u32x4, qop[s])));
+    const bool rowok = __syncthreads_and(my_ok);
+    auto okmask = [&](int t) __attribute__((always_inline)) {
+      return rowok ? 0xFu : tile_okmask(bt_row, nblk, nb32, t);
+    };
+
+    // after the copy of V tile t has landed: zero the rows of keys the tile
+    // lacks (past the sequence, absent blocks), each lane exactly the positions
+    // its own copies wrote
+    auto fix_v = [&](int t, u32x4* Vs) __attribute__((always_inline)) {
+      if (kTileK * t + kTileK <= s_eff && rowok) return;
+      const unsigned ok = okmask(t);
+#pragma unroll
+      for (int i = 0; i < IPW; ++i) {
+        const int pidx = (wave * IPW + i) * LPI + lane;
+        const int key = pidx / L::CPR;
+        if (kTileK * t + key >= s_eff || !((ok >> (key / kBlock)) & 1u)) Vs[pidx] = u32x4{0u, 0u, 0u, 0u};
+      }
+    };
+
+    // 8-bit caches: after this wave's copies of tile t have landed, widen them
+    // (16 bytes per lane) into the operand stage in the LdsTile layout; V rows
+    // of keys the tile lacks become zeros (K rows need not: their scores are
+    // masked by selects)
+    auto widen = [&](const u32x4* src8, u32x4* dst, int t, bool is_v) __attribute__((always_inline)) {
+      if (!copy_lane) return;
+      const int pidx = wave * LPI + lane;
+      const int key = pidx / CPR8, c8 = pidx % CPR8;
+      const u32x4 w = src8[pidx];
+      u32x4 lo{widen8x2<CT, I8>(w[0], false), widen8x2<CT, I8>(w[0], true),
+               widen8x2<CT, I8>(w[1], false), widen8x2<CT, I8>(w[1], true)};
+      u32x4 hi{widen8x2<CT, I8>(w[2], false), widen8x2<CT, I8>(w[2], true),
+               widen8x2<CT, I8>(w[3], false), widen8x2<CT, I8>(w[3], true)};
+      int sw = L::swk(key);
+      if (is_v) {
+        sw = L::swv(key);
+        if (!(kTileK * t + kTileK <= s_eff && rowok)) {
+          const unsigned ok = okmask(t);
+          if (kTileK * t + key >= s_eff || !((ok >> (key / kBlock)) & 1u)) lo = hi = u32x4{0u, 0u, 0u, 0u};
+        }
+      }
+      dst[key * L::CPR + ((2 * c8) ^ sw)] = lo;
+      dst[key * L::CPR + ((2 * c8 + 1) ^ sw)] = hi;
+    };
+
+    const float scale_log2 = pp->scale_log2;
+    const float c2 = MASK ? 1.f : scale_log2;
+    const float slope2 = (MASK && pp->alibi != nullptr)
+                             ? __builtin_bit_cast(float, load_uniform(reinterpret_cast<const int32_t*>(pp->alibi), qh)) * kLog2e
+                             : 0.f;
+    f32x16 acc[DT];
+#pragma unroll
+    for (int t = 0; t < DT; ++t) acc[t] = f32x16{};
+    float m_used = -INFINITY, l_run = 0.f;
+    f32x16 sc[2];
+    u32x4 pk[4];    // P of the previous tile, two 16-bit values per dword: pk[2u + v] feeds PV step (u, v)
+#pragma unroll
+    for (int i = 0; i < 4; ++i) pk[i] = u32x4{0u, 0u, 0u, 0u};
+    auto active = [&](int t) __attribute__((always_inline)) {
+      const int k0 = t * kTileK;
+      return k0 <= wave_last_pos && (!MASK || k0 + kTileK - 1 >= wave_first_pos - window_left);
+    };
+
+    // M phase: S_j (QK) and O += V_{j-1} P_{j-1} (PV), the two MFMA chains interleaved
+    auto mphase = [&](const u32x4* Kt, const u32x4* Vt) __attribute__((always_inline)) {
+      sc[0] = f32x16{};
+      sc[1] = f32x16{};
+#pragma unroll
+      for (int s = 0; s < QS; ++s) {
+#pragma unroll
+        for (int u = 0; u < 2; ++u) {
+          const vec8 kop = __builtin_bit_cast(vec8, Kt[(32 * u + l32) * L::CPR + ((2 * s + half) ^ kswz)]);
+          sc[u] = M::mma32(kop, qop[s], sc[u]);
+        }
+#pragma unroll
+        for (int e = 0; e < PPS; ++e) {
+          const int pv = s * PPS + e;
+          const int uv = pv / DT, t = pv % DT;
+          // keys of this step: 32u + 16v + 8r + 4h + a (h = lane/32), element e = 4r + a
+          const int key_r0 = 32 * (uv >> 1) + 16 * (uv & 1) + 4 * half + ta;
+          const int chunk = 4 * t + 2 * (g16 & 1) + (tb >> 1);
+          const int byte_off = 8 * (tb & 1);
+          const u32x2 lo = lds_read_tr16(Vt, key_r0 * L::CPR + (chunk ^ vswz), byte_off);
+          const u32x2 hi = lds_read_tr16(Vt, (key_r0 + 8) * L::CPR + (chunk ^ vswz), byte_off);
+          const vec8 vop = __builtin_bit_cast(vec8, u32x4{lo[0], lo[1], hi[0], hi[1]});
+          acc[t] = M::mma32(vop, __builtin_bit_cast(vec8, pk[uv]), acc[t]);
+        }
+      }
+      // issue order: LDS reads run ahead of the MFMAs that consume them
+      constexpr int kReads = 2 * QS + 8 * DT;
+      constexpr int kMfma = 2 * QS + 4 * DT;
+      constexpr int kLead = 6;
+      constexpr int kPer = (kReads - kLead + kMfma - 1) / kMfma;
+      __builtin_amdgcn_sched_group_barrier(0x100, kLead, 0);
+#pragma unroll
+      for (int i = 0; i < kMfma; ++i) {
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+        __builtin_amdgcn_sched_group_barrier(0x100, kPer, 0);
+      }
+    };
+
+    // V phase softmax of tile j: scores in sc -> probabilities in pk, row sums in l_run
+    auto softmax = [&](int j) __attribute__((always_inline)) {
+      const int k0 = j * kTileK;
+      if (k0 + kTileK - 1 > wave_first_pos || k0 + kTileK > s_eff) {
+        // element g of subtile u is key k0 + 4 half + (32u + 8(g/4) + g%4):
+        // masked past the query's position and past the sequence
+        const int lim = min(qpos, s_eff - 1) - (k0 + 4 * half);
+#pragma unroll
+        for (int u = 0; u < 2; ++u)
+#pragma unroll
+          for (int g = 0; g < 16; ++g)
+            sc[u][g] = (32 * u + 8 * (g / 4) + (g % 4) > lim) ? -INFINITY : sc[u][g];
+      }
+      if (!rowok) {
+        const unsigned okj = okmask(j);
+        // absent blocks: block b of the tile holds elements 8(b%2) .. 8(b%2)+7 of subtile b/2
+#pragma unroll
+        for (int b = 0; b < 4; ++b)
+          if (!((okj >> b) & 1u)) {
+#pragma unroll
+            for (int g = 0; g < 8; ++g) sc[b >> 1][8 * (b & 1) + g] = -INFINITY;
+          }
+      }
+      if constexpr (MASK)
+        window_alibi(sc, k0, half, qpos, window_left, scale_log2, slope2, k0 < wave_last_pos - window_left);
+      // row max of the lane's 32 scores as a tree of three-input maxima (16
+      // instructions, short dependency chains)
+      float m10[11];
+#pragma unroll
+      for (int k = 0; k < 10; ++k)
+        m10[k] = max3f(sc[(3 * k) >> 4][(3 * k) & 15], sc[(3 * k + 1) >> 4][(3 * k + 1) & 15],
+                       sc[(3 * k + 2) >> 4][(3 * k + 2) & 15]);
+      m10[10] = fmaxf(sc[1][14], sc[1][15]);
+      const float m3a = max3f(m10[0], m10[1], m10[2]), m3b = max3f(m10[3], m10[4], m10[5]);
+      const float m3c = max3f(m10[6], m10[7], m10[8]);
+      float mx = max3f(max3f(m3a, m3b, m3c), m10[9], m10[10]);
+      mx = pair32_max_swap(mx);
+      // lazy rescale: move the reference max only when it grew by more than 2^8
+      const bool grow = (m_used == -INFINITY) ? (mx > -INFINITY) : ((mx - m_used) * c2 > kRescaleLog2);
+      if (__ballot(grow)) {
+        const float m_new = grow ? mx : m_used;
+        const float alpha = (m_used == -INFINITY) ? 0.f : fast_exp2((m_used - m_new) * c2);
+        l_run *= alpha;
+#pragma unroll
+        for (int t = 0; t < DT; ++t) acc[t] *= alpha;
+        m_used = m_new;
+      }
+      const float mref = (m_used == -INFINITY) ? 0.f : m_used * c2;
 #pragma unroll
       for (int u = 0; u < 2; ++u)
 #pragma unroll
-        for (int g = 0; g < 16; ++g)
-          sc[u][g] = (32 * u + 8 * (g / 4) + (g % 4) > lim) ? -INFINITY : sc[u][g];
-    }
-    if (!rowok) {
-      const unsigned okj = okmask(j);
-      // absent blocks: block b of the tile holds elements 8(b%2) .. 8(b%2)+7 of subtile b/2
+        for (int g = 0; g < 16; ++g) sc[u][g] = fast_exp2(__builtin_fmaf(sc[u][g], c2, -mref));
+      // pack to the MFMA operand; row sums of the rounded probabilities the PV
+      // product uses, in four independent chains
+      float ls[4] = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-      for (int b = 0; b < 4; ++b)
-        if (!((okj >> b) & 1u)) {
+      for (int u = 0; u < 2; ++u)
 #pragma unroll
-          for (int g = 0; g < 8; ++g) sc[b >> 1][8 * (b & 1) + g] = -INFINITY;
+        for (int v = 0; v < 2; ++v) {
+          const u32x4 w{pack2<CT>(sc[u][8 * v + 0], sc[u][8 * v + 1]), pack2<CT>(sc[u][8 * v + 2], sc[u][8 * v + 3]),
+                        pack2<CT>(sc[u][8 * v + 4], sc[u][8 * v + 5]), pack2<CT>(sc[u][8 * v + 6], sc[u][8 * v + 7])};
+          pk[2 * u + v] = w;
+#pragma unroll
+          for (int k = 0; k < 4; ++k) ls[k] = M::sum2(w[k], ls[k]);
         }
-    }
-    if constexpr (MASK)
-      window_alibi(sc, k0, half, qpos, p.window_left, p.scale_log2, slope2, k0 < wave_last_pos - p.window_left);
-    // row max of the lane's 32 scores as a tree of three-input maxima (16
-    // instructions, short dependency chains)
-    float m10[11];
-#pragma unroll
-    for (int k = 0; k < 10; ++k)
-      m10[k] = max3f(sc[(3 * k) >> 4][(3 * k) & 15], sc[(3 * k + 1) >> 4][(3 * k + 1) & 15],
-                     sc[(3 * k + 2) >> 4][(3 * k + 2) & 15]);
-    m10[10] = fmaxf(sc[1][14], sc[1][15]);
-    const float m3a = max3f(m10[0], m10[1], m10[2]), m3b = max3f(m10[3], m10[4], m10[5]);
-    const float m3c = max3f(m10[6], m10[7], m10[8]);
-    float mx = max3f(max3f(m3a, m3b, m3c), m10[9], m10[10]);
-    mx = pair32_max_swap(mx);
-    // lazy rescale: move the reference max only when it grew by more than 2^8
-    const bool grow = (m_used == -INFINITY) ? (mx > -INFINITY) : ((mx - m_used) * c2 > kRescaleLog2);
-    if (__ballot(grow)) {
-      const float m_new = grow ? mx : m_used;
-      const float alpha = (m_used == -INFINITY) ? 0.f : fast_exp2((m_used - m_new) * c2);
-      l_run *= alpha;
-#pragma unroll
-      for (int t = 0; t < DT; ++t) acc[t] *= alpha;
-      m_used = m_new;
-    }
-    const float mref = (m_used == -INFINITY) ? 0.f : m_used * c2;
-#pragma unroll
-    for (int u = 0; u < 2; ++u)
-#pragma unroll
-      for (int g = 0; g < 16; ++g) sc[u][g] = fast_exp2(__builtin_fmaf(sc[u][g], c2, -mref));
-    // pack to the MFMA operand; row sums of the rounded probabilities the PV
-    // product uses, in four independent chains
-    float ls[4] = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-    for (int u = 0; u < 2; ++u)
-#pragma unroll
-      for (int v = 0; v < 2; ++v) {
-        const u32x4 w{pack2<CT>(sc[u][8 * v + 0], sc[u][8 * v + 1]), pack2<CT>(sc[u][8 * v + 2], sc[u][8 * v + 3]),
-                      pack2<CT>(sc[u][8 * v + 4], sc[u][8 * v + 5]), pack2<CT>(sc[u][8 * v + 6], sc[u][8 * v + 7])};
-        pk[2 * u + v] = w;
-#pragma unroll
-        for (int k = 0; k < 4; ++k) ls[k] = M::sum2(w[k], ls[k]);
-      }
-    l_run += (ls[0] + ls[1]) + (ls[2] + ls[3]);
-  };
-
-  if (ntiles > kt0) {
-    // prologue: K tiles t0 .. t0+2 and V tiles t0 .. t0+1
-    const int id0 = copy_id(raw_id(kt0), kt0);
-    const int id1 = copy_id(raw_id(kt0 + 1), kt0 + 1);
-    const int id2 = copy_id(raw_id(kt0 + 2), kt0 + 2);
-    int raw_n = raw_id(kt0 + 3);      // tile j+3's entry, checked in V(j)
-    int id_v = id2;                   // tile j+2's id (its V copy in V(j))
-    copy_tile(kbase, koff, id0, kr0);
-    copy_tile(vbase, voff, id0, vr0);
-    if (kt0 + 1 < ntiles) {
-      copy_tile(kbase, koff, id1, kr0 + kTileBytes);
-      copy_tile(vbase, voff, id1, vr0 + kTileBytes);
-    }
-    if (kt0 + 2 < ntiles) copy_tile(kbase, koff, id2, kr0 + 2 * kTileBytes);
-    // the first M phase multiplies zero probabilities with V operand stage
-    // NO-1: clear it, so stale LDS contents cannot turn 0 * V into NaN
-    for (int i = threadIdx.x; i < L::kPos; i += kPPThreads)
-      Vr[(NO - 1) * L::kPos + i] = u32x4{0u, 0u, 0u, 0u};
-    wait_vmcnt<0>();
-    if constexpr (KVB == 2) {
-      fix_v(kt0, Vr);
-      if (kt0 + 1 < ntiles) fix_v(kt0 + 1, Vr + L::kPos);
-    } else {
-      widen(K8, Kr, kt0, false);   // K(kt0); K(kt0 + 1) and V(kt0) in M(kt0)
-    }
-    barrier_nowait<true>();
-
-    auto step = [&](auto st_c, int j) __attribute__((always_inline)) {
-      constexpr int ST = decltype(st_c)::value;
-      const u32x4* Kt = Kr + (ST % NO) * L::kPos;
-      const u32x4* Vt = Vr + ((ST + NO - 1) % NO) * L::kPos;
-      // ---- M(j) ----
-      // one straight MFMA path (branches around MFMAs cost accumulator
-      // copies): a tile the wave does not need still runs, with zero
-      // probabilities (P of the first tile, of tiles past the wave's queries
-      // or before its window); its scores are discarded
-      mphase(Kt, Vt);
-      // retire the copies of V(j-2) (those of V(j-1) may stay in flight)
-      if (j - 1 >= kt0 && j + 2 < ntiles) wait_vmcnt<2 * IPW>();
-      else if (j - 1 >= kt0 && j + 1 < ntiles) wait_vmcnt<IPW>();
-      else wait_vmcnt<0>();
-      if constexpr (KVB == 2) {
-        if (j >= kt0 + 2 && j < ntiles) fix_v(j, Vr + ST * L::kPos);
-      } else {
-        // operand stages of K(j+1) and V(j): their previous tiles, K(j-1) and
-        // V(j-2), were last read in M(j-1), which every wave has finished
-        if (j + 1 < ntiles) widen(K8 + ((ST + 1) % NS) * kPos8, Kr + ((ST + 1) % NO) * L::kPos, j + 1, false);
-        if (j < ntiles) widen(V8 + ST * kPos8, Vr + (ST % NO) * L::kPos, j, true);
-      }
-      barrier_nowait<true>();
-      // ---- V(j) ----
-      const int id_k = copy_id(raw_n, j + 3);
-      raw_n = raw_id(j + 4);
-      if (j + 3 < ntiles) copy_tile(kbase, koff, id_k, kr0 + (unsigned)((ST + 3) % NS) * kTileBytes);
-      if (j + 2 < ntiles) copy_tile(vbase, voff, id_v, vr0 + (unsigned)((ST + 2) % NS) * kTileBytes);
-      if (j < ntiles && active(j)) {
-        softmax(j);
-      } else {
-#pragma unroll
-        for (int i = 0; i < 4; ++i) pk[i] = u32x4{0u, 0u, 0u, 0u};
-      }
-      id_v = id_k;
-      barrier_nowait<false>();
+      l_run += (ls[0] + ls[1]) + (ls[2] + ls[3]);
     };
 
-    if (grp == 1) barrier_nowait<false>();
-    for (int j = kt0; j <= ntiles; j += NS) {
-      step(std::integral_constant<int, 0>{}, j);
-      if (j + 1 <= ntiles) step(std::integral_constant<int, 1>{}, j + 1);
-      if (j + 2 <= ntiles) step(std::integral_constant<int, 2>{}, j + 2);
-      if (j + 3 <= ntiles) step(std::integral_constant<int, 3>{}, j + 3);
-    }
-    if (grp == 0) barrier_nowait<false>();
-  }
+    if (ntiles > kt0) {
+      // the first M phase multiplies zero probabilities with V operand stage
+      // NO-1: clear it, so stale LDS contents cannot turn 0 * V into NaN
+      for (int i = threadIdx.x; i < L::kPos; i += kPPThreads)
+        Vr[(NO - 1) * L::kPos + i] = u32x4{0u, 0u, 0u, 0u};
+      wait_vmcnt<0>();
+      if constexpr (KVB == 2) {
+        fix_v(kt0, Vr);
+        if (kt0 + 1 < ntiles) fix_v(kt0 + 1, Vr + L::kPos);
+      } else {
+        widen(K8, Kr, kt0, false);   // K(kt0); K(kt0 + 1) and V(kt0) in M(kt0)
+      }
+      barrier_nowait<true>();
 
-  // ---- normalise and store: lane holds O[qi][32 t + 8 j + 4 half + i] ----
-  const float lt = pair32_sum_swap(l_run);
-  if (!q_ok) return;
-  const float inv = (lt > 0.f) ? p.v_scale / lt : 0.f;
-  unsigned short* orow = static_cast<unsigned short*>(p.out) +
-                         (int64_t)(q_first + qi) * p.out_row_stride + (int64_t)qh * D;
+      auto step = [&](auto st_c, int j) __attribute__((always_inline)) {
+        constexpr int ST = decltype(st_c)::value;
+        const u32x4* Kt = Kr + (ST % NO) * L::kPos;
+        const u32x4* Vt = Vr + ((ST + NO - 1) % NO) * L::kPos;
+        // ---- M(j) ----
+        // one straight MFMA path (branches around MFMAs cost accumulator
+        // copies): a tile the wave does not need still runs, with zero
+        // probabilities (P of the first tile, of tiles past the wave's queries
+        // or before its window); its scores are discarded
+        mphase(Kt, Vt);
+        // retire the copies of V(j-2) (those of V(j-1) may stay in flight)
+        if (j - 1 >= kt0 && j + 2 < ntiles) wait_vmcnt<2 * IPW>();
+        else if (j - 1 >= kt0 && j + 1 < ntiles) wait_vmcnt<IPW>();
+        else wait_vmcnt<0>();
+        if constexpr (KVB == 2) {
+          if (j >= kt0 + 2 && j < ntiles) fix_v(j, Vr + ST * L::kPos);
+        } else {
+          // operand stages of K(j+1) and V(j): their previous tiles, K(j-1) and
+          // V(j-2), were last read in M(j-1), which every wave has finished
+          if (j + 1 < ntiles) widen(K8 + ((ST + 1) % NS) * kPos8, Kr + ((ST + 1) % NO) * L::kPos, j + 1, false);
+          if (j < ntiles) widen(V8 + ST * kPos8, Vr + (ST % NO) * L::kPos, j, true);
+        }
+        barrier_nowait<true>();
+        // ---- V(j) ----
+        const int id_k = copy_id(raw_n, j + 3);
+        raw_n = raw_id(j + 4);
+        if (j + 3 < ntiles) copy_tile(kbase, koff, id_k, kr0 + (unsigned)((ST + 3) % NS) * kTileBytes);
+        if (j + 2 < ntiles) copy_tile(vbase, voff, id_v, vr0 + (unsigned)((ST + 2) % NS) * kTileBytes);
+        if (j < ntiles && active(j)) {
+          softmax(j);
+        } else {
 #pragma unroll
-  for (int t = 0; t < DT; ++t) {
+          for (int i = 0; i < 4; ++i) pk[i] = u32x4{0u, 0u, 0u, 0u};
+        }
+        id_v = id_k;
+        barrier_nowait<false>();
+      };
+
+      if (grp == 1) barrier_nowait<false>();
+      for (int j = kt0; j <= ntiles; j += NS) {
+        step(std::integral_constant<int, 0>{}, j);
+        if (j + 1 <= ntiles) step(std::integral_constant<int, 1>{}, j + 1);
+        if (j + 2 <= ntiles) step(std::integral_constant<int, 2>{}, j + 2);
+        if (j + 3 <= ntiles) step(std::integral_constant<int, 3>{}, j + 3);
+      }
+      if (grp == 0) barrier_nowait<false>();
+    }
+
+    // ---- normalise and store: lane holds O[qi][32 t + 8 j + 4 half + i] ----
+    const float lt = pair32_sum_swap(l_run);
+    if (q_ok) {
+      const CParams* pe = params();
+      const float inv = (lt > 0.f) ? pe->v_scale / lt : 0.f;
+      unsigned short* orow = static_cast<unsigned short*>(pe->out) +
+                             (int64_t)(q_first + qi) * pe->out_row_stride + (int64_t)qh * D;
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      const int d = 32 * t + 8 * j + 4 * half;
-      u32x2 w{pack2<CT>(acc[t][4 * j] * inv, acc[t][4 * j + 1] * inv),
-              pack2<CT>(acc[t][4 * j + 2] * inv, acc[t][4 * j + 3] * inv)};
-      st8(orow + d, w);
+      for (int t = 0; t < DT; ++t) {
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          const int d = 32 * t + 8 * j + 4 * half;
+          u32x2 w{pack2<CT>(acc[t][4 * j] * inv, acc[t][4 * j + 1] * inv),
+                  pack2<CT>(acc[t][4 * j + 2] * inv, acc[t][4 * j + 3] * inv)};
+          st8(orow + d, w);
+        }
+      }
     }
   }
+}
+
+// Compute units of the current device (256 on MI355X when the query fails).
+int compute_units() {
+  int dev = 0, cus = 0;
+  if (hipGetDevice(&dev) != hipSuccess ||
+      hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus <= 0) {
+    (void)hipGetLastError();
+    cus = 256;
+  }
+  return cus;
 }
 
 int heads_per_wg(int G) {
@@ -630,12 +726,20 @@ hipError_t launch_typed(const AttnParams& p, hipStream_t stream) {
   const int QB = 32 * kPPWaves / hpw;
   const int qtiles = (p.max_query_len + QB - 1) / QB;
   if (qtiles == 0) return hipSuccess;
-  // x: query-head group, y: request, z: tile counted from the end of the request
-  dim3 grid((unsigned)(p.num_q_heads / hpw), (unsigned)p.num_reqs, (unsigned)qtiles);
+  // one workgroup per compute unit (a multiple of the head-group count when
+  // there are no more head groups than units), no more than there can be items
+  const int nhg = p.num_q_heads / hpw;
+  const int cus = compute_units();
+  int wgs = nhg <= cus ? cus / nhg * nhg : cus;
+  const int64_t max_items = (int64_t)nhg * p.num_reqs * qtiles;
+  if (max_items < wgs) wgs = (int)max_items;
+  dim3 grid((unsigned)wgs);
+  AttnParams pk = p;
+  pk.heads_per_wg = hpw;
   if (p.masked) {
-    hipLaunchKernelGGL((prefill_pp_kernel<D, CT, KVB, I8, true>), grid, dim3(kPPThreads), 0, stream, p, hpw);
+    hipLaunchKernelGGL((prefill_pp_kernel<D, CT, KVB, I8, true>), grid, dim3(kPPThreads), 0, stream, pk);
   } else {
-    hipLaunchKernelGGL((prefill_pp_kernel<D, CT, KVB, I8, false>), grid, dim3(kPPThreads), 0, stream, p, hpw);
+    hipLaunchKernelGGL((prefill_pp_kernel<D, CT, KVB, I8, false>), grid, dim3(kPPThreads), 0, stream, pk);
   }
   return hipGetLastError();
 }
