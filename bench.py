@@ -445,6 +445,8 @@ def main():
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--config", default="chunked_prefill_mix")
+    ap.add_argument("--cache", choices=["act", "fp8_e4m3", "int8"], default=None,
+                    help="run the headline workload over this cache format instead of its own")
     ap.add_argument("--iters", type=int, default=50, help="timed runs per call in configs/extra")
     ap.add_argument("--warm-calls", type=int, default=10, help="untimed runs per call first")
     ap.add_argument("--cpu-budget", type=float, default=12.0,
@@ -476,6 +478,8 @@ def main():
 
     # ---- headline: the whole step, K timed steps ----
     wl = S.CONFIGS[args.config]()
+    if args.cache is not None:
+        wl = S.with_cache(wl, args.cache)
     t = S.make_tensors(wl, "cuda", poison=False)
     cpu_req = cpu_sample(wl, budget_units=1000000)
     snap = None if args.no_cpu else take_snapshot(wl, t, cpu_req[0] + cpu_req[1])
