@@ -182,10 +182,10 @@ def test_small_mixed_parity(hq, hkv, d, act, kind):
 
 @pytest.mark.parametrize("case", ["equal_lengths", "many_requests"])
 def test_prefill_dispatch_order_parity(case):
-    """The prefill takes up to 64 requests longest first, equal lengths tile by
-    tile: a group of six requests of one sequence length with 1 to 300 new
-    tokens (so their tile counts differ) and a pair of another length; past 64
-    requests the launch order is kept (70 small prefills)."""
+    """The prefill's work lists rank requests longest first within each run of
+    64 (ties by index): a group of six requests of one sequence length with 1 to
+    300 new tokens (so their tile counts differ) and a pair of another length;
+    70 small prefills take two runs of the per-wave request cursor."""
     if case == "equal_lengths":
         prefills = [(0, 300), (100, 200), (50, 120), (200, 100), (0, 300), (250, 50), (50, 120),
                     (299, 1)]
@@ -194,6 +194,15 @@ def test_prefill_dispatch_order_parity(case):
         rng = np.random.default_rng(92)
         prefills = [(int(c), int(n)) for c, n in zip(rng.integers(0, 80, 70), rng.integers(1, 90, 70))]
         wl = S.random_batch(92, [33], prefills, hq=8, hkv=2, d=64, act=torch.float16)
+    _run_and_check(wl)
+
+
+def test_prefill_unpinned_schedule_parity():
+    """More head groups than compute units (320 query heads, one per K/V head):
+    the grid is no multiple of the head-group count, so every workgroup takes
+    items of every head group from one shared list instead of keeping one group."""
+    wl = S.random_batch(93, [20], [(0, 150), (40, 90), (300, 33), (0, 1)], hq=320, hkv=320, d=64,
+                        act=torch.float16)
     _run_and_check(wl)
 
 
