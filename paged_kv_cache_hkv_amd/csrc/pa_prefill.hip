@@ -152,8 +152,8 @@ __device__ inline u32x2 lds_read_tr16(const u32x4* base, int pos16, int byte_off
 // rows of one block of every tile, so it needs one table entry per tile: a
 // scalar load issued one V phase ahead of its use (no vector load the
 // compiler would wait for behind the copies in flight).  The workgroup checks
-// its table entries once up front; only rows holding ids outside the pool
-// test block presence per tile.
+// the table entries of an item once, when the item starts; only rows holding
+// ids outside the pool test block presence per tile.
 // 8-bit caches: the copies fill rings of 8-bit tiles in plain [key][chunk]
 // order (one instruction per wave per tile: 1 KB at head_dim 128, 512 bytes
 // from the lower 32 lanes at head_dim 64), and at the end of M(j)
@@ -163,7 +163,9 @@ __device__ inline u32x2 lds_read_tr16(const u32x4* base, int pos16, int byte_off
 // stages suffice: K(j+1) and V(j) replace K(j-1) and V(j-2), whose last
 // reads were in M(j-1), and the other group is in its softmax phase.  The
 // widening (one 16-byte LDS read, 8 converts, two 16-byte writes per lane
-// and tensor) runs in the MFMA phase, off the critical softmax path.
+// and tensor) has to run in the MFMA phase: a wave can wait only for its own
+// copies, and every row of K(j+1) and V(j) must be widened before the first
+// group's M(j+1).
 constexpr int kPPWaves = 8;
 constexpr int kPPThreads = 64 * kPPWaves;
 constexpr int kPPStages = 4;
