@@ -356,10 +356,14 @@ pa_status pa_decode_workspace_size(const pa_attn_desc* desc, int32_t num_reqs,
  * query i (row qsl[r] + i) attends keys 0 .. c + i (bottom-right causal: the
  * new token sees the whole cached prefix and itself, never a later token).
  * max_query_len and max_seq_len (host scalars, as the tour's metadata keeps
- * them on the CPU) must bound every n and seq_len of the range; rows past
- * max_query_len are not computed; max_seq_len above 2^30 returns
- * PA_ERR_UNSUPPORTED.  Output rows of other requests and padding
- * rows are never written.  Accumulation float32; out act_dtype.
+ * them on the CPU) must bound every n and seq_len of the range: max_query_len
+ * sizes the launch (the kernel takes each request's length from
+ * query_start_loc; max_query_len 0 computes nothing) and max_seq_len caps the
+ * keys read; max_seq_len above 2^30 returns PA_ERR_UNSUPPORTED.  Output rows
+ * of other requests and padding rows are never written.  Accumulation
+ * float32; out act_dtype.  Results do not depend on the order in which the
+ * work is spread over the device (each output row is computed by one wave
+ * along one fixed key order).
  */
 pa_status pa_prefill_varlen(const pa_attn_desc* desc, int32_t req_begin, int32_t req_end,
                             const void* q, int64_t q_row_stride,
