@@ -295,23 +295,28 @@ __global__ __launch_bounds__(kPPThreads) void prefill_pp_kernel(AttnParams p) {
   cur_sc[wave][2] = 0;
   cur_sc[wave][3] = 0;
 
-  for (;;) {
-    const CParams* pp = params();
-    const int hpw = pp->heads_per_wg;
-    const int QB = (32 * kPPWaves) / hpw;   // queries per item
-    const int nhg = pp->num_q_heads / hpw;  // head groups
+  // the first block-table entries of an item, read while the item before it
+  // starts (tag = the item's number, then this wave's entries of its first
+  // four tiles), so an item issues its first copies without a round trip
+  __shared__ int pre_ids[kPPWaves][5];
+  pre_ids[wave][0] = -1;
+
+  struct ItemRec {
+    int hg, r, bz, q_first, n, s_all;
+  };
+  // item number kk of this workgroup's list (false past its end); moves the
+  // cursor forward only, so numbers must not decrease between calls
+  auto lookup = [&](int kk, const CParams* pp, int QB, int nhg, ItemRec& it) __attribute__((always_inline)) {
     const int P = (int)gridDim.x;
     const bool pinned = P % nhg == 0;
     const int C = pinned ? P / nhg : P;
     const int cw = pinned ? (int)blockIdx.x / nhg : (int)blockIdx.x;
-    const int hg_pin = pinned ? (int)blockIdx.x % nhg : 0;
-    const int k = wave_uniform(cur_sc[wave][3]);
+    const int pos = kk * C + ((kk & 1) ? C - 1 - cw : cw);
+    it.hg = pinned ? (int)blockIdx.x % nhg : pos % nhg;
+    const int tt = pinned ? pos : pos / nhg;
     int ch = wave_uniform(cur_sc[wave][0]);
     int ch_base = wave_uniform(cur_sc[wave][1]);
     int ch_total = wave_uniform(cur_sc[wave][2]);
-    const int pos = k * C + ((k & 1) ? C - 1 - cw : cw);
-    const int hg = pinned ? hg_pin : pos % nhg;
-    const int tt = pinned ? pos : pos / nhg;
     bool found = true;
     while (ch < 0 || tt >= ch_base + ch_total) {
       if (ch >= 0) ch_base += ch_total;
@@ -346,20 +351,32 @@ __global__ __launch_bounds__(kPPThreads) void prefill_pp_kernel(AttnParams p) {
       cur_lane[wave][4][lane] = pre;
       ch_total = tot;
     }
-    if (!found) break;
+    if (!found) return false;
     cur_sc[wave][0] = ch;
     cur_sc[wave][1] = ch_base;
     cur_sc[wave][2] = ch_total;
-    cur_sc[wave][3] = k + 1;
     const int rel = tt - ch_base;
     const int c_cnt = cur_lane[wave][3][lane], c_pre = cur_lane[wave][4][lane];
     const bool mine = c_cnt > 0 && rel >= c_pre && rel < c_pre + c_cnt;
     const int sel = (int)__builtin_ctzll(__ballot(mine));
-    const int r = pp->req_begin + ch * 64 + sel;
-    const int bz = rel - wave_uniform(cur_lane[wave][4][sel]);   // tile, counted from the request's end
-    const int q_first = wave_uniform(cur_lane[wave][0][sel]);
-    const int n = wave_uniform(cur_lane[wave][1][sel]);
-    const int s_all = wave_uniform(cur_lane[wave][2][sel]);
+    it.r = pp->req_begin + ch * 64 + sel;
+    it.bz = rel - wave_uniform(cur_lane[wave][4][sel]);   // tile, counted from the request's end
+    it.q_first = wave_uniform(cur_lane[wave][0][sel]);
+    it.n = wave_uniform(cur_lane[wave][1][sel]);
+    it.s_all = wave_uniform(cur_lane[wave][2][sel]);
+    return true;
+  };
+
+  for (;;) {
+    const CParams* pp = params();
+    const int hpw = pp->heads_per_wg;
+    const int QB = (32 * kPPWaves) / hpw;   // queries per item
+    const int nhg = pp->num_q_heads / hpw;  // head groups
+    const int k = wave_uniform(cur_sc[wave][3]);
+    ItemRec it;
+    if (!lookup(k, pp, QB, nhg, it)) break;
+    cur_sc[wave][3] = k + 1;
+    const int hg = it.hg, r = it.r, bz = it.bz, q_first = it.q_first, n = it.n, s_all = it.s_all;
 
     const int q_hi = n - bz * QB;      // the item covers queries [q_hi - QB, q_hi)
     const int c = s_all - n;
@@ -417,10 +434,14 @@ __global__ __launch_bounds__(kPPThreads) void prefill_pp_kernel(AttnParams p) {
     // overlap; the loads' wait below covers the copies as well.
     int raw_n = 0, id_v = 0;
     if (ntiles > kt0) {
-      const int id0 = copy_id(raw_id(kt0), kt0);
-      const int id1 = copy_id(raw_id(kt0 + 1), kt0 + 1);
-      const int id2 = copy_id(raw_id(kt0 + 2), kt0 + 2);
-      raw_n = raw_id(kt0 + 3);      // tile j+3's entry, checked in V(j)
+      const bool pre = wave_uniform(pre_ids[wave][0]) == k;
+      const int raw0 = pre ? wave_uniform(pre_ids[wave][1]) : raw_id(kt0);
+      const int raw1 = pre ? wave_uniform(pre_ids[wave][2]) : raw_id(kt0 + 1);
+      const int raw2 = pre ? wave_uniform(pre_ids[wave][3]) : raw_id(kt0 + 2);
+      raw_n = pre ? wave_uniform(pre_ids[wave][4]) : raw_id(kt0 + 3);   // tile j+3's entry, checked in V(j)
+      const int id0 = copy_id(raw0, kt0);
+      const int id1 = copy_id(raw1, kt0 + 1);
+      const int id2 = copy_id(raw2, kt0 + 2);
       id_v = id2;                   // tile j+2's id (its V copy in V(j))
       copy_tile(kbase, koff, id0, kr0);
       copy_tile(vbase, voff, id0, vr0);
@@ -429,6 +450,27 @@ __global__ __launch_bounds__(kPPThreads) void prefill_pp_kernel(AttnParams p) {
         copy_tile(vbase, voff, id1, vr0 + kTileBytes);
       }
       if (kt0 + 2 < ntiles) copy_tile(kbase, koff, id2, kr0 + 2 * kTileBytes);
+    }
+
+    // the next item's first four block-table entries for this wave (scalar
+    // loads, in flight with the Q loads below; stored once they are retired)
+    int nraw[4] = {0, 0, 0, 0};
+    bool nxt_ok = false;
+    {
+      ItemRec nx;
+      if (lookup(k + 1, pp, QB, nhg, nx)) {
+        const int q_hi2 = nx.n - nx.bz * QB;
+        const int c2_ = nx.s_all - nx.n;
+        const int s_eff2 = min(min(nx.s_all, pp->max_seq_len), pp->max_blocks_per_req * kBlock);
+        const int nblk2 = (s_eff2 + kBlock - 1) / kBlock;
+        const int kt02 = MASK ? max(0, c2_ + max(q_hi2 - QB, 0) - pp->window_left) / kTileK : 0;
+        if (nblk2 > 0) {
+          const int32_t* bt2 = pp->block_tables + (int64_t)nx.r * pp->max_blocks_per_req;
+#pragma unroll
+          for (int u = 0; u < 4; ++u) nraw[u] = load_uniform(bt2, min(4 * (kt02 + u) + cb, nblk2 - 1));
+          nxt_ok = true;
+        }
+      }
     }
 
     // Q as the B operand of S^T = K . Q^T: B[k = 8*half + e][col = l32] = Q[qi][16 s + 8 half + e]
@@ -454,6 +496,13 @@ __global__ __launch_bounds__(kPPThreads) void prefill_pp_kernel(AttnParams p) {
     // also wait for every copy in flight
 #pragma unroll
     for (int s = 0; s < QS; ++s) asm volatile("" : : "v"(__builtin_bit_cast(u32x4, qop[s])));
+    if (nxt_ok) {
+      pre_ids[wave][1] = nraw[0];
+      pre_ids[wave][2] = nraw[1];
+      pre_ids[wave][3] = nraw[2];
+      pre_ids[wave][4] = nraw[3];
+      pre_ids[wave][0] = k + 1;
+    }
     const bool rowok = __syncthreads_and(my_ok);
     auto okmask = [&](int t) __attribute__((always_inline)) {
       return rowok ? 0xFu : tile_okmask(bt_row, nblk, nb32, t);
