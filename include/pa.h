@@ -22,7 +22,9 @@
  * - Ownership: the caller allocates every buffer (device memory unless stated
  *   otherwise) and keeps it alive until the work on `stream` has finished.
  *   The library allocates nothing, frees nothing and keeps no state between
- *   calls.  Calls are thread-safe and reentrant.
+ *   calls, except the fixed device array of pa_decode_noalloc (held per GPU
+ *   for the process's lifetime).  Calls are thread-safe and reentrant
+ *   (pa_decode_noalloc: see there).
  * - Ordering: every call only enqueues kernels on `stream` (a hipStream_t;
  *   NULL means the default stream) and returns without waiting.  It never
  *   copies device data to the host.  The write of a layer's new K/V must be
