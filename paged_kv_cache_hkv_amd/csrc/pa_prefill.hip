@@ -156,16 +156,19 @@ __device__ inline u32x2 lds_read_tr16(const u32x4* base, int pos16, int byte_off
 // ids outside the pool test block presence per tile.
 // 8-bit caches: the copies fill rings of 8-bit tiles in plain [key][chunk]
 // order (one instruction per wave per tile: 1 KB at head_dim 128, 512 bytes
-// from the lower 32 lanes at head_dim 64), and at the end of M(j)
-// each wave widens the rows it copied of K tile j+1 and V tile j into two
-// operand stages (tile t in stage t % 2, LdsTile layout, V rows of absent
-// keys zeroed); the barrier that ends M(j) publishes them.  Two operand
-// stages suffice: K(j+1) and V(j) replace K(j-1) and V(j-2), whose last
-// reads were in M(j-1), and the other group is in its softmax phase.  The
-// widening (one 16-byte LDS read, 8 converts, two 16-byte writes per lane
-// and tensor) has to run in the MFMA phase: a wave can wait only for its own
-// copies, and every row of K(j+1) and V(j) must be widened before the first
-// group's M(j+1).
+// from the lower 32 lanes at head_dim 64), and in M(j) each wave widens the
+// rows it copied of K tile j+1 and V tile j into two operand stages (tile t
+// in stage t % 2, LdsTile layout, V rows of absent keys zeroed); the barrier
+// that ends M(j) publishes them.  Two operand stages suffice: K(j+1) and V(j)
+// replace K(j-1) and V(j-2), whose last reads were in M(j-1), and the other
+// group is in its softmax phase.  The widening (one 16-byte LDS read, 8
+// converts, two 16-byte writes per lane and tensor) has to run in the MFMA
+// phase: a wave can wait only for its own copies, and every row of K(j+1) and
+// V(j) must be widened before the first group's M(j+1).  At head_dim 128 the
+// copies are retired before the MFMAs, the 8-bit rows read ahead of them and
+// converted among them, so only the two stores follow the last MFMA; at
+// head_dim 64 (a phase half as long) the rows are read and widened after the
+// MFMAs and the retiring wait.
 constexpr int kPPWaves = 8;
 constexpr int kPPThreads = 64 * kPPWaves;
 constexpr int kPPStages = 4;
@@ -219,6 +222,10 @@ __global__ __launch_bounds__(kPPThreads) void prefill_pp_kernel(AttnParams p) {
   static_assert(2 * IPW * KPI == kBlock, "two waves copy each block of a tile");
   static_assert(KVB == 2 || IPW == 1, "8-bit tiles: one copy instruction per wave");
   constexpr unsigned kTileBytes = kCopyPos * 16;
+  // 8-bit caches at head_dim 128 widen among the MFMAs of the phase (at
+  // head_dim 64 the phase is too short to cover the earlier wait for the
+  // copies: measured slower there)
+  constexpr bool kWidenInM = KVB == 1 && D == 128;
 
   __shared__ u32x4 Kr[NO * L::kPos];
   __shared__ u32x4 Vr[NO * L::kPos];
@@ -547,6 +554,27 @@ __global__ __launch_bounds__(kPPThreads) void prefill_pp_kernel(AttnParams p) {
       dst[key * L::CPR + ((2 * c8 + 1) ^ sw)] = hi;
     };
 
+    // the same widening in two parts, for the MFMA phase: the 8-bit row is read
+    // before the MFMAs, converted among them and stored after them
+    auto widen_store = [&](const u32x4 w, u32x4* dst, bool is_v, bool vz) __attribute__((always_inline)) {
+      const int pidx = wave * LPI + lane;
+      const int key = pidx / CPR8, c8 = pidx % CPR8;
+      u32x4 lo{widen8x2<CT, I8>(w[0], false), widen8x2<CT, I8>(w[0], true),
+               widen8x2<CT, I8>(w[1], false), widen8x2<CT, I8>(w[1], true)};
+      u32x4 hi{widen8x2<CT, I8>(w[2], false), widen8x2<CT, I8>(w[2], true),
+               widen8x2<CT, I8>(w[3], false), widen8x2<CT, I8>(w[3], true)};
+      const int sw = is_v ? L::swv(key) : L::swk(key);
+      if (is_v) {
+        const u32x4 z{0u, 0u, 0u, 0u};
+        lo = vz ? z : lo;
+        hi = vz ? z : hi;
+      }
+      if (copy_lane) {
+        dst[key * L::CPR + ((2 * c8) ^ sw)] = lo;
+        dst[key * L::CPR + ((2 * c8 + 1) ^ sw)] = hi;
+      }
+    };
+
     const float scale_log2 = pp->scale_log2;
     const float c2 = MASK ? 1.f : scale_log2;
     const float slope2 = (MASK && pp->alibi != nullptr)
@@ -594,12 +622,16 @@ __global__ __launch_bounds__(kPPThreads) void prefill_pp_kernel(AttnParams p) {
       constexpr int kReads = 2 * QS + 8 * DT;
       constexpr int kMfma = 2 * QS + 4 * DT;
       constexpr int kLead = 6;
+      constexpr int W8V = 2 * 24;   // widening in the phase: 2 x (16 converts + 8 packs) per lane
       constexpr int kPer = (kReads - kLead + kMfma - 1) / kMfma;
       __builtin_amdgcn_sched_group_barrier(0x100, kLead, 0);
 #pragma unroll
       for (int i = 0; i < kMfma; ++i) {
         __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
         __builtin_amdgcn_sched_group_barrier(0x100, kPer, 0);
+        if constexpr (kWidenInM) {
+          if (i >= 2 && i < 2 + W8V / 2) __builtin_amdgcn_sched_group_barrier(0x002, 2, 0);
+        }
       }
     };
 
@@ -694,18 +726,42 @@ __global__ __launch_bounds__(kPPThreads) void prefill_pp_kernel(AttnParams p) {
         // copies): a tile the wave does not need still runs, with zero
         // probabilities (P of the first tile, of tiles past the wave's queries
         // or before its window); its scores are discarded
-        mphase(Kt, Vt);
-        // retire the copies of V(j-2) (those of V(j-1) may stay in flight)
-        if (j - 1 >= kt0 && j + 2 < ntiles) wait_vmcnt<2 * IPW>();
-        else if (j - 1 >= kt0 && j + 1 < ntiles) wait_vmcnt<IPW>();
-        else wait_vmcnt<0>();
-        if constexpr (KVB == 2) {
-          if (j >= kt0 + 2 && j < ntiles) fix_v(j, Vr + ST * L::kPos);
+        if constexpr (!kWidenInM) {
+          mphase(Kt, Vt);
+          // retire the copies of V(j-2) (those of V(j-1) may stay in flight)
+          if (j - 1 >= kt0 && j + 2 < ntiles) wait_vmcnt<2 * IPW>();
+          else if (j - 1 >= kt0 && j + 1 < ntiles) wait_vmcnt<IPW>();
+          else wait_vmcnt<0>();
+          if constexpr (KVB == 2) {
+            if (j >= kt0 + 2 && j < ntiles) fix_v(j, Vr + ST * L::kPos);
+          } else {
+            // operand stages of K(j+1) and V(j): their previous tiles, K(j-1) and
+            // V(j-2), were last read in M(j-1), which every wave has finished
+            if (j + 1 < ntiles) widen(K8 + ((ST + 1) % NS) * kPos8, Kr + ((ST + 1) % NO) * L::kPos, j + 1, false);
+            if (j < ntiles) widen(V8 + ST * kPos8, Vr + (ST % NO) * L::kPos, j, true);
+          }
         } else {
-          // operand stages of K(j+1) and V(j): their previous tiles, K(j-1) and
-          // V(j-2), were last read in M(j-1), which every wave has finished
-          if (j + 1 < ntiles) widen(K8 + ((ST + 1) % NS) * kPos8, Kr + ((ST + 1) % NO) * L::kPos, j + 1, false);
-          if (j < ntiles) widen(V8 + ST * kPos8, Vr + (ST % NO) * L::kPos, j, true);
+          // retire the copies of V(j-2) first (those of V(j-1) may stay in
+          // flight): this wave's 8-bit rows of K(j+1) and V(j) are read before
+          // the MFMAs and widened among them into the operand stages of K(j+1)
+          // and V(j), whose previous tiles, K(j-1) and V(j-2), were last read
+          // in M(j-1), which every wave has finished.  Past the last tile the
+          // rows are stale and their widened copies are never read.
+          if (j - 1 >= kt0 && j + 2 < ntiles) wait_vmcnt<2 * IPW>();
+          else if (j - 1 >= kt0 && j + 1 < ntiles) wait_vmcnt<IPW>();
+          else wait_vmcnt<0>();
+          const int pidx = wave * LPI + (copy_lane ? lane : 0);
+          const u32x4 wk = K8[((ST + 1) % NS) * kPos8 + pidx];
+          const u32x4 wv = V8[ST * kPos8 + pidx];
+          bool vz = false;
+          if (!(kTileK * j + kTileK <= s_eff && rowok)) {
+            const int key = pidx / CPR8;
+            const unsigned ok = okmask(j);
+            vz = kTileK * j + key >= s_eff || !((ok >> (key / kBlock)) & 1u);
+          }
+          mphase(Kt, Vt);
+          widen_store(wk, Kr + ((ST + 1) % NO) * L::kPos, false, false);
+          widen_store(wv, Vr + (ST % NO) * L::kPos, true, vz);
         }
         barrier_nowait<true>();
         // ---- V(j) ----
