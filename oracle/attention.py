@@ -108,11 +108,13 @@ def causal_attention(q, k, v, num_computed, scale, sliding_window=0, alibi_slope
 
 
 def decode_cache(cache_bits, cache_dtype, scale=1.0):
-    """Stored cache bits -> float64 values (fp8 and int8 codes are multiplied
-    by the tensor's scale)."""
+    """Stored cache bits [..., Hkv, D] -> float64 values (fp8 and int8 codes
+    are multiplied by the tensor's scale, or by their K/V head's when ``scale``
+    is an array [Hkv])."""
     vals = codecs.decode(cache_bits, cache_dtype)
     if cache_dtype in ("fp8_e4m3", "int8"):
-        vals = vals * float(scale)
+        sc = np.asarray(scale, dtype=np.float64)
+        vals = vals * (sc[:, None] if sc.ndim == 1 else sc)
     return vals
 
 
@@ -127,6 +129,8 @@ def paged_attention(q, key_cache, value_cache, block_tables, query_start_loc, se
       raw bits when ``cache_dtype`` is given ('f16' | 'bf16' | 'fp8_e4m3' | 'int8'); raw
       bits are decoded per request, so a large pool is never widened at once.
     requests: iterable of request indices to compute (default: all).
+    k_scale/v_scale: the quantized formats' scale of the tensor, or one per
+      K/V head (array [Hkv]).
     sliding_window, alibi_slopes: the mask variants of ``causal_attention``.
     num_blocks: pool size; when given, table entries outside [0, num_blocks)
       are absent blocks (their keys are left out; K/V read as zeros).

@@ -18,6 +18,13 @@ same way: symmetric signed codes -127..127 (two's complement bytes; -128 is
 never produced), one float32 scale per tensor, a code means ``code * scale``,
 encoding ``round_to_nearest_even(saturate(float32(x) * float32(1/scale)))``
 with saturation to +-127; int8 has no NaN, and a NaN input becomes 0.
+
+Both quantized formats also take the per-K/V-head option the int8 row of the
+build names (the same reading applied per head): one float32 scale per K/V
+head of a tensor, so a code of head ``h`` means ``code * scale[h]`` and is
+encoded with ``float32(1/scale[h])``.  The encoders below multiply by
+whatever inverse scale they are given, a number or an array that broadcasts
+against the values (``[Hkv, 1]`` against ``[..., Hkv, D]``).
 """
 
 import numpy as np
@@ -68,7 +75,7 @@ _POS_VALUES = E4M3FN_TABLE[:0x7F]
 
 
 def e4m3fn_encode(x_f32, inv_scale_f32):
-    """Encode float32 values as e4m3fn codes with the per-tensor scale.
+    """Encode float32 values as e4m3fn codes with the tensor's (or each head's) scale.
 
     ``y = float32(x * inv_scale)`` (one IEEE float32 multiply), then ``y`` is
     clamped to [-448, 448] (saturation; 448 is representable, so clamping first
@@ -82,7 +89,7 @@ def e4m3fn_encode(x_f32, inv_scale_f32):
     """
     x = np.asarray(x_f32, dtype=np.float32)
     with np.errstate(over="ignore", invalid="ignore"):
-        y = (x * np.float32(inv_scale_f32)).astype(np.float32)   # float32 multiply
+        y = (x * np.asarray(inv_scale_f32, dtype=np.float32)).astype(np.float32)   # float32 multiply
     neg = np.signbit(y)
     nan = np.isnan(y)
     mag = np.abs(y.astype(np.float64))
@@ -112,7 +119,7 @@ INT8_MAX = 127
 
 
 def int8_encode(x_f32, inv_scale_f32):
-    """Encode float32 values as symmetric int8 codes with the per-tensor scale.
+    """Encode float32 values as symmetric int8 codes with the tensor's (or each head's) scale.
 
     ``y = float32(x * inv_scale)`` (one IEEE float32 multiply); NaN gives 0;
     ``y`` is clamped to [-127, 127] (127 is an integer, so clamping first and
@@ -122,7 +129,7 @@ def int8_encode(x_f32, inv_scale_f32):
     """
     x = np.asarray(x_f32, dtype=np.float32)
     with np.errstate(over="ignore", invalid="ignore"):
-        y = (x * np.float32(inv_scale_f32)).astype(np.float32)   # float32 multiply
+        y = (x * np.asarray(inv_scale_f32, dtype=np.float32)).astype(np.float32)   # float32 multiply
     y = y.astype(np.float64)
     nan = np.isnan(y)
     y = np.where(nan, 0.0, np.clip(y, -INT8_MAX, INT8_MAX))
