@@ -100,6 +100,16 @@ typedef enum pa_dtype {
  * never written) and stores 0 for NaN.  KV-cache int8 is the quantization the
  * "vLLM 推理全流程深度解析" PagedAttention section names as a throughput lever.
  *
+ * k_scales / v_scales (optional, quantized caches only; PA_ERR_INVALID_ARG
+ * with a 16-bit cache or a pointer not 4-byte aligned): device float32
+ * [num_kv_heads], one scale per K/V head in place of k_scale / v_scale (either
+ * may be set alone).  A code of head h means c * scales[h]; the write paths
+ * encode head h with the IEEE float32 reciprocal 1.0f / scales[h], computed on
+ * the device (correctly rounded, so the same value the host would compute).
+ * Each value must be finite and > 0; the library reads them on the device and
+ * does not check them.  The arrays stay owned by the caller and must live
+ * until the calls that use this descriptor have finished.
+ *
  * decode_workers: number of waves pa_decode divides its key stream among
  * (see pa_decode); 0 lets the library choose (per compute unit of the
  * current device: four for 16-bit caches, eight for 8-bit ones).  Otherwise
@@ -135,6 +145,8 @@ typedef struct pa_attn_desc {
   int32_t decode_workers;
   int32_t sliding_window;     /* 0: none; W > 0: see below */
   const float* alibi_slopes;  /* NULL: none; else device float32 [num_q_heads] */
+  const float* k_scales;      /* NULL: k_scale; else device float32 [num_kv_heads] */
+  const float* v_scales;      /* NULL: v_scale; else device float32 [num_kv_heads] */
 } pa_attn_desc;
 
 /* Human-readable name of a status code (static storage). */

@@ -41,22 +41,28 @@ class AttnDesc(ctypes.Structure):
         ("decode_workers", ctypes.c_int32),
         ("sliding_window", ctypes.c_int32),
         ("alibi_slopes", ctypes.c_void_p),
+        ("k_scales", ctypes.c_void_p),
+        ("v_scales", ctypes.c_void_p),
     ]
 
 
 def make_desc(num_q_heads, num_kv_heads, head_dim, block_size=16, act_dtype=PA_BF16,
               cache_dtype=None, softmax_scale=None, k_scale=1.0, v_scale=1.0,
-              decode_workers=0, sliding_window=0, alibi_slopes=None):
-    """alibi_slopes: float32 device tensor [num_q_heads] or None; the descriptor
-    keeps a reference so the memory outlives it."""
+              decode_workers=0, sliding_window=0, alibi_slopes=None, k_scales=None,
+              v_scales=None):
+    """alibi_slopes: float32 device tensor [num_q_heads] or None; k_scales /
+    v_scales: float32 device tensors [num_kv_heads] (per-head scales of a
+    quantized cache) or None.  The descriptor keeps references so the memory
+    outlives it."""
     if cache_dtype is None:
         cache_dtype = act_dtype
     if softmax_scale is None:
         softmax_scale = head_dim ** -0.5
+    ptr = lambda t: None if t is None else t.data_ptr()
     d = AttnDesc(num_q_heads, num_kv_heads, head_dim, block_size, act_dtype, cache_dtype,
                  softmax_scale, k_scale, v_scale, decode_workers, sliding_window,
-                 None if alibi_slopes is None else alibi_slopes.data_ptr())
-    d._alibi_ref = alibi_slopes
+                 ptr(alibi_slopes), ptr(k_scales), ptr(v_scales))
+    d._refs = (alibi_slopes, k_scales, v_scales)
     return d
 
 

@@ -56,6 +56,13 @@ pa_status check_desc(const pa_attn_desc* d) {
   if (d->decode_workers < 0 || d->decode_workers > pa::kMaxDecodeWorkers) return PA_ERR_INVALID_ARG;
   if (d->sliding_window < 0) return PA_ERR_INVALID_ARG;
   if ((reinterpret_cast<uintptr_t>(d->alibi_slopes) & 3u) != 0) return PA_ERR_INVALID_ARG;
+  // per-head scales: quantized caches only, float32-aligned
+  if ((d->k_scales != nullptr || d->v_scales != nullptr) && !quantized(d->cache_dtype)) {
+    return PA_ERR_INVALID_ARG;
+  }
+  if (((reinterpret_cast<uintptr_t>(d->k_scales) | reinterpret_cast<uintptr_t>(d->v_scales)) & 3u) != 0) {
+    return PA_ERR_INVALID_ARG;
+  }
   return PA_OK;
 }
 
@@ -138,8 +145,10 @@ bool device_address(const void* ptr, const void** out) {
   return false;
 }
 
+// The score scale in log2 units; with per-head K scales the kernels multiply
+// it by the head's scale.
 float scale_log2(const pa_attn_desc* d) {
-  const float ks = quantized(d->cache_dtype) ? d->k_scale : 1.0f;
+  const float ks = (quantized(d->cache_dtype) && d->k_scales == nullptr) ? d->k_scale : 1.0f;
   return d->softmax_scale * ks * kLog2e;
 }
 
@@ -223,6 +232,9 @@ pa_status pa_cache_write(const pa_attn_desc* desc, int64_t num_tokens, const voi
   p.num_slots = num_blocks * desc->block_size;
   p.k_inv_scale = quantized(desc->cache_dtype) ? 1.0f / desc->k_scale : 1.0f;
   p.v_inv_scale = quantized(desc->cache_dtype) ? 1.0f / desc->v_scale : 1.0f;
+  p.k_scales = desc->k_scales;
+  p.v_scales = desc->v_scales;
+  p.head_dim = desc->head_dim;
   return from_hip(pa::launch_cache_write(p, desc->act_dtype, desc->cache_dtype,
                                          static_cast<hipStream_t>(stream)));
 }
@@ -284,6 +296,8 @@ pa_status pa_rope_cache_write(const pa_attn_desc* desc, int64_t num_tokens,
   p.num_slots = num_blocks * desc->block_size;
   p.k_inv_scale = quantized(desc->cache_dtype) ? 1.0f / desc->k_scale : 1.0f;
   p.v_inv_scale = quantized(desc->cache_dtype) ? 1.0f / desc->v_scale : 1.0f;
+  p.k_scales = desc->k_scales;
+  p.v_scales = desc->v_scales;
   return from_hip(pa::launch_rope_cache_write(p, desc->act_dtype, desc->cache_dtype,
                                               static_cast<hipStream_t>(stream)));
 }
@@ -375,6 +389,8 @@ static pa::AttnParams make_params(const pa_attn_desc* desc, int32_t req_begin, i
   p.out_row_stride = out_row_stride;
   p.scale_log2 = scale_log2(desc);
   p.v_scale = quantized(desc->cache_dtype) ? desc->v_scale : 1.0f;
+  p.k_scales = desc->k_scales;
+  p.v_scales = desc->v_scales;
   p.window_left = (desc->sliding_window > 0 && desc->sliding_window - 1 < pa::kNoWindow)
                       ? desc->sliding_window - 1
                       : pa::kNoWindow;

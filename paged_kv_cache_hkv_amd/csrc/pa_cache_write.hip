@@ -61,7 +61,10 @@ __global__ __launch_bounds__(kThreads) void cache_write_kernel(CacheWriteParams 
   const int64_t dst_elem = slot * p.row_elems + (int64_t)c * 8;
   if constexpr (ENC != 0) {
     unsigned char* dst = static_cast<unsigned char*>(is_v ? p.value_cache : p.key_cache);
-    st8(dst + dst_elem, encode8<T, ENC>(v, is_v ? p.v_inv_scale : p.k_inv_scale));
+    float inv = is_v ? p.v_inv_scale : p.k_inv_scale;
+    const float* hs = is_v ? p.v_scales : p.k_scales;
+    if (hs != nullptr) inv = 1.0f / hs[(c * 8) / p.head_dim];   // IEEE division: the host's reciprocal
+    st8(dst + dst_elem, encode8<T, ENC>(v, inv));
   } else {
     unsigned short* dst = static_cast<unsigned short*>(is_v ? p.value_cache : p.key_cache);
     st16(dst + dst_elem, v);

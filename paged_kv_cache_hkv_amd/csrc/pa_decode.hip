@@ -132,6 +132,29 @@ __device__ inline u32x2 lds_read_tr16(const unsigned char* p) {
 
 // First key a decode row of s keys may see (its position is s - 1), and the
 // first block holding one: 0 without a sliding window.
+// The kernel's parameter block in the kernarg segment, read through a pointer
+// the compiler cannot see through: a field used only where a segment starts
+// or ends is loaded there instead of being held in scalar registers through
+// the stream.
+typedef __attribute__((address_space(4))) const AttnParams CAttnParams;
+__device__ inline const CAttnParams* kernarg_params() {
+  const CAttnParams* q = (const CAttnParams*)__builtin_amdgcn_kernarg_segment_ptr();
+  asm volatile("" : "+s"(q));
+  return q;
+}
+
+// V scale of K/V head kvh: the tensor's, or the head's own (per-head scales
+// exist for 8-bit caches only)
+template <int KVB>
+__device__ inline float v_scale_of(const AttnParams& p, int kvh) {
+  if constexpr (KVB == 1) {
+    const CAttnParams* kp = kernarg_params();
+    return kp->v_scales != nullptr ? head_scale(kp->v_scales, kvh) : kp->v_scale;
+  } else {
+    return p.v_scale;
+  }
+}
+
 __device__ inline int first_key(const AttnParams& p, int s) { return max(0, s - 1 - p.window_left); }
 __device__ inline int first_block(const AttnParams& p, int s) { return first_key(p, s) / kBlock; }
 
@@ -410,7 +433,7 @@ __global__ __launch_bounds__(64 * WV) void decode_kernel(AttnParams p) {
 
   while (can_issue(S - 1)) issue_one();
 
-  const float c2 = p.scale_log2;
+  float c2 = p.scale_log2;   // per segment with per-head K scales
   vec8 qop[HT][KS];
   float slope2[HT];     // ALiBi slope of this lane's head, in log2 units
   int seg = 0;          // segments this worker has finished
@@ -425,6 +448,10 @@ __global__ __launch_bounds__(64 * WV) void decode_kernel(AttnParams p) {
     // ---- segment start: query operands, fresh softmax state ----
     if (cur.b == 0 || i == 0) {
       seg_b0 = cur.b;
+      if constexpr (KVB == 1) {
+        const CAttnParams* kp = kernarg_params();
+        if (kp->k_scales != nullptr) c2 = kp->scale_log2 * head_scale(kp->k_scales, cur.kvh);
+      }
 #pragma unroll
       for (int ht = 0; ht < HT; ++ht) {
         const int hig = ht * 16 + c16;
@@ -571,6 +598,7 @@ __global__ __launch_bounds__(64 * WV) void decode_kernel(AttnParams p) {
     if (cur.b == cur.nb - 1 || i == n - 1) {
       const bool whole = seg_b0 == 0 && cur.b == cur.nb - 1;
       if (whole) {
+        const float vsc = v_scale_of<KVB>(p, cur.kvh);
 #pragma unroll
         for (int ht = 0; ht < HT; ++ht) {
           float lt = l_run[ht];
@@ -578,7 +606,7 @@ __global__ __launch_bounds__(64 * WV) void decode_kernel(AttnParams p) {
           lt += shfl_xor(lt, 32);
           const int hig = ht * 16 + c16;
           if (hig < G) {
-            const float inv = (lt > 0.f) ? p.v_scale / lt : 0.f;
+            const float inv = (lt > 0.f) ? vsc / lt : 0.f;
             unsigned short* orow = static_cast<unsigned short*>(p.out) +
                                    (int64_t)cur.q_row * p.out_row_stride +
                                    (int64_t)(cur.kvh * G + hig) * D;
@@ -752,7 +780,7 @@ __global__ __launch_bounds__(64 * WV) void decode_kernel(AttnParams p) {
         A += wgt * fv;
       }
       if (complete) {
-        const float inv = (L > 0.f) ? p.v_scale / L : 0.f;
+        const float inv = (L > 0.f) ? v_scale_of<KVB>(p, kvh) / L : 0.f;
         unsigned short* orow = static_cast<unsigned short*>(p.out) + (int64_t)q_row * p.out_row_stride +
                                (int64_t)kvh * G * D + e;
         st8(orow, u32x2{pack2<CT>(A[0] * inv, A[1] * inv), pack2<CT>(A[2] * inv, A[3] * inv)});
@@ -893,7 +921,7 @@ __global__ __launch_bounds__(64) void decode_reduce_kernel(AttnParams p) {
         for (int e = 0; e < DPL; ++e) o[e] += wj[u] * v[u][e];
     }
   }
-  const float inv = (lsum > 0.f) ? p.v_scale / lsum : 0.f;
+  const float inv = (lsum > 0.f) ? v_scale_of<1>(p, kvh) / lsum : 0.f;
   const int q_row = load_uniform(p.qsl, p.req_begin + rr);
   unsigned short* orow = static_cast<unsigned short*>(p.out) + (int64_t)q_row * p.out_row_stride +
                          (int64_t)qh * D;

@@ -191,6 +191,13 @@ __device__ inline int32_t load_uniform(const int32_t* table, int64_t idx) {
   return p[idx];
 }
 
+// Per-K/V-head scale h of a quantized cache (a scalar load of a wave-uniform
+// entry, so it never waits for vector loads or LDS transfers in flight).
+__device__ inline float head_scale(const float* scales, int h) {
+  return __builtin_bit_cast(float, load_uniform(reinterpret_cast<const int32_t*>(scales),
+                                                __builtin_amdgcn_readfirstlane(h)));
+}
+
 // Byte offset of an LDS location (the M0 / ds address of a __shared__ pointer).
 __device__ inline unsigned lds_offset(const void* p) {
   typedef __attribute__((address_space(3))) const void lds_cvoid;

@@ -32,7 +32,12 @@ struct CacheWriteParams {
   void* key_cache;
   void* value_cache;
   int64_t num_slots;       // num_blocks * block_size
-  float k_inv_scale, v_inv_scale;  // fp8 only
+  float k_inv_scale, v_inv_scale;  // 8-bit caches only
+  // per K/V head scales (8-bit caches; null: the inverse scales above): head
+  // h is encoded with 1.0f / scales[h]
+  const float* k_scales;
+  const float* v_scales;
+  int32_t head_dim;
 };
 
 struct RopeParams {
@@ -51,7 +56,9 @@ struct RopeParams {
   void* key_cache;
   void* value_cache;
   int64_t num_slots;
-  float k_inv_scale, v_inv_scale;  // fp8 only
+  float k_inv_scale, v_inv_scale;  // 8-bit caches only
+  const float* k_scales;           // per K/V head scales, as in CacheWriteParams
+  const float* v_scales;
 };
 
 struct CopyBlocksParams {
@@ -86,8 +93,13 @@ struct AttnParams {
   void* out;
   int64_t out_row_stride;
   // scalars
-  float scale_log2;   // softmax_scale * k_scale * log2(e)
-  float v_scale;      // 1 unless the cache is fp8
+  float scale_log2;   // softmax_scale * k_scale * log2(e) (without k_scale when k_scales is set)
+  float v_scale;      // 1 unless the cache is quantized
+  // per K/V head scales of a quantized cache (null: k_scale / v_scale): the
+  // kernels multiply scale_log2 by k_scales[kv head] and use v_scales[kv head]
+  // in place of v_scale
+  const float* k_scales;
+  const float* v_scales;
   // mask variants: keys j < p - window_left are masked for the query at
   // position p (kNoWindow when there is no window); alibi (may be null):
   // per query head slope of the bias slope * (j - p) on the scaled score

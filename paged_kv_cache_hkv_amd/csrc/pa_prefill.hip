@@ -575,7 +575,10 @@ __global__ __launch_bounds__(kPPThreads) void prefill_pp_kernel(AttnParams p) {
       }
     };
 
-    const float scale_log2 = pp->scale_log2;
+    // per-head K scales exist for 8-bit caches only (the 16-bit kernels never read them)
+    const float scale_log2 = (KVB == 1 && pp->k_scales != nullptr)
+                                 ? pp->scale_log2 * head_scale(pp->k_scales, kvh)
+                                 : pp->scale_log2;
     const float c2 = MASK ? 1.f : scale_log2;
     const float slope2 = (MASK && pp->alibi != nullptr)
                              ? __builtin_bit_cast(float, load_uniform(reinterpret_cast<const int32_t*>(pp->alibi), qh)) * kLog2e
@@ -793,7 +796,11 @@ __global__ __launch_bounds__(kPPThreads) void prefill_pp_kernel(AttnParams p) {
     const float lt = pair32_sum_swap(l_run);
     if (q_ok) {
       const CParams* pe = params();
-      const float inv = (lt > 0.f) ? pe->v_scale / lt : 0.f;
+      // (the K/V head from the re-read parameters: no value of the item's
+      // start stays live through the tile loop for this)
+      const float vsc = (KVB == 1 && pe->v_scales != nullptr) ? head_scale(pe->v_scales, qh / pe->group)
+                                                              : pe->v_scale;
+      const float inv = (lt > 0.f) ? vsc / lt : 0.f;
       unsigned short* orow = static_cast<unsigned short*>(pe->out) +
                              (int64_t)(q_first + qi) * pe->out_row_stride + (int64_t)qh * D;
 #pragma unroll

@@ -90,6 +90,15 @@ __device__ inline u32x2 encode8(const u32x4& v, float inv) {
   return u32x2{out[0], out[1]};
 }
 
+// The inverse scale K/V head h is encoded with: the tensor's, or with
+// per-head scales the IEEE float32 reciprocal of the head's (the value the
+// host computes for a tensor scale)
+template <int ENC>
+__device__ inline float head_inv(const float* scales, int h, float tensor_inv) {
+  if constexpr (ENC == 0) return tensor_inv;
+  return scales != nullptr ? 1.0f / scales[h] : tensor_inv;
+}
+
 // ENC: 0 copy (cache in the activation dtype), 1 fp8 e4m3fn, 2 int8
 template <typename T, int ENC>
 __device__ inline void store_chunk(void* cache, int64_t elem, const u32x4& v, float inv) {
@@ -158,8 +167,9 @@ __global__ __launch_bounds__(kThreads) void rope_cache_write_kernel(RopeParams p
       st16(base + eb, yb);
     } else {
       const int64_t dst = slot * row + (int64_t)h * D;
-      store_chunk<T, ENC>(p.key_cache, dst + ea, ya, p.k_inv_scale);
-      store_chunk<T, ENC>(p.key_cache, dst + eb, yb, p.k_inv_scale);
+      const float inv = head_inv<ENC>(p.k_scales, h, p.k_inv_scale);
+      store_chunk<T, ENC>(p.key_cache, dst + ea, ya, inv);
+      store_chunk<T, ENC>(p.key_cache, dst + eb, yb, inv);
     }
     return;
   }
@@ -170,7 +180,8 @@ __global__ __launch_bounds__(kThreads) void rope_cache_write_kernel(RopeParams p
     const int h = u / P8, e = R + 8 * (u % P8);
     const unsigned short* src = static_cast<const unsigned short*>(p.key) + t * p.key_row_stride +
                                 (int64_t)h * D + e;
-    store_chunk<T, ENC>(p.key_cache, slot * row + (int64_t)h * D + e, ld16(src), p.k_inv_scale);
+    store_chunk<T, ENC>(p.key_cache, slot * row + (int64_t)h * D + e, ld16(src),
+                        head_inv<ENC>(p.k_scales, h, p.k_inv_scale));
     return;
   }
   u -= ukp;
@@ -179,7 +190,8 @@ __global__ __launch_bounds__(kThreads) void rope_cache_write_kernel(RopeParams p
     const int h = u / D8, e = 8 * (u % D8);
     const unsigned short* src = static_cast<const unsigned short*>(p.value) + t * p.value_row_stride +
                                 (int64_t)h * D + e;
-    store_chunk<T, ENC>(p.value_cache, slot * row + (int64_t)h * D + e, ld16(src), p.v_inv_scale);
+    store_chunk<T, ENC>(p.value_cache, slot * row + (int64_t)h * D + e, ld16(src),
+                        head_inv<ENC>(p.v_scales, h, p.v_inv_scale));
   }
 }
 

@@ -29,7 +29,8 @@ class PagedAttentionStep:
         self.desc = B.make_desc(wl.num_q_heads, wl.num_kv_heads, wl.head_dim, wl.block_size,
                                 act, cache, k_scale=tensors.k_scale, v_scale=tensors.v_scale,
                                 decode_workers=decode_workers, sliding_window=sliding_window,
-                                alibi_slopes=alibi_slopes)
+                                alibi_slopes=alibi_slopes, k_scales=tensors.k_scales,
+                                v_scales=tensors.v_scales)
         R = wl.num_reqs
         self.T_pad = tensors.q.shape[0]
         self.qsl = torch.empty(qsl_len or (R + 1), dtype=torch.int32, device=dev)

@@ -240,6 +240,24 @@ class Tensors:
     block_tables: torch.Tensor   # int32 [R, W]
     k_scale: float = 1.0
     v_scale: float = 1.0
+    # per K/V head scales of a quantized cache (float32 device tensors [Hkv]),
+    # used in place of k_scale / v_scale when set
+    k_scales: object = None
+    v_scales: object = None
+
+
+def with_head_scales(t, seed, k=True, v=True):
+    """The same tensors read with per-K/V-head scales: head h's scale is the
+    tensor scale times a factor in [2^-1.5, 2^1.5] (drawn per seed), so the
+    pool's codes stand for other values and new rows are written with other
+    inverse scales (some saturating)."""
+    hkv = t.key_cache.shape[2]
+    rng = np.random.default_rng(seed)
+    dev = t.key_cache.device
+    def draw(base):
+        f = np.exp2(rng.uniform(-1.5, 1.5, size=hkv))
+        return torch.from_numpy((np.float32(base) * f).astype(np.float32)).to(dev)
+    return replace(t, k_scales=draw(t.k_scale) if k else None, v_scales=draw(t.v_scale) if v else None)
 
 
 def _randn(gen, shape, device):

@@ -48,6 +48,16 @@ def oracle_metadata(wl, qsl_len=None):
                              wl.block_size, max(wl.num_tokens_padded, wl.num_tokens), qsl_len)
 
 
+def head_scales(tensors):
+    """The K and V scales the library reads with: float32 arrays [Hkv] when the
+    tensors carry per-head scales, else the tensor scales as float32."""
+    def one(per_head, tensor):
+        if per_head is not None:
+            return per_head.cpu().numpy().astype(np.float32)
+        return np.float32(tensor)
+    return one(tensors.k_scales, tensors.k_scale), one(tensors.v_scales, tensors.v_scale)
+
+
 class Snapshot:
     """Host copy of the generator's pool blocks that some requests reference."""
 
@@ -87,15 +97,16 @@ class OraclePrep:
         T = max(wl.num_tokens_padded, wl.num_tokens)
         kb, vb = bits16(tensors.k_new[:T]), bits16(tensors.v_new[:T])
         self.cache_dt = oracle_cache_dtype(wl)
-        k_inv = np.float32(1.0) / np.float32(tensors.k_scale)
-        v_inv = np.float32(1.0) / np.float32(tensors.v_scale)
+        k_sc, v_sc = head_scales(tensors)
+        k_inv = np.float32(1.0) / k_sc
+        v_inv = np.float32(1.0) / v_sc
         self.kc, self.vc = OC.scatter(snapshot.kbits, snapshot.vbits, kb, vb, local_slots, bs,
                                       act_dtype=act, cache_dtype=self.cache_dt, k_inv_scale=k_inv,
                                       v_inv_scale=v_inv, num_tokens=T)
         self.q = OD.decode(bits16(tensors.q), act)
         self.qsl, self.seq_lens = qsl, seq_lens
         self.wl, self.snapshot = wl, snapshot
-        self.k_scale, self.v_scale = tensors.k_scale, tensors.v_scale
+        self.k_scale, self.v_scale = k_sc, v_sc
 
     def rows(self, requests, sliding_window=0, alibi_slopes=None):
         """Oracle rows {r: float64 [n_r, Hq, D]} for the given requests."""

@@ -84,6 +84,34 @@ def test_desc_rejections(kw, status):
     assert _write(_desc(**kw)) == status
 
 
+class _Ptr:
+    """A fake device array: only its address is passed (the calls fail first)."""
+
+    def __init__(self, addr):
+        self.addr = addr
+
+    def data_ptr(self):
+        return self.addr
+
+
+@pytest.mark.parametrize("kw", [
+    dict(k_scales=_Ptr(1 << 20)),                                   # per-head scales, 16-bit cache
+    dict(v_scales=_Ptr(1 << 20)),
+    dict(cache_dtype=B.PA_INT8, k_scales=_Ptr((1 << 20) + 2)),      # not float32-aligned
+    dict(cache_dtype=B.PA_FP8_E4M3, v_scales=_Ptr((1 << 20) + 1)),
+])
+def test_head_scale_rejections(kw):
+    assert _write(_desc(**kw)) == B.PA_ERR_INVALID_ARG
+
+
+def test_head_scales_accepted_with_quantized_cache():
+    # aligned per-head scales on an 8-bit cache pass the descriptor checks (the
+    # call then stops at its own argument check: a null key)
+    d = _desc(cache_dtype=B.PA_INT8, k_scales=_Ptr(1 << 20), v_scales=_Ptr(1 << 21))
+    assert _write(d, key=None) == B.PA_ERR_INVALID_ARG
+    assert _write(d, num_tokens=0) == B.PA_OK
+
+
 def test_cache_write_argument_checks():
     d = _desc()
     assert _write(d, key=None) == B.PA_ERR_INVALID_ARG
