@@ -158,25 +158,24 @@ __device__ inline float v_scale_of(const AttnParams& p, int kvh) {
 __device__ inline int first_key(const AttnParams& p, int s) { return max(0, s - 1 - p.window_left); }
 __device__ inline int first_block(const AttnParams& p, int s) { return first_key(p, s) / kBlock; }
 
-// Cache blocks request rr (index within the call) streams: 0 for a request
-// that is not a decode (query length != 1) or has no keys; with a sliding
-// window only the blocks from the window's first key on.  `uniform`: rr is
-// the same in every lane (scalar loads).
-__device__ inline int stream_blocks(const AttnParams& p, int rr, bool uniform) {
-  const int r = p.req_begin + rr;
-  int q0, q1, s;
-  if (uniform) {
-    q0 = load_uniform(p.qsl, r);
-    q1 = load_uniform(p.qsl, r + 1);
-    s = load_uniform(p.seq_lens, r);
-  } else {
-    q0 = p.qsl[r];
-    q1 = p.qsl[r + 1];
-    s = p.seq_lens[r];
-  }
+// Cache blocks a request streams, from its query_start_loc entries q0, q1 and
+// its seq_len s: 0 for a request that is not a decode (query length != 1)
+// or has no keys; with a sliding window only the blocks from the window's
+// first key on.
+__device__ inline int blocks_of(const AttnParams& p, int q0, int q1, int s) {
   if (q1 - q0 != 1) return 0;
   s = min(min(s, p.max_seq_len), p.max_blocks_per_req * kBlock);
   return s > 0 ? (s + kBlock - 1) / kBlock - first_block(p, s) : 0;
+}
+
+// The same for request rr (index within the call), the same in every lane
+// (scalar loads, all three issued together).
+__device__ inline int stream_blocks(const AttnParams& p, int rr) {
+  const int r = p.req_begin + rr;
+  const int q0 = load_uniform(p.qsl, r);
+  const int q1 = load_uniform(p.qsl, r + 1);
+  const int s = load_uniform(p.seq_lens, r);
+  return blocks_of(p, q0, q1, s);
 }
 
 __device__ inline int64_t readlane64(int64_t v, int l) {
@@ -185,17 +184,22 @@ __device__ inline int64_t readlane64(int64_t v, int l) {
   return (int64_t)(((uint64_t)(uint32_t)hi << 32) | (uint32_t)lo);
 }
 
-// Inclusive prefix sum over the 64 lanes.
+// Inclusive prefix sum over the 64 lanes: shifts within each 16-lane row,
+// then the row totals carried into the rows above (DPP row broadcasts of
+// lanes 15 and 31); lanes a shift leaves without a source add 0.
+template <int CTRL, int ROWS>
+__device__ inline int64_t dpp_shift64(int64_t v) {
+  const int lo = __builtin_amdgcn_update_dpp(0, (int)(uint32_t)v, CTRL, ROWS, 0xF, false);
+  const int hi = __builtin_amdgcn_update_dpp(0, (int)(v >> 32), CTRL, ROWS, 0xF, false);
+  return (int64_t)(((uint64_t)(uint32_t)hi << 32) | (uint32_t)lo);
+}
 __device__ inline int64_t wave_scan(int64_t v) {
-  const int lane = __lane_id();
-#pragma unroll
-  for (int off = 1; off < 64; off <<= 1) {
-    const int src = ((lane - off) & 63) << 2;
-    const int lo = __builtin_amdgcn_ds_bpermute(src, (int)(uint32_t)v);
-    const int hi = __builtin_amdgcn_ds_bpermute(src, (int)(v >> 32));
-    const int64_t t = (int64_t)(((uint64_t)(uint32_t)hi << 32) | (uint32_t)lo);
-    v += (lane >= off) ? t : 0;
-  }
+  v += dpp_shift64<0x111, 0xF>(v);   // row_shr:1
+  v += dpp_shift64<0x112, 0xF>(v);   // row_shr:2
+  v += dpp_shift64<0x114, 0xF>(v);   // row_shr:4
+  v += dpp_shift64<0x118, 0xF>(v);   // row_shr:8
+  v += dpp_shift64<0x142, 0xA>(v);   // row_bcast:15 into rows 1 and 3
+  v += dpp_shift64<0x143, 0xC>(v);   // row_bcast:31 into rows 2 and 3
   return v;
 }
 
@@ -213,18 +217,26 @@ struct Cursor {
   const int32_t* row;   // the request's block-table entries from block b0 on
 };
 
-// Fill the request fields of c for request c.rr (wave-uniform loads).
-__device__ inline void load_request(const AttnParams& p, Cursor& c) {
+// Fill the request fields of c for request c.rr from its query_start_loc
+// entries q0, q1 and its seq_len s_raw.
+__device__ inline void set_request(const AttnParams& p, Cursor& c, int q0, int q1, int s_raw) {
   const int r = p.req_begin + c.rr;
-  const int q0 = load_uniform(p.qsl, r);
-  const int q1 = load_uniform(p.qsl, r + 1);
-  const int s = min(min(load_uniform(p.seq_lens, r), p.max_seq_len), p.max_blocks_per_req * kBlock);
+  const int s = min(min(s_raw, p.max_seq_len), p.max_blocks_per_req * kBlock);
   c.q_row = q0;
   c.s_eff = s;
   c.lo = first_key(p, s);
   c.b0 = c.lo / kBlock;
   c.nb = (q1 - q0 == 1 && s > 0) ? (s + kBlock - 1) / kBlock - c.b0 : 0;
   c.row = p.block_tables + (int64_t)r * p.max_blocks_per_req + c.b0;
+}
+
+// The same from wave-uniform loads.
+__device__ inline void load_request(const AttnParams& p, Cursor& c) {
+  const int r = p.req_begin + c.rr;
+  const int q0 = load_uniform(p.qsl, r);
+  const int q1 = load_uniform(p.qsl, r + 1);
+  const int s = load_uniform(p.seq_lens, r);
+  set_request(p, c, q0, q1, s);
 }
 
 // Advance by one unit (wave-uniform); skips requests that stream nothing.
@@ -271,22 +283,63 @@ __global__ __launch_bounds__(64 * WV) void decode_kernel(AttnParams p) {
   const int G = p.group;
   const int Hkv = p.num_kv_heads;
 
-  // ---- the stream: total units T, this worker's range, its first unit ----
+  // ---- the stream: total units T, this worker's range, its first unit.
+  // Lanes take 64 requests at a time (their three fields loaded together);
+  // with at most 64 requests in the call the first pass's values serve the
+  // search too. ----
   int64_t T = 0;
+  int f_q0 = 0, f_q1 = 0, f_s = 0;   // lane's request of the first 64
+  int64_t f_v = 0, f_incl = 0;
   for (int c = 0; c < Rn; c += 64) {
-    const int64_t v = (c + lane < Rn) ? (int64_t)Hkv * stream_blocks(p, c + lane, false) : 0;
-    T += readlane64(wave_scan(v), 63);
+    int q0 = 0, q1 = 0, s = 0;
+    if (c + lane < Rn) {
+      const int r = p.req_begin + c + lane;
+      q0 = p.qsl[r];
+      q1 = p.qsl[r + 1];
+      s = p.seq_lens[r];
+    }
+    const int64_t v = (c + lane < Rn) ? (int64_t)Hkv * blocks_of(p, q0, q1, s) : 0;
+    const int64_t incl = wave_scan(v);
+    if (c == 0) {
+      f_q0 = q0;
+      f_q1 = q1;
+      f_s = s;
+      f_v = v;
+      f_incl = incl;
+    }
+    T += readlane64(incl, 63);
   }
   const int64_t g0 = in_range ? range_begin(worker, T, W) : T;
   // units of this worker: the host keeps every share below 2^31
   const int n = in_range ? (int)(range_begin(worker + 1, T, W) - g0) : 0;
   Cursor cur{0, 0, 0, 0, 0, 0, 0, 0, nullptr};
   bool found = false;
-  if (in_range) {
+  if (in_range && Rn <= 64) {
+    if (worker == 0 && lane < Rn) p.ws_cum[lane] = f_incl - f_v;
+    const int64_t excl = f_incl - f_v;
+    const uint64_t hit = __builtin_amdgcn_ballot_w64(f_v > 0 && excl <= g0 && g0 < f_incl);
+    if (hit != 0) {
+      const int l = __builtin_ctzll(hit);
+      cur.rr = l;
+      const int64_t within = g0 - readlane64(excl, l);
+      set_request(p, cur, __builtin_amdgcn_readlane(f_q0, l), __builtin_amdgcn_readlane(f_q1, l),
+                  __builtin_amdgcn_readlane(f_s, l));
+      cur.kvh = (int)(within / cur.nb);
+      cur.b = (int)(within % cur.nb);
+      found = true;
+    }
+  } else if (in_range) {
     // worker 0 also publishes the exclusive prefix for the reduce kernel
     int64_t run = 0;
     for (int c = 0; c < Rn; c += 64) {
-      const int64_t v = (c + lane < Rn) ? (int64_t)Hkv * stream_blocks(p, c + lane, false) : 0;
+      int q0 = 0, q1 = 0, s = 0;
+      if (c + lane < Rn) {
+        const int r = p.req_begin + c + lane;
+        q0 = p.qsl[r];
+        q1 = p.qsl[r + 1];
+        s = p.seq_lens[r];
+      }
+      const int64_t v = (c + lane < Rn) ? (int64_t)Hkv * blocks_of(p, q0, q1, s) : 0;
       const int64_t incl = wave_scan(v);
       const int64_t excl = run + incl - v;
       if (worker == 0 && c + lane < Rn) p.ws_cum[c + lane] = excl;
@@ -295,7 +348,8 @@ __global__ __launch_bounds__(64 * WV) void decode_kernel(AttnParams p) {
         const int l = __builtin_ctzll(hit);
         cur.rr = c + l;
         const int64_t within = g0 - readlane64(excl, l);
-        load_request(p, cur);
+        set_request(p, cur, __builtin_amdgcn_readlane(q0, l), __builtin_amdgcn_readlane(q1, l),
+                    __builtin_amdgcn_readlane(s, l));
         cur.kvh = (int)(within / cur.nb);
         cur.b = (int)(within % cur.nb);
         found = true;
@@ -303,8 +357,8 @@ __global__ __launch_bounds__(64 * WV) void decode_kernel(AttnParams p) {
       }
       run += readlane64(incl, 63);
     }
-    if (worker == 0 && lane == 0) p.ws_cum[Rn] = T;
   }
+  if (in_range && worker == 0 && lane == 0) p.ws_cum[Rn] = T;
   const bool active = found && n > 0;
 
   // partial state of the worker's last head when a range boundary cuts it
@@ -748,32 +802,44 @@ __global__ __launch_bounds__(64 * WV) void decode_kernel(AttnParams p) {
   float* const slot_ml = p.ws_ml + (int64_t)blockIdx.x * 2 * G * 2;
   // one run: the last-head partials of `lmask` and the first-head partial
   // of worker fw (or none), merged in worker order
+  // Every wave's region is read whatever the mask says (a region outside
+  // the run may hold anything, so its terms are removed by selects, never by
+  // a zero weight): reads behind a branch per wave would each wait out a
+  // full LDS latency on their own.
   auto merge_run = [&](unsigned lmask, int fw, bool complete, int slot, int kvh, int q_row)
       __attribute__((always_inline)) {
+    const int fsel = fw >= 0 ? fw : 0;
 #pragma unroll
     for (int q = 0; q < kGPT; ++q) {
       const int e = 4 * (tid + q * NT);
       if (e >= G * D) break;
       const int h = e / D;
+      f32x2 ml[WV];
+      f32x4 av[WV];
+#pragma unroll
+      for (int v = 0; v < WV; ++v) {
+        ml[v] = *reinterpret_cast<const f32x2*>(lml(v) + 2 * h);
+        av[v] = *reinterpret_cast<const f32x4*>(lacc(v) + e);
+      }
+      const f32x2 fml_h = *reinterpret_cast<const f32x2*>(fml(fsel) + 2 * h);
       float mx = -INFINITY;
 #pragma unroll
-      for (int v = 0; v < WV; ++v)
-        if ((lmask >> v) & 1u) mx = fmaxf(mx, lml(v)[2 * h]);
-      if (fw >= 0) mx = fmaxf(mx, fml(fw)[2 * h]);
+      for (int v = 0; v < WV; ++v) mx = ((lmask >> v) & 1u) ? fmaxf(mx, ml[v][0]) : mx;
+      if (fw >= 0) mx = fmaxf(mx, fml_h[0]);
       const float Ms = (mx == -INFINITY) ? 0.f : mx;
       float L = 0.f;
       f32x4 A{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
       for (int v = 0; v < WV; ++v) {
-        if ((lmask >> v) & 1u) {
-          const float wgt = fast_exp2(lml(v)[2 * h] - Ms);
-          L += wgt * lml(v)[2 * h + 1];
-          A += wgt * *reinterpret_cast<const f32x4*>(lacc(v) + e);
-        }
+        const bool in = (lmask >> v) & 1u;
+        const float wgt = fast_exp2(ml[v][0] - Ms);
+        L = in ? L + wgt * ml[v][1] : L;
+        const f32x4 t = A + wgt * av[v];
+        A = in ? t : A;
       }
       if (fw >= 0) {
-        const float wgt = fast_exp2(fml(fw)[2 * h] - Ms);
-        L += wgt * fml(fw)[2 * h + 1];
+        const float wgt = fast_exp2(fml_h[0] - Ms);
+        L += wgt * fml_h[1];
         f32x4 fv{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
         for (int v = 0; v < WV; ++v) fv = (v == fw) ? fa[v][q] : fv;
@@ -850,15 +916,21 @@ __global__ __launch_bounds__(64) void decode_reduce_kernel(AttnParams p) {
   const int rr = blockIdx.y;
   const int qh = blockIdx.x;
   const int lane = threadIdx.x;
-  const int nb = stream_blocks(p, rr, true);
+  // every value the partials' location depends on, loaded together
+  const int r = p.req_begin + rr;
+  const int rq0 = load_uniform(p.qsl, r);
+  const int rq1 = load_uniform(p.qsl, r + 1);
+  const int rs = load_uniform(p.seq_lens, r);
+  const int64_t T = p.ws_cum[p.num_reqs];
+  const int64_t cum = p.ws_cum[rr];
+  const int nb = blocks_of(p, rq0, rq1, rs);
   if (nb == 0) return;
   const int G = p.group;
   const int kvh = qh / G;
   const int hig = qh % G;
   const int64_t W = p.num_workers;
   const int64_t WV = p.wg_waves;
-  const int64_t T = p.ws_cum[p.num_reqs];
-  const int64_t a = p.ws_cum[rr] + (int64_t)kvh * nb;
+  const int64_t a = cum + (int64_t)kvh * nb;
   const int64_t b = a + nb;
   const int64_t ga = (((a + 1) * W - 1) / T) / WV;   // workgroup holding unit a
   const int64_t gb = ((b * W - 1) / T) / WV;         // workgroup holding unit b-1
@@ -875,6 +947,46 @@ __global__ __launch_bounds__(64) void decode_reduce_kernel(AttnParams p) {
     return (g * 2 + (i == 0 ? sl_a : 0)) * G + hig;
   };
 
+  float lsum = 0.f;
+  float o[DPL];
+#pragma unroll
+  for (int e = 0; e < DPL; ++e) o[e] = 0.f;
+  bool ok0;
+  const int64_t ix0 = part_index(0, ok0);   // workgroup g_a always holds a partial
+  if (cnt <= RB) {
+    // the common case: every partial's (max, sum) pair (one per lane) and
+    // columns loaded at once, then the weights
+    bool ok = false;
+    int64_t ix = ix0;
+    if (lane < cnt) {
+      ix = part_index(lane, ok);
+      ix = ok ? ix : ix0;   // a missing partial reads an existing one, weight 0
+    }
+    const f32x2 ml = *reinterpret_cast<const f32x2*>(p.ws_ml + ix * 2);
+    float v[RB][DPL];
+#pragma unroll
+    for (int u = 0; u < RB; ++u) {
+      const float* ap = p.ws_acc + readlane64(ix, min(u, cnt - 1)) * D + lane;
+#pragma unroll
+      for (int e = 0; e < DPL; ++e) v[u][e] = ap[64 * e];
+    }
+    float mx = ok ? ml[0] : -INFINITY;
+#pragma unroll
+    for (int off = RB / 2; off >= 1; off >>= 1) mx = fmaxf(mx, shfl_xor(mx, off));
+    mx = __builtin_bit_cast(float, __builtin_amdgcn_readfirstlane(__builtin_bit_cast(int, mx)));
+    const float msafe = (mx == -INFINITY) ? 0.f : mx;
+    const float w = ok ? fast_exp2(ml[0] - msafe) : 0.f;
+    float t = ok ? w * ml[1] : 0.f;
+#pragma unroll
+    for (int off = RB / 2; off >= 1; off >>= 1) t += shfl_xor(t, off);
+    lsum = __builtin_bit_cast(float, __builtin_amdgcn_readfirstlane(__builtin_bit_cast(int, t)));
+#pragma unroll
+    for (int u = 0; u < RB; ++u) {
+      const float wu = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, w), u));
+#pragma unroll
+      for (int e = 0; e < DPL; ++e) o[e] += (u < cnt ? wu : 0.f) * v[u][e];
+    }
+  } else {
   float mloc = -INFINITY;
   for (int i = lane; i < cnt; i += 64) {
     bool ok;
@@ -884,13 +996,6 @@ __global__ __launch_bounds__(64) void decode_reduce_kernel(AttnParams p) {
 #pragma unroll
   for (int off = 32; off >= 1; off >>= 1) mloc = fmaxf(mloc, shfl_xor(mloc, off));
   const float msafe = (mloc == -INFINITY) ? 0.f : mloc;
-
-  float lsum = 0.f;
-  float o[DPL];
-#pragma unroll
-  for (int e = 0; e < DPL; ++e) o[e] = 0.f;
-  bool ok0;
-  const int64_t ix0 = part_index(0, ok0);   // workgroup g_a always holds a partial
   for (int g = 0; g < cnt; g += 64) {
     const int i = g + lane;
     bool ok = false;
@@ -921,9 +1026,9 @@ __global__ __launch_bounds__(64) void decode_reduce_kernel(AttnParams p) {
         for (int e = 0; e < DPL; ++e) o[e] += wj[u] * v[u][e];
     }
   }
+  }
   const float inv = (lsum > 0.f) ? v_scale_of<1>(p, kvh) / lsum : 0.f;
-  const int q_row = load_uniform(p.qsl, p.req_begin + rr);
-  unsigned short* orow = static_cast<unsigned short*>(p.out) + (int64_t)q_row * p.out_row_stride +
+  unsigned short* orow = static_cast<unsigned short*>(p.out) + (int64_t)rq0 * p.out_row_stride +
                          (int64_t)qh * D;
 #pragma unroll
   for (int e = 0; e < DPL; ++e) orow[lane + 64 * e] = Mfma<CT>::from_float(o[e] * inv);
