@@ -777,20 +777,27 @@ __global__ __launch_bounds__(64 * WV) void decode_kernel(AttnParams p) {
     mi->f_kvh = f_kvh;
     mi->f_qrow = f_qrow;
   }
-  wait_vmcnt<0>();   // the first-head sums (and this worker's output rows) are stored
-  __syncthreads();
+  // the workgroup's range (formed while the other waves finish)
   const int64_t wg0 = (int64_t)blockIdx.x * WV;
   const int64_t wg_begin = range_begin(wg0, T, W);
   const int64_t wg_end = range_begin(min(wg0 + WV, (int64_t)W), T, W);
+  wait_vmcnt<0>();   // the first-head sums (and this worker's output rows) are stored
+  __syncthreads();
   const int tid = threadIdx.x;
   constexpr int NT = 64 * WV;
   // each thread takes groups of 4 consecutive elements (one head each)
   constexpr int kGPT = (16 * HT * D / 4 + NT - 1) / NT;   // element groups per thread, at most
+  // the workers' records, lane v of every wave holding worker v's
+  const MergeInfo* mi_l = info(lane < WV ? lane : 0);
+  const int r_flags = lane < WV ? mi_l->flags : 0;
+  const int64_t r_lfirst = mi_l->l_first, r_lend = mi_l->l_end, r_ffirst = mi_l->f_first;
+  const int r_lkvh = mi_l->l_kvh, r_lqrow = mi_l->l_qrow, r_fkvh = mi_l->f_kvh, r_fqrow = mi_l->f_qrow;
+  const unsigned fmask = (unsigned)__builtin_amdgcn_ballot_w64((r_flags & kF) != 0);
   // every first-head partial's sums of this thread's groups, loaded first
   f32x4 fa[WV][kGPT];
 #pragma unroll
   for (int v = 0; v < WV; ++v) {
-    const bool fv = (info(v)->flags & kF) != 0;   // LDS broadcast reads, issued together
+    const bool fv = (fmask >> v) & 1u;
     const float* src = p.ws_facc + (wg0 + v) * G * D;
 #pragma unroll
     for (int q = 0; q < kGPT; ++q) {
@@ -859,43 +866,38 @@ __global__ __launch_bounds__(64 * WV) void decode_kernel(AttnParams p) {
       }
     }
   };
-  // the workers' records, lane v of every wave holding worker v's, read
-  // back uniformly with lane reads (no LDS round trip per step of the walk)
-  const MergeInfo* mi_l = info(lane < WV ? lane : 0);
-  const int r_flags = lane < WV ? mi_l->flags : 0;
-  const int64_t r_lfirst = mi_l->l_first, r_lend = mi_l->l_end, r_ffirst = mi_l->f_first;
-  const int r_lkvh = mi_l->l_kvh, r_lqrow = mi_l->l_qrow, r_fkvh = mi_l->f_kvh, r_fqrow = mi_l->f_qrow;
-  auto flags_of = [&](int v) { return __builtin_amdgcn_readlane(r_flags, v); };
-  auto lfirst_of = [&](int v) { return readlane64(r_lfirst, v); };
-  auto ffirst_of = [&](int v) { return readlane64(r_ffirst, v); };
-  for (int w = 0; w < WV; ++w) {   // uniform
-    const int fl = flags_of(w);
-    if (!(fl & (kL | kF))) continue;
-    int u = w - 1;                          // previous worker that streamed anything
-    while (u >= 0 && !(flags_of(u) & kBusy)) --u;
-    if ((fl & kF) && !(u >= 0 && (flags_of(u) & kL) && lfirst_of(u) == ffirst_of(w))) {
-      // a first head begun before the workgroup's range: its only piece
-      // here, and it holds the range's first unit (slot 0)
-      merge_run(0u, w, false, 0, __builtin_amdgcn_readlane(r_fkvh, w),
-                __builtin_amdgcn_readlane(r_fqrow, w));
-    }
-    if (!(fl & kL)) continue;
-    const int64_t X = lfirst_of(w);
-    if (u >= 0 && (flags_of(u) & kL) && lfirst_of(u) == X) continue;   // merged with an earlier run
-    // the run of workers holding head X: this one, workers whose whole range
-    // lies inside it, and possibly the one where it ends (its first head)
-    unsigned lmask = 1u << w;
-    int fw = -1;
-    for (int v = w + 1; v < WV; ++v) {
-      const int fv = flags_of(v);
-      if (!(fv & kBusy)) continue;
-      if ((fv & kL) && lfirst_of(v) == X) {
-        lmask |= 1u << v;
-        continue;
-      }
-      if ((fv & kF) && ffirst_of(v) == X) fw = v;
-      break;
-    }
+  // The runs, found lane-parallel from the records (lane v = worker v):
+  // worker v continues a run when it holds a cut last head equal to the one
+  // of the previous worker that streamed anything; its first head ends that
+  // worker's run when it equals that worker's last head.  A run starts at
+  // each last head that continues nothing and ends before the first
+  // streaming worker after it that does not continue it, whose first head
+  // (if attached) closes it; a first head attached to nothing began before
+  // the workgroup's range and is its only piece here (slot 0).
+  const unsigned bmask = (unsigned)__builtin_amdgcn_ballot_w64((r_flags & kBusy) != 0);
+  const unsigned lmask_all = (unsigned)__builtin_amdgcn_ballot_w64((r_flags & kL) != 0);
+  const unsigned below = lane < WV ? bmask & ((1u << lane) - 1u) : 0u;
+  const int prv = below != 0u ? 31 - __builtin_clz(below) : 0;
+  const int p_flags = __builtin_amdgcn_ds_bpermute(prv << 2, r_flags);
+  const int p_lo = __builtin_amdgcn_ds_bpermute(prv << 2, (int)(uint32_t)r_lfirst);
+  const int p_hi = __builtin_amdgcn_ds_bpermute(prv << 2, (int)(r_lfirst >> 32));
+  const int64_t p_lfirst = (int64_t)(((uint64_t)(uint32_t)p_hi << 32) | (uint32_t)p_lo);
+  const bool prev_l = below != 0u && (p_flags & kL) != 0;
+  const unsigned cmask =
+      (unsigned)__builtin_amdgcn_ballot_w64((r_flags & kL) != 0 && prev_l && p_lfirst == r_lfirst);
+  const unsigned amask =
+      (unsigned)__builtin_amdgcn_ballot_w64((r_flags & kF) != 0 && prev_l && p_lfirst == r_ffirst);
+  for (unsigned a = fmask & ~amask; a != 0u; a &= a - 1u) {   // uniform
+    const int w = __builtin_ctz(a);
+    merge_run(0u, w, false, 0, __builtin_amdgcn_readlane(r_fkvh, w), __builtin_amdgcn_readlane(r_fqrow, w));
+  }
+  for (unsigned st = lmask_all & ~cmask; st != 0u; st &= st - 1u) {   // uniform
+    const int w = __builtin_ctz(st);
+    const unsigned after = bmask & ~cmask & ~((2u << w) - 1u);
+    const int e1 = after != 0u ? __builtin_ctz(after) : WV;
+    const unsigned lmask = (cmask & ((1u << e1) - 1u) & ~((2u << w) - 1u)) | (1u << w);
+    const int fw = (e1 < WV && ((amask >> e1) & 1u)) ? e1 : -1;
+    const int64_t X = readlane64(r_lfirst, w);
     const int64_t Xend = readlane64(r_lend, w);
     merge_run(lmask, fw, X >= wg_begin && Xend <= wg_end, X <= wg_begin ? 0 : 1,
               __builtin_amdgcn_readlane(r_lkvh, w), __builtin_amdgcn_readlane(r_lqrow, w));
