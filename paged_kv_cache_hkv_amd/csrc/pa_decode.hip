@@ -203,8 +203,21 @@ __device__ inline int64_t wave_scan(int64_t v) {
   return v;
 }
 
+// floor(x / y) for x >= 0, y > 0.  Below 2^53 both convert to double exactly
+// and the double quotient is off by at most one, which the integer check
+// corrects; the generic 64-bit division is a long instruction sequence.
+__device__ inline int64_t div_floor(int64_t x, int64_t y) {
+  if (x < (int64_t(1) << 53)) {
+    int64_t q = (int64_t)((double)x / (double)y);
+    q -= (q * y > x) ? 1 : 0;
+    q += ((q + 1) * y <= x) ? 1 : 0;
+    return q;
+  }
+  return x / y;
+}
+
 // First stream unit of worker w (W workers over T units).
-__device__ inline int64_t range_begin(int64_t w, int64_t T, int64_t W) { return w * T / W; }
+__device__ inline int64_t range_begin(int64_t w, int64_t T, int64_t W) { return div_floor(w * T, W); }
 
 // Position in the stream: request (index within the call), K/V head, block
 // of that head counted from b0 (the first block the request streams: 0, or
@@ -934,8 +947,9 @@ __global__ __launch_bounds__(64) void decode_reduce_kernel(AttnParams p) {
   const int64_t WV = p.wg_waves;
   const int64_t a = cum + (int64_t)kvh * nb;
   const int64_t b = a + nb;
-  const int64_t ga = (((a + 1) * W - 1) / T) / WV;   // workgroup holding unit a
-  const int64_t gb = ((b * W - 1) / T) / WV;         // workgroup holding unit b-1
+  // workgroups holding units a and b-1 (worker indices fit 32 bits)
+  const int64_t ga = (int)div_floor((a + 1) * W - 1, T) / (int)WV;
+  const int64_t gb = (int)div_floor(b * W - 1, T) / (int)WV;
   if (ga == gb) return;
   const int cnt = (int)(gb - ga + 1);
   // partial of the i-th workgroup of the cut: slot 1 for g_a if its range
